@@ -1,0 +1,200 @@
+/*
+ * lbp.h - load-balanced paged GQA decode attention for AMD Instinct MI355X
+ * (gfx950).  C ABI of liblbp.so.
+ *
+ * The method (SGLang x HPC-Ops page, "Scheduling around live KV work";
+ * vLLM x HPC-Ops page, "Solution: per-step load-balanced decode scheduler"):
+ * once per decode step an assign kernel turns the live sequence lengths
+ * into a task map that spreads 64-token KV tiles evenly over a fixed number
+ * of persistent workgroups; for every layer a persistent attention kernel
+ * drains each workgroup's bin and writes one partial output plus its
+ * log-sum-exp per task descriptor, and a light combine kernel merges each
+ * (KV head, request) pair's partials into the final BF16 output.
+ *
+ * Conventions for every function below:
+ *  - Pointers named *_dev are device pointers; everything else is host
+ *    memory.  The caller allocates and owns every buffer; the library keeps
+ *    no device allocation and no per-call state.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Every launching call is asynchronous on that stream, performs no
+ *    host<->device copy and no synchronisation, so it can be captured into
+ *    a HIP graph.
+ *  - Arguments are checked on the host before anything is launched; a bad
+ *    argument returns an error status and launches nothing.  Faults inside
+ *    a kernel surface at the caller's next synchronisation, as for any HIP
+ *    call.  No C++ exception crosses this interface.
+ *
+ * Fixed data layouts (all contiguous, row-major):
+ *  - q        [batch][num_q_heads][128]                 bf16
+ *  - out      [batch][num_q_heads][128]                 bf16
+ *  - k_cache, v_cache [num_pages][num_kv_heads][64][128] bf16, or uint8
+ *             OCP e4m3 codes for LBP_KV_FP8_E4M3 (page, KV head, slot, dim)
+ *  - k_scale, v_scale [num_pages][num_kv_heads][64]     fp32 (FP8 only);
+ *             the stored value is e4m3(code) * scale
+ *  - seq_lens [batch] int32; page_table [batch][page_table_stride] int32:
+ *             token t of request r lives in page page_table[r][t / 64] at
+ *             slot t % 64.  Entries past a request's last page are not read.
+ *  - Query head h belongs to KV head h / (num_q_heads / num_kv_heads).
+ */
+#ifndef LBP_H
+#define LBP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LBP_VERSION 1
+#define LBP_HEAD_DIM 128
+#define LBP_PAGE_SIZE 64
+#define LBP_MAX_GROUP 16
+#define LBP_PLAN_MAGIC 0x4C425031u /* "LBP1" */
+
+typedef enum lbp_status {
+  LBP_OK = 0,
+  LBP_ERR_INVALID_ARG = 1,         /* NULL pointer, non-positive size, ... */
+  LBP_ERR_UNSUPPORTED = 2,         /* head_dim != 128, page != 64, group > 16 */
+  LBP_ERR_WORKSPACE_TOO_SMALL = 3, /* a caller workspace is below the query */
+  LBP_ERR_MISMATCH = 4,            /* plan info does not match the config */
+  LBP_ERR_HIP = 5                  /* the HIP runtime refused a launch/query */
+} lbp_status;
+
+typedef enum lbp_kv_dtype { LBP_KV_BF16 = 0, LBP_KV_FP8_E4M3 = 1 } lbp_kv_dtype;
+
+/* Scheduling policies.  DYNAMIC is the method; the two static split-KV
+ * policies are the comparison the SGLang x HPC-Ops page describes under
+ * "Attention: load balancing for mixed-length decode" (one fixed grid over
+ * KV heads, requests and splits, with a fixed split count or a fixed chunk
+ * size for every request).  All three emit the same task-map format. */
+typedef enum lbp_policy {
+  LBP_POLICY_DYNAMIC = 0,       /* param = F, the minimum tiles per bin (0 = cfg) */
+  LBP_POLICY_STATIC_SPLITS = 1, /* param = S, splits per (KV head, request) */
+  LBP_POLICY_STATIC_CHUNK = 2   /* param = C, tiles per split; every pair gets
+                                   ceil(max_pages_per_seq / C) bins */
+} lbp_policy;
+
+typedef struct lbp_config {
+  int32_t num_q_heads;       /* Hq >= 1 */
+  int32_t num_kv_heads;      /* H_kv >= 1, Hq % H_kv == 0, Hq / H_kv <= 16 */
+  int32_t head_dim;          /* must be 128 */
+  int32_t page_size;         /* must be 64 (one page = one 64-token tile) */
+  int32_t max_batch;         /* largest batch any plan will be built for */
+  int32_t max_pages_per_seq; /* page-table row capacity; lengths above
+                                64 * max_pages_per_seq are clamped and flagged */
+  int32_t num_workgroups;    /* W, persistent workgroups (bins); 0 = one per CU */
+  int32_t min_tiles_per_bin; /* F, the minimum-work floor in tiles; 0 = 4 */
+  int32_t kv_dtype;          /* lbp_kv_dtype */
+  float sm_scale;            /* softmax scale, > 0 (1/sqrt(128) typically) */
+} lbp_config;
+
+/* Host-side record of a built plan, filled by lbp_plan / lbp_plan_static and
+ * read by the attend calls.  Plain data; copy it freely. */
+typedef struct lbp_plan_info {
+  uint32_t magic;            /* LBP_PLAN_MAGIC once filled */
+  int32_t policy;            /* lbp_policy */
+  int32_t param;             /* F, S or C as used */
+  int32_t batch;
+  int32_t num_kv_heads;
+  int32_t num_q_heads;
+  int32_t num_bins;          /* workgroups the attention kernel launches */
+  int32_t max_desc;          /* descriptor (and split-buffer slot) capacity */
+  uint64_t plan_bytes;       /* bytes of the plan workspace in use */
+  const int32_t* page_table_dev; /* bound page table (must outlive the plan) */
+  int64_t page_table_stride; /* in int32 entries */
+} lbp_plan_info;
+
+/* Byte offsets of the task map inside a plan workspace (for readers such as
+ * tests; the kernels use the same offsets).  All sections are int32:
+ *   header[16]: [0] magic [1] policy [2] num_bins [3] batch [4] num_kv_heads
+ *               [5] T (tiles) [6] budget (F-floored for DYNAMIC, S or C for
+ *               the static policies) [7] D (descriptors) [8] U (bins with
+ *               work) [9] status bits (1 = a length was clamped)
+ *   bin_offset[num_bins + 1]  descriptors of bin b: [bin_offset[b], bin_offset[b+1])
+ *   desc[max_desc][4]         (kv_head, request, token_begin, token_end)
+ *   pair_first[H_kv * batch], pair_count[H_kv * batch]; pair p = kv_head * batch + request
+ *   scratch[H_kv * batch]     assign-kernel scratch */
+typedef struct lbp_plan_offsets {
+  uint64_t header, bin_offset, desc, pair_first, pair_count, scratch, total;
+} lbp_plan_offsets;
+
+/* Human-readable name of a status code (static storage). */
+const char* lbp_status_string(lbp_status s);
+
+/* LBP_VERSION of the built library. */
+int32_t lbp_version(void);
+
+/* Workspace sizes a (config, policy, param) needs at batch = max_batch.
+ * plan_bytes: the task map; split_bytes: the partial-output buffer
+ * (max_desc x G x 128 fp32 plus max_desc x G fp32 log-sum-exp).  Host only;
+ * may query the current device's CU count when num_workgroups == 0. */
+lbp_status lbp_query_workspace(const lbp_config* cfg, int32_t policy, int32_t param,
+                               size_t* plan_bytes, size_t* split_bytes);
+
+/* Dynamic plan (the method's assign step; SGLang x HPC-Ops page, "Scheduling
+ * around live KV work"; vLLM x HPC-Ops page, bullet "Assign"): cut each of
+ * the num_kv_heads x batch (KV head, request) pairs into ceil(L / 64) tiles,
+ * set budget = max(ceil(T / W), F) from the total T, and fill bins 0..W-1 in
+ * head-major, batch-minor order, each up to the budget before spilling into
+ * the next; one descriptor per run of one pair in one bin.  Runs one
+ * workgroup on `stream`, reading seq_lens_dev on the device (no D2H).  The
+ * map is valid for every layer of the step while page_table_dev and the
+ * lengths stay unchanged.  Negative lengths count as 0. */
+lbp_status lbp_plan(const lbp_config* cfg, const int32_t* seq_lens_dev, int32_t batch,
+                    const int32_t* page_table_dev, int64_t page_table_stride,
+                    void* plan_ws_dev, size_t plan_ws_bytes, lbp_plan_info* info,
+                    void* stream);
+
+/* Static split-KV plan in the same format (comparison schedules).
+ * policy = LBP_POLICY_STATIC_SPLITS: pair p's n tiles are cut into S ranges
+ * of ceil(n / S) tiles, range s in bin p * S + s (empty ranges: no
+ * descriptor).  policy = LBP_POLICY_STATIC_CHUNK: range s = tiles
+ * [s*C, min((s+1)*C, n)) in bin p * ceil(max_pages_per_seq / C) + s. */
+lbp_status lbp_plan_static(const lbp_config* cfg, int32_t policy, int32_t param,
+                           const int32_t* seq_lens_dev, int32_t batch,
+                           const int32_t* page_table_dev, int64_t page_table_stride,
+                           void* plan_ws_dev, size_t plan_ws_bytes, lbp_plan_info* info,
+                           void* stream);
+
+/* Offsets of the task-map sections for a filled plan info (host only). */
+lbp_status lbp_plan_layout(const lbp_plan_info* info, lbp_plan_offsets* offsets);
+
+/* One decode-attention layer: the persistent attention kernel, then the
+ * combine kernel, both on `stream` (SGLang x HPC-Ops page, "Scheduling
+ * around live KV work", second paragraph; vLLM x HPC-Ops page, bullet
+ * "Compute and combine").  Workgroup b drains bin b: for each descriptor it
+ * computes softmax(sm_scale * q k^T) v over the descriptor's tokens for the
+ * KV head's whole query group, writing the normalised partial output and its
+ * log-sum-exp to the descriptor's slot of split_ws_dev; the combine kernel
+ * merges each pair's partials under the global softmax normalisation and
+ * writes out_dev in BF16 (round to nearest even).  A pair with no tokens
+ * gets zeros.  k_scale_dev / v_scale_dev are required for FP8 KV and
+ * ignored for BF16. */
+lbp_status lbp_attend(const lbp_config* cfg, const lbp_plan_info* info,
+                      const void* plan_ws_dev, const void* q_dev, const void* k_cache_dev,
+                      const void* v_cache_dev, const float* k_scale_dev,
+                      const float* v_scale_dev, void* split_ws_dev, size_t split_ws_bytes,
+                      void* out_dev, void* stream);
+
+/* The two halves of lbp_attend, for callers that schedule or time them
+ * separately.  lbp_attend_partials writes only the split buffer;
+ * lbp_combine reads it and writes out_dev.  Split-buffer layout:
+ * o_part[max_desc][G][128] fp32 at offset 0, then lse_part[max_desc][G]
+ * fp32 (base-2 log-sum-exp of sm_scale*log2(e)-scaled scores) at offset
+ * max_desc*G*128*4. */
+lbp_status lbp_attend_partials(const lbp_config* cfg, const lbp_plan_info* info,
+                               const void* plan_ws_dev, const void* q_dev,
+                               const void* k_cache_dev, const void* v_cache_dev,
+                               const float* k_scale_dev, const float* v_scale_dev,
+                               void* split_ws_dev, size_t split_ws_bytes, void* stream);
+
+lbp_status lbp_combine(const lbp_config* cfg, const lbp_plan_info* info,
+                       const void* plan_ws_dev, const void* split_ws_dev,
+                       size_t split_ws_bytes, void* out_dev, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LBP_H */

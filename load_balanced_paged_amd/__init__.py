@@ -1,0 +1,294 @@
+"""Python binding of liblbp (load-balanced paged decode attention, gfx950).
+
+A thin ctypes layer over the C ABI in ``include/lbp.h``: the functions keep
+the C names and only marshal arguments (torch tensors -> device pointers,
+streams -> hipStream_t).  Every step of the computation runs in the HIP
+kernels of ``liblbp.so``; there is no fallback.  If the library has not been
+built, :func:`load` raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "liblbp.so")
+
+LBP_OK = 0
+LBP_ERR_INVALID_ARG = 1
+LBP_ERR_UNSUPPORTED = 2
+LBP_ERR_WORKSPACE_TOO_SMALL = 3
+LBP_ERR_MISMATCH = 4
+LBP_ERR_HIP = 5
+
+LBP_KV_BF16 = 0
+LBP_KV_FP8_E4M3 = 1
+
+LBP_POLICY_DYNAMIC = 0
+LBP_POLICY_STATIC_SPLITS = 1
+LBP_POLICY_STATIC_CHUNK = 2
+
+LBP_PLAN_MAGIC = 0x4C425031
+HEAD_DIM = 128
+PAGE_SIZE = 64
+
+EXPORTED_SYMBOLS = (
+    "lbp_status_string", "lbp_version", "lbp_query_workspace", "lbp_plan", "lbp_plan_static",
+    "lbp_plan_layout", "lbp_attend", "lbp_attend_partials", "lbp_combine",
+)
+
+
+class lbp_config(ctypes.Structure):
+    _fields_ = [
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("max_batch", ctypes.c_int32),
+        ("max_pages_per_seq", ctypes.c_int32),
+        ("num_workgroups", ctypes.c_int32),
+        ("min_tiles_per_bin", ctypes.c_int32),
+        ("kv_dtype", ctypes.c_int32),
+        ("sm_scale", ctypes.c_float),
+    ]
+
+
+class lbp_plan_info(ctypes.Structure):
+    _fields_ = [
+        ("magic", ctypes.c_uint32),
+        ("policy", ctypes.c_int32),
+        ("param", ctypes.c_int32),
+        ("batch", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_bins", ctypes.c_int32),
+        ("max_desc", ctypes.c_int32),
+        ("plan_bytes", ctypes.c_uint64),
+        ("page_table_dev", ctypes.c_void_p),
+        ("page_table_stride", ctypes.c_int64),
+    ]
+
+
+class lbp_plan_offsets(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_uint64) for n in
+                ("header", "bin_offset", "desc", "pair_first", "pair_count", "scratch", "total")]
+
+
+class LbpError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what} failed: {status_name(status)}")
+
+
+_lib = None
+_STATUS_NAMES = {0: "LBP_OK", 1: "LBP_ERR_INVALID_ARG", 2: "LBP_ERR_UNSUPPORTED",
+                 3: "LBP_ERR_WORKSPACE_TOO_SMALL", 4: "LBP_ERR_MISMATCH", 5: "LBP_ERR_HIP"}
+
+
+def status_name(s: int) -> str:
+    return _STATUS_NAMES.get(int(s), f"status {s}")
+
+
+def load(path: str = LIB_PATH):
+    """Load liblbp.so (once).  Raises RuntimeError if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "`python -m load_balanced_paged_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(path)
+    P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    cfgp = ctypes.POINTER(lbp_config)
+    infop = ctypes.POINTER(lbp_plan_info)
+    sig = {
+        "lbp_status_string": (ctypes.c_char_p, [I32]),
+        "lbp_version": (I32, []),
+        "lbp_query_workspace": (I32, [cfgp, I32, I32, ctypes.POINTER(SZ), ctypes.POINTER(SZ)]),
+        "lbp_plan": (I32, [cfgp, P, I32, P, I64, P, SZ, infop, P]),
+        "lbp_plan_static": (I32, [cfgp, I32, I32, P, I32, P, I64, P, SZ, infop, P]),
+        "lbp_plan_layout": (I32, [infop, ctypes.POINTER(lbp_plan_offsets)]),
+        "lbp_attend": (I32, [cfgp, infop, P, P, P, P, P, P, P, SZ, P, P]),
+        "lbp_attend_partials": (I32, [cfgp, infop, P, P, P, P, P, P, P, SZ, P]),
+        "lbp_combine": (I32, [cfgp, infop, P, P, SZ, P, P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+# ---------------------------------------------------------------------------
+# marshalling helpers
+# ---------------------------------------------------------------------------
+
+def _ptr(t, what, dtype=None, optional=False):
+    if t is None:
+        if optional:
+            return None
+        raise ValueError(f"{what} is required")
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{what} must be a torch tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{what} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise TypeError(f"{what} has dtype {t.dtype}, expected {dtype}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(status, what):
+    if status != LBP_OK:
+        raise LbpError(status, what)
+
+
+def make_config(num_q_heads, num_kv_heads, max_batch, max_pages_per_seq, kv_dtype="bf16",
+                num_workgroups=0, min_tiles_per_bin=0, sm_scale=None, head_dim=HEAD_DIM,
+                page_size=PAGE_SIZE) -> lbp_config:
+    dt = {"bf16": LBP_KV_BF16, "fp8_e4m3": LBP_KV_FP8_E4M3}.get(kv_dtype, kv_dtype)
+    return lbp_config(num_q_heads, num_kv_heads, head_dim, page_size, max_batch,
+                      max_pages_per_seq, num_workgroups, min_tiles_per_bin, int(dt),
+                      float(sm_scale if sm_scale is not None else head_dim ** -0.5))
+
+
+# ---------------------------------------------------------------------------
+# C entry points (same names)
+# ---------------------------------------------------------------------------
+
+def lbp_status_string(status: int) -> str:
+    return load().lbp_status_string(int(status)).decode()
+
+
+def lbp_version() -> int:
+    return int(load().lbp_version())
+
+
+def lbp_query_workspace(cfg: lbp_config, policy: int = LBP_POLICY_DYNAMIC, param: int = 0):
+    """(plan_bytes, split_bytes) for cfg.max_batch."""
+    pb, sb = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(load().lbp_query_workspace(ctypes.byref(cfg), policy, param, ctypes.byref(pb),
+                                      ctypes.byref(sb)), "lbp_query_workspace")
+    return pb.value, sb.value
+
+
+def lbp_plan(cfg, seq_lens, page_table, plan_ws, stream=None) -> lbp_plan_info:
+    import torch
+    info = lbp_plan_info()
+    _check(load().lbp_plan(ctypes.byref(cfg), _ptr(seq_lens, "seq_lens", torch.int32),
+                           int(seq_lens.numel()), _ptr(page_table, "page_table", torch.int32),
+                           int(page_table.shape[1]), _ptr(plan_ws, "plan_ws"),
+                           plan_ws.numel() * plan_ws.element_size(), ctypes.byref(info),
+                           _stream(stream)), "lbp_plan")
+    return info
+
+
+def lbp_plan_static(cfg, policy, param, seq_lens, page_table, plan_ws, stream=None) -> lbp_plan_info:
+    import torch
+    info = lbp_plan_info()
+    _check(load().lbp_plan_static(ctypes.byref(cfg), int(policy), int(param),
+                                  _ptr(seq_lens, "seq_lens", torch.int32), int(seq_lens.numel()),
+                                  _ptr(page_table, "page_table", torch.int32),
+                                  int(page_table.shape[1]), _ptr(plan_ws, "plan_ws"),
+                                  plan_ws.numel() * plan_ws.element_size(), ctypes.byref(info),
+                                  _stream(stream)), "lbp_plan_static")
+    return info
+
+
+def lbp_plan_layout(info: lbp_plan_info) -> lbp_plan_offsets:
+    off = lbp_plan_offsets()
+    _check(load().lbp_plan_layout(ctypes.byref(info), ctypes.byref(off)), "lbp_plan_layout")
+    return off
+
+
+def _kv_ptrs(cfg, k_cache, v_cache, k_scale, v_scale):
+    import torch
+    kv_t = torch.bfloat16 if cfg.kv_dtype == LBP_KV_BF16 else torch.uint8
+    fp8 = cfg.kv_dtype == LBP_KV_FP8_E4M3
+    return (_ptr(k_cache, "k_cache", kv_t), _ptr(v_cache, "v_cache", kv_t),
+            _ptr(k_scale, "k_scale", torch.float32, optional=not fp8),
+            _ptr(v_scale, "v_scale", torch.float32, optional=not fp8))
+
+
+def lbp_attend(cfg, info, plan_ws, q, k_cache, v_cache, k_scale, v_scale, split_ws, out,
+               stream=None):
+    import torch
+    kp, vp, ksp, vsp = _kv_ptrs(cfg, k_cache, v_cache, k_scale, v_scale)
+    _check(load().lbp_attend(ctypes.byref(cfg), ctypes.byref(info), _ptr(plan_ws, "plan_ws"),
+                             _ptr(q, "q", torch.bfloat16), kp, vp, ksp, vsp,
+                             _ptr(split_ws, "split_ws"),
+                             split_ws.numel() * split_ws.element_size(),
+                             _ptr(out, "out", torch.bfloat16), _stream(stream)), "lbp_attend")
+
+
+def lbp_attend_partials(cfg, info, plan_ws, q, k_cache, v_cache, k_scale, v_scale, split_ws,
+                        stream=None):
+    import torch
+    kp, vp, ksp, vsp = _kv_ptrs(cfg, k_cache, v_cache, k_scale, v_scale)
+    _check(load().lbp_attend_partials(ctypes.byref(cfg), ctypes.byref(info),
+                                      _ptr(plan_ws, "plan_ws"), _ptr(q, "q", torch.bfloat16),
+                                      kp, vp, ksp, vsp, _ptr(split_ws, "split_ws"),
+                                      split_ws.numel() * split_ws.element_size(),
+                                      _stream(stream)), "lbp_attend_partials")
+
+
+def lbp_combine(cfg, info, plan_ws, split_ws, out, stream=None):
+    import torch
+    _check(load().lbp_combine(ctypes.byref(cfg), ctypes.byref(info), _ptr(plan_ws, "plan_ws"),
+                              _ptr(split_ws, "split_ws"),
+                              split_ws.numel() * split_ws.element_size(),
+                              _ptr(out, "out", torch.bfloat16), _stream(stream)), "lbp_combine")
+
+
+# ---------------------------------------------------------------------------
+# readers for host-side inspection (tests, benchmark)
+# ---------------------------------------------------------------------------
+
+def read_taskmap(plan_ws, info: lbp_plan_info) -> dict:
+    """Copy a plan workspace to the host and slice it by lbp_plan_layout."""
+    off = lbp_plan_layout(info)
+    raw = plan_ws.view(-1).view(dtype=__import__("torch").uint8)[:off.total].cpu().numpy()
+    words = raw.view(np.int32)
+    h = words[off.header // 4: off.header // 4 + 16]
+    D = int(h[7])
+    npairs = info.num_kv_heads * info.batch
+
+    def sl(o, n):
+        return words[o // 4: o // 4 + n].copy()
+
+    return {
+        "magic": int(np.uint32(h[0])), "policy": int(h[1]), "num_bins": int(h[2]),
+        "batch": int(h[3]), "num_kv_heads": int(h[4]),
+        "header": (int(h[5]), int(h[6]), int(h[7]), int(h[8])), "status": int(h[9]),
+        "bin_offset": sl(off.bin_offset, info.num_bins + 1),
+        "desc": sl(off.desc, 4 * D).reshape(D, 4),
+        "pair_first": sl(off.pair_first, npairs),
+        "pair_count": sl(off.pair_count, npairs),
+    }
+
+
+def split_views(split_ws, info: lbp_plan_info, group: int):
+    """(o_part [max_desc, G, 128], lse_part [max_desc, G]) fp32 views of a split buffer."""
+    import torch
+    flat = split_ws.view(-1).view(torch.uint8)
+    md = info.max_desc
+    o_bytes = md * group * HEAD_DIM * 4
+    lse_off = (o_bytes + 255) // 256 * 256
+    o = flat[:o_bytes].view(torch.float32).view(md, group, HEAD_DIM)
+    lse = flat[lse_off:lse_off + md * group * 4].view(torch.float32).view(md, group)
+    return o, lse

@@ -1,0 +1,362 @@
+// Persistent split-KV decode attention over a paged KV cache.
+//
+// Method (SGLang x HPC-Ops page, "Scheduling around live KV work", second
+// paragraph; vLLM x HPC-Ops page, bullet "Compute and combine"): one
+// resident workgroup per bin walks its task descriptors in order; for each
+// descriptor (KV head g, request r, tokens [a, e)) it computes attention of
+// the KV head's whole query group over those tokens and writes a partial
+// output with its log-sum-exp, then moves on to the next descriptor without
+// a relaunch.
+//
+// gfx950 mapping (our design, not the pages'):
+//  * A workgroup is 8 waves.  A descriptor's tokens are cut into 16-token
+//    slices (a slice never crosses a 64-token page because descriptors start
+//    on page boundaries); slice i goes to wave i % 8.  Each wave keeps its
+//    own running max, sum and output for the group, so there is no barrier
+//    inside a descriptor; the 8 states are merged through LDS at its end.
+//  * Scores use MFMA 16x16x32 bf16 with the 16 slice tokens as rows and the
+//    query heads as columns (S^T = K Q^T; G <= 16 heads, unused columns are
+//    zero).  P.V uses MFMA 16x16x16 bf16 as O^T = V^T P^T, whose B operand
+//    is exactly the score accumulator layout, so probabilities never leave
+//    registers.
+//  * K rows are loaded straight into the MFMA A layout (each lane 16 B of
+//    one token).  V is loaded 4 tokens x 256 contiguous bytes per
+//    instruction (lane = 8 dims of one token); the contraction over tokens
+//    is order-free and the output dims can be permuted, so lane c's 8 dims
+//    become the c-th row of 8 different 16-dim output blocks and only an
+//    in-register 16-bit pack is needed - no LDS transpose.
+//  * Every KV load is a buffer load whose resource covers only the slice's
+//    valid rows: rows past the descriptor's end read as zero and cost no
+//    memory traffic, which both masks the unused slots of a request's last
+//    page (they may hold NaN) and lets the prefetch of nonexistent slices be
+//    issued unconditionally, keeping the wait counts static.
+//  * Three slices are in flight per wave (one computing, two loading).
+//  * FP8 KV (OCP e4m3 codes with one fp32 scale per token and KV head): codes
+//    are widened to bf16 exactly in registers; the K scale multiplies the
+//    score of its token, the V scale is folded into the probability before
+//    the bf16 P.V product (sum_t p_t (c_t s_t) = sum_t (p_t s_t) c_t).
+#include "lbp_internal.h"
+
+namespace lbp {
+namespace {
+
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
+constexpr int kSlice = 16;
+constexpr int kRedRow = kHeadDim + 4;  // padded LDS row (floats) for the merge
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x2_t __attribute__((ext_vector_type(2)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// Raw (untyped) buffer, 32-bit data format, as the gfx9 buffer resource
+// word 3 requires for offset-addressed loads.
+constexpr int kRsrcWord3 = 0x00020000;
+
+__device__ inline rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kRsrcWord3);
+}
+
+__device__ inline uint32_t pack_bf16(float lo, float hi) {
+  bf16x2_t v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ inline float wave_max_across_groups(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16, 64));
+  x = fmaxf(x, __shfl_xor(x, 32, 64));
+  return x;
+}
+__device__ inline float wave_sum_across_groups(float x) {
+  x += __shfl_xor(x, 16, 64);
+  x += __shfl_xor(x, 32, 64);
+  return x;
+}
+
+// ---------------------------------------------------------------------------
+// KV formats
+// ---------------------------------------------------------------------------
+
+struct SliceRsrc {
+  rsrc_t k, v, ks, vs;
+};
+
+struct Bf16Kv {
+  static constexpr int kRowBytes = kHeadDim * 2;
+  static constexpr bool kScaled = false;
+  struct Buf {
+    i32x4_t k[4];   // K A-operand, one per 32-dim k-step
+    i32x4_t v[4];   // V rows 4*grp+i, dims [8c, 8c+8)
+  };
+  // Q B-operand for k-step s: dims [32s + 8grp, +8) of head n.
+  __device__ static int q_offset(int n, int grp, int s) { return n * 256 + 64 * s + 16 * grp; }
+
+  __device__ static void issue(Buf& b, const SliceRsrc& rs, int lane) {
+    const int m = lane & 15, grp = lane >> 4;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      b.k[s] = __builtin_amdgcn_raw_buffer_load_b128(rs.k, m * kRowBytes + 64 * s + 16 * grp, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      b.v[i] = __builtin_amdgcn_raw_buffer_load_b128(rs.v, (4 * grp + i) * kRowBytes + 16 * m, 0, 0);
+  }
+
+  __device__ static f32x4_t scores(const Buf& b, const bf16x8_t* qb) {
+    f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, b.k[k]), qb[k], s,
+                                                  0, 0, 0);
+    return s;
+  }
+  __device__ static f32x4_t k_scales(const Buf&) { return f32x4_t{1.f, 1.f, 1.f, 1.f}; }
+  __device__ static f32x4_t v_scales(const Buf&) { return f32x4_t{1.f, 1.f, 1.f, 1.f}; }
+
+  // A operand of output block mb (dims 8c + mb) over the slice's 16 tokens.
+  __device__ static i16x4_t v_operand(const Buf& b, int mb) {
+    const int w = mb >> 1;
+    uint32_t x0 = b.v[0][w], x1 = b.v[1][w], x2 = b.v[2][w], x3 = b.v[3][w];
+    uint32_t lo, hi;
+    if (mb & 1) {
+      lo = (x0 >> 16) | (x1 & 0xFFFF0000u);
+      hi = (x2 >> 16) | (x3 & 0xFFFF0000u);
+    } else {
+      lo = (x0 & 0xFFFFu) | (x1 << 16);
+      hi = (x2 & 0xFFFFu) | (x3 << 16);
+    }
+    i32x2_t r = {int(lo), int(hi)};
+    return __builtin_bit_cast(i16x4_t, r);
+  }
+};
+
+struct Fp8Kv {
+  static constexpr int kRowBytes = kHeadDim;
+  static constexpr bool kScaled = true;
+  struct Buf {
+    i32x4_t k[2];   // 32 codes: dims [32grp, 32grp + 32) of token m
+    i32x2_t v[4];   // 8 codes: dims [8c, 8c+8) of token 4grp+i
+    i32x4_t ks;     // k scales of tokens 4grp .. 4grp+3
+    i32x4_t vs;     // v scales of tokens 4grp .. 4grp+3
+  };
+  // Q B-operand for k-step s: dims [32grp + 8s, +8) of head n.
+  __device__ static int q_offset(int n, int grp, int s) { return n * 256 + 64 * grp + 16 * s; }
+
+  __device__ static void issue(Buf& b, const SliceRsrc& rs, int lane) {
+    const int m = lane & 15, grp = lane >> 4;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      b.k[h] = __builtin_amdgcn_raw_buffer_load_b128(rs.k, m * kRowBytes + 32 * grp + 16 * h, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      b.v[i] = __builtin_amdgcn_raw_buffer_load_b64(rs.v, (4 * grp + i) * kRowBytes + 8 * m, 0, 0);
+    b.ks = __builtin_amdgcn_raw_buffer_load_b128(rs.ks, 16 * grp, 0, 0);
+    b.vs = __builtin_amdgcn_raw_buffer_load_b128(rs.vs, 16 * grp, 0, 0);
+  }
+
+  // Two e4m3 codes (the low or high 16-bit word of `codes`) to two bf16, exactly.
+  template <bool kHiWord>
+  __device__ static uint32_t widen2(uint32_t codes) {
+    return __builtin_bit_cast(uint32_t,
+                              __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(int(codes), 1.0f, kHiWord));
+  }
+
+  __device__ static f32x4_t scores(const Buf& b, const bf16x8_t* qb) {
+    f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      uint32_t c0 = b.k[k >> 1][2 * (k & 1)], c1 = b.k[k >> 1][2 * (k & 1) + 1];
+      i32x4_t w = {int(widen2<false>(c0)), int(widen2<true>(c0)), int(widen2<false>(c1)),
+                   int(widen2<true>(c1))};
+      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, w), qb[k], s, 0,
+                                                  0, 0);
+    }
+    return s;
+  }
+  __device__ static f32x4_t k_scales(const Buf& b) { return __builtin_bit_cast(f32x4_t, b.ks); }
+  __device__ static f32x4_t v_scales(const Buf& b) { return __builtin_bit_cast(f32x4_t, b.vs); }
+
+  __device__ static i16x4_t v_operand(const Buf& b, int mb) {
+    const int h = mb >> 2;           // which dword of the 8 codes
+    const int k = mb & 3;            // byte inside it
+    // bytes {t0.bk, t1.bk, t0.bk+1, t1.bk+1} for the token pairs (0,1), (2,3)
+    const uint32_t sel = (k < 2) ? 0x05010400u : 0x07030602u;
+    uint32_t p01 = __builtin_amdgcn_perm(uint32_t(b.v[1][h]), uint32_t(b.v[0][h]), sel);
+    uint32_t p23 = __builtin_amdgcn_perm(uint32_t(b.v[3][h]), uint32_t(b.v[2][h]), sel);
+    i32x2_t r;
+    if (k & 1)
+      r = i32x2_t{int(widen2<true>(p01)), int(widen2<true>(p23))};
+    else
+      r = i32x2_t{int(widen2<false>(p01)), int(widen2<false>(p23))};
+    return __builtin_bit_cast(i16x4_t, r);
+  }
+};
+
+// ---------------------------------------------------------------------------
+// the kernel
+// ---------------------------------------------------------------------------
+
+template <class Kv>
+__device__ inline SliceRsrc slice_rsrc(const AttendArgs& a, int g, int r, int tok, int e) {
+  const bool valid = tok < e;
+  const int pidx = (valid ? tok : e - 1) >> 6;
+  const int page = a.page_table[int64_t(r) * a.page_table_stride + pidx];
+  const int nvalid = valid ? min(kSlice, e - tok) : 0;
+  const int64_t row = (int64_t(page) * a.num_kv_heads + g) * kPageTokens + (tok & (kPageTokens - 1));
+  SliceRsrc rs;
+  rs.k = make_rsrc(static_cast<const char*>(a.k_cache) + row * Kv::kRowBytes, nvalid * Kv::kRowBytes);
+  rs.v = make_rsrc(static_cast<const char*>(a.v_cache) + row * Kv::kRowBytes, nvalid * Kv::kRowBytes);
+  if constexpr (Kv::kScaled) {
+    rs.ks = make_rsrc(a.k_scale + row, nvalid * 4);
+    rs.vs = make_rsrc(a.v_scale + row, nvalid * 4);
+  } else {
+    rs.ks = rs.k;
+    rs.vs = rs.v;
+  }
+  return rs;
+}
+
+struct WaveState {
+  float m;          // running max of log2-scaled scores (per head n = lane & 15)
+  float l;          // this lane's share of the running sum
+  f32x4_t acc[8];   // O^T blocks: lane (grp, n) holds dims 32grp + 8j + mb
+};
+
+template <class Kv>
+__device__ inline void consume(WaveState& st, const typename Kv::Buf& b, const bf16x8_t* qb,
+                               int tok, int e, float scale_log2, int grp) {
+  f32x4_t s = Kv::scores(b, qb);
+  f32x4_t ks = Kv::k_scales(b);
+  f32x4_t vs = Kv::v_scales(b);
+  float x[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    x[j] = (tok + 4 * grp + j < e) ? s[j] * ks[j] * scale_log2 : -INFINITY;
+  float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+  mx = wave_max_across_groups(mx);
+  const float m_new = fmaxf(st.m, mx);
+  const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
+  st.m = m_new;
+  float p[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) p[j] = __builtin_amdgcn_exp2f(x[j] - m_new);
+  st.l = st.l * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+  i32x2_t pb2 = {int(pack_bf16(p[0] * vs[0], p[1] * vs[1])),
+                 int(pack_bf16(p[2] * vs[2], p[3] * vs[3]))};
+  const i16x4_t pb = __builtin_bit_cast(i16x4_t, pb2);
+#pragma unroll
+  for (int mb = 0; mb < 8; ++mb) {
+    st.acc[mb] *= alpha;
+    st.acc[mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(Kv::v_operand(b, mb), pb, st.acc[mb],
+                                                            0, 0, 0);
+  }
+}
+
+template <class Kv>
+__global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a) {
+  extern __shared__ float smem[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15;         // query head within the group (MFMA column)
+  const int grp = lane >> 4;
+  const int G = a.group;
+  const int red_stride = 32 + G * kRedRow;
+  float* red = smem + wave * red_stride;
+
+  const int bin = blockIdx.x;
+  const int d_begin = a.bin_offset[bin];
+  const int d_end = a.bin_offset[bin + 1];
+
+  for (int d = d_begin; d < d_end; ++d) {
+    const int4 ds = reinterpret_cast<const int4*>(a.desc)[d];
+    const int g = ds.x, r = ds.y, t_begin = ds.z, t_end = ds.w;
+
+    // query group of KV head g for request r as the MFMA B operand
+    const rsrc_t qr = make_rsrc(static_cast<const char*>(a.q) +
+                                    (int64_t(r) * a.num_q_heads + int64_t(g) * G) * kHeadDim * 2,
+                                G * kHeadDim * 2);
+    bf16x8_t qb[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      qb[s] = __builtin_bit_cast(bf16x8_t,
+                                 __builtin_amdgcn_raw_buffer_load_b128(qr, Kv::q_offset(n, grp, s), 0, 0));
+
+    WaveState st;
+    st.m = -INFINITY;
+    st.l = 0.f;
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) st.acc[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    const int step = kWaves * kSlice;
+    int tok = t_begin + wave * kSlice;
+    typename Kv::Buf b0, b1, b2;
+    Kv::issue(b0, slice_rsrc<Kv>(a, g, r, tok, t_end), lane);
+    Kv::issue(b1, slice_rsrc<Kv>(a, g, r, tok + step, t_end), lane);
+    while (tok < t_end) {
+      Kv::issue(b2, slice_rsrc<Kv>(a, g, r, tok + 2 * step, t_end), lane);
+      consume<Kv>(st, b0, qb, tok, t_end, a.scale_log2, grp);
+      tok += step;
+      if (tok >= t_end) break;
+      Kv::issue(b0, slice_rsrc<Kv>(a, g, r, tok + 2 * step, t_end), lane);
+      consume<Kv>(st, b1, qb, tok, t_end, a.scale_log2, grp);
+      tok += step;
+      if (tok >= t_end) break;
+      Kv::issue(b1, slice_rsrc<Kv>(a, g, r, tok + 2 * step, t_end), lane);
+      consume<Kv>(st, b2, qb, tok, t_end, a.scale_log2, grp);
+      tok += step;
+    }
+
+    // merge the 8 wave states of this descriptor
+    st.l = wave_sum_across_groups(st.l);
+    if (n < G) {
+      if (grp == 0) {
+        red[n] = st.m;
+        red[16 + n] = st.l;
+      }
+      float* orow = red + 32 + n * kRedRow + 32 * grp;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        *reinterpret_cast<f32x4_t*>(orow + 8 * j) =
+            f32x4_t{st.acc[0][j], st.acc[1][j], st.acc[2][j], st.acc[3][j]};
+        *reinterpret_cast<f32x4_t*>(orow + 8 * j + 4) =
+            f32x4_t{st.acc[4][j], st.acc[5][j], st.acc[6][j], st.acc[7][j]};
+      }
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < G * kHeadDim; idx += kThreads) {
+      const int q = idx >> 7, dim = idx & (kHeadDim - 1);
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, smem[w * red_stride + q]);
+      float L = 0.f, o = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float* rw = smem + w * red_stride;
+        const float c = __builtin_amdgcn_exp2f(rw[q] - M);
+        L += rw[16 + q] * c;
+        o += rw[32 + q * kRedRow + dim] * c;
+      }
+      a.o_part[(int64_t(d) * G + q) * kHeadDim + dim] = o / L;
+      if (dim == 0) a.lse_part[int64_t(d) * G + q] = M + __builtin_amdgcn_logf(L);
+    }
+    __syncthreads();
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attend(const AttendArgs& a, int kv_dtype, int num_bins, hipStream_t s) {
+  AttendArgs copy = a;
+  void* args[] = {&copy};
+  const size_t lds = size_t(kWaves) * (32 + a.group * kRedRow) * sizeof(float);
+  const void* fn = kv_dtype == LBP_KV_FP8_E4M3
+                       ? reinterpret_cast<const void*>(&attend_kernel<Fp8Kv>)
+                       : reinterpret_cast<const void*>(&attend_kernel<Bf16Kv>);
+  if (num_bins <= 0) return hipSuccess;
+  return hipLaunchKernel(fn, dim3(num_bins), dim3(kThreads), args, lds, s);
+}
+
+}  // namespace lbp

@@ -1,0 +1,297 @@
+// Host side of liblbp: argument guards, workspace sizing and launches.
+// Every entry point checks its arguments before touching the device and
+// never synchronises or copies between host and device.
+#include <math.h>
+#include <string.h>
+
+#include "lbp_internal.h"
+
+namespace lbp {
+namespace {
+
+constexpr int kMaxDevices = 64;
+int g_cu_count[kMaxDevices];  // cached per device; 0 = not queried yet
+
+lbp_status cu_count(int* out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return LBP_ERR_HIP;
+  if (dev < kMaxDevices && g_cu_count[dev] > 0) {
+    *out = g_cu_count[dev];
+    return LBP_OK;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return LBP_ERR_HIP;
+  if (dev < kMaxDevices) g_cu_count[dev] = n;
+  *out = n;
+  return LBP_OK;
+}
+
+lbp_status check_config(const lbp_config* c) {
+  if (!c) return LBP_ERR_INVALID_ARG;
+  if (c->head_dim != kHeadDim || c->page_size != kPageTokens) return LBP_ERR_UNSUPPORTED;
+  if (c->num_q_heads < 1 || c->num_kv_heads < 1) return LBP_ERR_INVALID_ARG;
+  if (c->num_q_heads % c->num_kv_heads != 0) return LBP_ERR_INVALID_ARG;
+  if (c->num_q_heads / c->num_kv_heads > kMaxGroup) return LBP_ERR_UNSUPPORTED;
+  if (c->max_batch < 1 || c->max_pages_per_seq < 1) return LBP_ERR_INVALID_ARG;
+  if (c->num_workgroups < 0 || c->min_tiles_per_bin < 0) return LBP_ERR_INVALID_ARG;
+  if (c->kv_dtype != LBP_KV_BF16 && c->kv_dtype != LBP_KV_FP8_E4M3) return LBP_ERR_UNSUPPORTED;
+  if (!(c->sm_scale > 0.f) || !isfinite(c->sm_scale)) return LBP_ERR_INVALID_ARG;
+  // all tile, token and descriptor counts must fit in int32
+  const int64_t pairs = int64_t(c->num_kv_heads) * c->max_batch;
+  if (int64_t(c->max_pages_per_seq) * kPageTokens > INT32_MAX / 2) return LBP_ERR_UNSUPPORTED;
+  if (pairs * c->max_pages_per_seq > INT32_MAX / 2) return LBP_ERR_UNSUPPORTED;
+  if (c->num_workgroups > (1 << 20)) return LBP_ERR_UNSUPPORTED;
+  return LBP_OK;
+}
+
+lbp_status resolve_bins(const lbp_config* c, int* W) {
+  if (c->num_workgroups > 0) {
+    *W = c->num_workgroups;
+    return LBP_OK;
+  }
+  return cu_count(W);
+}
+
+// Grid and descriptor capacity of a (policy, param) at a given batch.
+lbp_status plan_shape(const lbp_config* c, int policy, int param, int batch, int* num_bins,
+                      int* max_desc, int* splits_per_pair, int* used_param) {
+  const int64_t pairs = int64_t(c->num_kv_heads) * batch;
+  if (policy == LBP_POLICY_DYNAMIC) {
+    int W;
+    lbp_status st = resolve_bins(c, &W);
+    if (st != LBP_OK) return st;
+    int F = param > 0 ? param : (c->min_tiles_per_bin > 0 ? c->min_tiles_per_bin : kDefaultMinTiles);
+    if (param < 0) return LBP_ERR_INVALID_ARG;
+    *num_bins = W;
+    *max_desc = int(pairs + W - 1);   // a boundary between bins adds at most one descriptor
+    *splits_per_pair = 0;
+    *used_param = F;
+    return LBP_OK;
+  }
+  if (param < 1) return LBP_ERR_INVALID_ARG;
+  int S;
+  if (policy == LBP_POLICY_STATIC_SPLITS) {
+    if (param > 4096) return LBP_ERR_UNSUPPORTED;
+    S = param;
+  } else if (policy == LBP_POLICY_STATIC_CHUNK) {
+    S = (c->max_pages_per_seq + param - 1) / param;
+  } else {
+    return LBP_ERR_INVALID_ARG;
+  }
+  if (pairs * S > INT32_MAX / 4) return LBP_ERR_UNSUPPORTED;
+  *num_bins = int(pairs * S);
+  *max_desc = int(pairs * S);
+  *splits_per_pair = S;
+  *used_param = param;
+  return LBP_OK;
+}
+
+lbp_status check_info(const lbp_config* c, const lbp_plan_info* info) {
+  if (!info || info->magic != LBP_PLAN_MAGIC) return LBP_ERR_MISMATCH;
+  if (info->num_kv_heads != c->num_kv_heads || info->num_q_heads != c->num_q_heads)
+    return LBP_ERR_MISMATCH;
+  if (info->batch < 1 || info->batch > c->max_batch) return LBP_ERR_MISMATCH;
+  if (info->num_bins < 1 || info->max_desc < 0 || !info->page_table_dev) return LBP_ERR_MISMATCH;
+  return LBP_OK;
+}
+
+lbp_status build_plan(const lbp_config* cfg, int policy, int param, const int32_t* seq_lens,
+                      int32_t batch, const int32_t* page_table, int64_t stride, void* ws,
+                      size_t ws_bytes, lbp_plan_info* info, void* stream) {
+  lbp_status st = check_config(cfg);
+  if (st != LBP_OK) return st;
+  if (!seq_lens || !page_table || !ws || !info) return LBP_ERR_INVALID_ARG;
+  if (batch < 1 || batch > cfg->max_batch) return LBP_ERR_INVALID_ARG;
+  if (stride < cfg->max_pages_per_seq) return LBP_ERR_INVALID_ARG;
+  int num_bins, max_desc, spp, used;
+  st = plan_shape(cfg, policy, param, batch, &num_bins, &max_desc, &spp, &used);
+  if (st != LBP_OK) return st;
+  const int npairs = cfg->num_kv_heads * batch;
+  const lbp_plan_offsets off = plan_layout(num_bins, max_desc, npairs);
+  if (ws_bytes < off.total) return LBP_ERR_WORKSPACE_TOO_SMALL;
+
+  char* base = static_cast<char*>(ws);
+  PlanArgs a;
+  a.seq_lens = seq_lens;
+  a.batch = batch;
+  a.num_kv_heads = cfg->num_kv_heads;
+  a.num_bins = num_bins;
+  a.policy = policy;
+  a.param = used;
+  a.splits_per_pair = spp;
+  a.max_tokens = cfg->max_pages_per_seq * kPageTokens;
+  a.header = reinterpret_cast<int32_t*>(base + off.header);
+  a.bin_offset = reinterpret_cast<int32_t*>(base + off.bin_offset);
+  a.desc = reinterpret_cast<int32_t*>(base + off.desc);
+  a.pair_first = reinterpret_cast<int32_t*>(base + off.pair_first);
+  a.pair_count = reinterpret_cast<int32_t*>(base + off.pair_count);
+  a.scratch = reinterpret_cast<int32_t*>(base + off.scratch);
+  if (launch_plan(a, static_cast<hipStream_t>(stream)) != hipSuccess) return LBP_ERR_HIP;
+
+  lbp_plan_info out;
+  memset(&out, 0, sizeof(out));
+  out.magic = LBP_PLAN_MAGIC;
+  out.policy = policy;
+  out.param = used;
+  out.batch = batch;
+  out.num_kv_heads = cfg->num_kv_heads;
+  out.num_q_heads = cfg->num_q_heads;
+  out.num_bins = num_bins;
+  out.max_desc = max_desc;
+  out.plan_bytes = off.total;
+  out.page_table_dev = page_table;
+  out.page_table_stride = stride;
+  *info = out;
+  return LBP_OK;
+}
+
+lbp_plan_offsets offsets_of(const lbp_plan_info* info) {
+  return plan_layout(info->num_bins, info->max_desc, info->num_kv_heads * info->batch);
+}
+
+lbp_status check_split(const lbp_config* cfg, const lbp_plan_info* info, size_t bytes) {
+  const int G = cfg->num_q_heads / cfg->num_kv_heads;
+  return bytes < split_bytes(info->max_desc, G) ? LBP_ERR_WORKSPACE_TOO_SMALL : LBP_OK;
+}
+
+}  // namespace
+}  // namespace lbp
+
+using namespace lbp;
+
+extern "C" {
+
+const char* lbp_status_string(lbp_status s) {
+  switch (s) {
+    case LBP_OK: return "LBP_OK";
+    case LBP_ERR_INVALID_ARG: return "LBP_ERR_INVALID_ARG";
+    case LBP_ERR_UNSUPPORTED: return "LBP_ERR_UNSUPPORTED";
+    case LBP_ERR_WORKSPACE_TOO_SMALL: return "LBP_ERR_WORKSPACE_TOO_SMALL";
+    case LBP_ERR_MISMATCH: return "LBP_ERR_MISMATCH";
+    case LBP_ERR_HIP: return "LBP_ERR_HIP";
+  }
+  return "LBP_ERR_UNKNOWN";
+}
+
+int32_t lbp_version(void) { return LBP_VERSION; }
+
+lbp_status lbp_query_workspace(const lbp_config* cfg, int32_t policy, int32_t param,
+                               size_t* plan_bytes, size_t* split_ws) {
+  lbp_status st = check_config(cfg);
+  if (st != LBP_OK) return st;
+  if (!plan_bytes || !split_ws) return LBP_ERR_INVALID_ARG;
+  int num_bins, max_desc, spp, used;
+  st = plan_shape(cfg, policy, param, cfg->max_batch, &num_bins, &max_desc, &spp, &used);
+  if (st != LBP_OK) return st;
+  *plan_bytes = plan_layout(num_bins, max_desc, cfg->num_kv_heads * cfg->max_batch).total;
+  *split_ws = split_bytes(max_desc, cfg->num_q_heads / cfg->num_kv_heads);
+  return LBP_OK;
+}
+
+lbp_status lbp_plan(const lbp_config* cfg, const int32_t* seq_lens_dev, int32_t batch,
+                    const int32_t* page_table_dev, int64_t page_table_stride, void* plan_ws_dev,
+                    size_t plan_ws_bytes, lbp_plan_info* info, void* stream) {
+  const int F = cfg && cfg->min_tiles_per_bin > 0 ? cfg->min_tiles_per_bin : kDefaultMinTiles;
+  return build_plan(cfg, LBP_POLICY_DYNAMIC, F, seq_lens_dev, batch, page_table_dev,
+                    page_table_stride, plan_ws_dev, plan_ws_bytes, info, stream);
+}
+
+lbp_status lbp_plan_static(const lbp_config* cfg, int32_t policy, int32_t param,
+                           const int32_t* seq_lens_dev, int32_t batch,
+                           const int32_t* page_table_dev, int64_t page_table_stride,
+                           void* plan_ws_dev, size_t plan_ws_bytes, lbp_plan_info* info,
+                           void* stream) {
+  if (policy != LBP_POLICY_STATIC_SPLITS && policy != LBP_POLICY_STATIC_CHUNK)
+    return LBP_ERR_INVALID_ARG;
+  return build_plan(cfg, policy, param, seq_lens_dev, batch, page_table_dev, page_table_stride,
+                    plan_ws_dev, plan_ws_bytes, info, stream);
+}
+
+lbp_status lbp_plan_layout(const lbp_plan_info* info, lbp_plan_offsets* offsets) {
+  if (!info || !offsets) return LBP_ERR_INVALID_ARG;
+  if (info->magic != LBP_PLAN_MAGIC) return LBP_ERR_MISMATCH;
+  *offsets = offsets_of(info);
+  return LBP_OK;
+}
+
+lbp_status lbp_attend_partials(const lbp_config* cfg, const lbp_plan_info* info,
+                               const void* plan_ws_dev, const void* q_dev,
+                               const void* k_cache_dev, const void* v_cache_dev,
+                               const float* k_scale_dev, const float* v_scale_dev,
+                               void* split_ws_dev, size_t split_ws_bytes, void* stream) {
+  lbp_status st = check_config(cfg);
+  if (st != LBP_OK) return st;
+  if ((st = check_info(cfg, info)) != LBP_OK) return st;
+  if (!plan_ws_dev || !q_dev || !k_cache_dev || !v_cache_dev || !split_ws_dev)
+    return LBP_ERR_INVALID_ARG;
+  if (cfg->kv_dtype == LBP_KV_FP8_E4M3 && (!k_scale_dev || !v_scale_dev))
+    return LBP_ERR_INVALID_ARG;
+  if ((st = check_split(cfg, info, split_ws_bytes)) != LBP_OK) return st;
+
+  const lbp_plan_offsets off = offsets_of(info);
+  const char* pb = static_cast<const char*>(plan_ws_dev);
+  const int G = cfg->num_q_heads / cfg->num_kv_heads;
+  AttendArgs a;
+  a.bin_offset = reinterpret_cast<const int32_t*>(pb + off.bin_offset);
+  a.desc = reinterpret_cast<const int32_t*>(pb + off.desc);
+  a.page_table = info->page_table_dev;
+  a.page_table_stride = info->page_table_stride;
+  a.q = q_dev;
+  a.k_cache = k_cache_dev;
+  a.v_cache = v_cache_dev;
+  a.k_scale = cfg->kv_dtype == LBP_KV_FP8_E4M3 ? k_scale_dev : nullptr;
+  a.v_scale = cfg->kv_dtype == LBP_KV_FP8_E4M3 ? v_scale_dev : nullptr;
+  a.o_part = static_cast<float*>(split_ws_dev);
+  a.lse_part = reinterpret_cast<float*>(static_cast<char*>(split_ws_dev) +
+                                        split_lse_offset(info->max_desc, G));
+  a.num_q_heads = cfg->num_q_heads;
+  a.num_kv_heads = cfg->num_kv_heads;
+  a.group = G;
+  a.scale_log2 = cfg->sm_scale * 1.4426950408889634f;
+  if (launch_attend(a, cfg->kv_dtype, info->num_bins, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return LBP_ERR_HIP;
+  return LBP_OK;
+}
+
+lbp_status lbp_combine(const lbp_config* cfg, const lbp_plan_info* info, const void* plan_ws_dev,
+                       const void* split_ws_dev, size_t split_ws_bytes, void* out_dev,
+                       void* stream) {
+  lbp_status st = check_config(cfg);
+  if (st != LBP_OK) return st;
+  if ((st = check_info(cfg, info)) != LBP_OK) return st;
+  if (!plan_ws_dev || !split_ws_dev || !out_dev) return LBP_ERR_INVALID_ARG;
+  if ((st = check_split(cfg, info, split_ws_bytes)) != LBP_OK) return st;
+  const lbp_plan_offsets off = offsets_of(info);
+  const char* pb = static_cast<const char*>(plan_ws_dev);
+  const int G = cfg->num_q_heads / cfg->num_kv_heads;
+  CombineArgs a;
+  a.pair_first = reinterpret_cast<const int32_t*>(pb + off.pair_first);
+  a.pair_count = reinterpret_cast<const int32_t*>(pb + off.pair_count);
+  a.o_part = static_cast<const float*>(split_ws_dev);
+  a.lse_part = reinterpret_cast<const float*>(static_cast<const char*>(split_ws_dev) +
+                                              split_lse_offset(info->max_desc, G));
+  a.out = out_dev;
+  a.batch = info->batch;
+  a.num_q_heads = cfg->num_q_heads;
+  a.num_kv_heads = cfg->num_kv_heads;
+  a.group = G;
+  if (launch_combine(a, cfg->num_kv_heads * info->batch, static_cast<hipStream_t>(stream)) !=
+      hipSuccess)
+    return LBP_ERR_HIP;
+  return LBP_OK;
+}
+
+lbp_status lbp_attend(const lbp_config* cfg, const lbp_plan_info* info, const void* plan_ws_dev,
+                      const void* q_dev, const void* k_cache_dev, const void* v_cache_dev,
+                      const float* k_scale_dev, const float* v_scale_dev, void* split_ws_dev,
+                      size_t split_ws_bytes, void* out_dev, void* stream) {
+  if (!out_dev) return LBP_ERR_INVALID_ARG;
+  lbp_status st = lbp_attend_partials(cfg, info, plan_ws_dev, q_dev, k_cache_dev, v_cache_dev,
+                                      k_scale_dev, v_scale_dev, split_ws_dev, split_ws_bytes,
+                                      stream);
+  if (st != LBP_OK) return st;
+  return lbp_combine(cfg, info, plan_ws_dev, split_ws_dev, split_ws_bytes, out_dev, stream);
+}
+
+}  // extern "C"

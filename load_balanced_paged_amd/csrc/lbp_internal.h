@@ -1,0 +1,91 @@
+// Internal definitions shared by the host API and the HIP kernels of liblbp.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "lbp.h"
+
+namespace lbp {
+
+constexpr int kHeadDim = LBP_HEAD_DIM;   // 128
+constexpr int kPageTokens = LBP_PAGE_SIZE;  // 64: one page is one scheduling tile
+constexpr int kMaxGroup = LBP_MAX_GROUP;    // query heads per KV head, padded to 16 MFMA rows
+constexpr int kDefaultMinTiles = 4;         // F, the minimum-work floor (tiles per bin)
+
+// header word indices inside the plan workspace
+enum HeaderWord {
+  kHdrMagic = 0, kHdrPolicy = 1, kHdrNumBins = 2, kHdrBatch = 3, kHdrKvHeads = 4,
+  kHdrTiles = 5, kHdrBudget = 6, kHdrDesc = 7, kHdrUsedBins = 8, kHdrStatus = 9,
+  kHdrWords = 16
+};
+constexpr int kStatusClamped = 1;
+
+inline uint64_t align_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
+
+// Byte layout of the task map for one plan.
+inline lbp_plan_offsets plan_layout(int num_bins, int max_desc, int npairs) {
+  lbp_plan_offsets o;
+  o.header = 0;
+  o.bin_offset = align_up(o.header + kHdrWords * 4, 64);
+  o.desc = align_up(o.bin_offset + uint64_t(num_bins + 1) * 4, 64);
+  o.pair_first = align_up(o.desc + uint64_t(max_desc) * 16, 64);
+  o.pair_count = align_up(o.pair_first + uint64_t(npairs) * 4, 64);
+  o.scratch = align_up(o.pair_count + uint64_t(npairs) * 4, 64);
+  o.total = align_up(o.scratch + uint64_t(npairs) * 4, 256);
+  return o;
+}
+
+// Split buffer: o_part[max_desc][G][128] fp32, then lse_part[max_desc][G] fp32.
+inline uint64_t split_lse_offset(int max_desc, int group) {
+  return align_up(uint64_t(max_desc) * group * kHeadDim * 4, 256);
+}
+inline uint64_t split_bytes(int max_desc, int group) {
+  return align_up(split_lse_offset(max_desc, group) + uint64_t(max_desc) * group * 4, 256);
+}
+
+struct PlanArgs {
+  const int32_t* seq_lens;
+  int32_t batch, num_kv_heads, num_bins, policy, param;
+  int32_t splits_per_pair;   // static policies: bins per pair
+  int32_t max_tokens;        // 64 * max_pages_per_seq
+  int32_t* header;
+  int32_t* bin_offset;
+  int32_t* desc;             // [max_desc][4]
+  int32_t* pair_first;
+  int32_t* pair_count;
+  int32_t* scratch;          // first flat tile of every pair (dynamic)
+};
+
+struct AttendArgs {
+  const int32_t* bin_offset;
+  const int32_t* desc;
+  const int32_t* page_table;
+  int64_t page_table_stride;
+  const void* q;             // [B][Hq][128] bf16
+  const void* k_cache;       // [P][H_kv][64][128] bf16 or e4m3
+  const void* v_cache;
+  const float* k_scale;      // [P][H_kv][64] (FP8 only)
+  const float* v_scale;
+  float* o_part;             // [max_desc][G][128]
+  float* lse_part;           // [max_desc][G]
+  int32_t num_q_heads, num_kv_heads, group;
+  float scale_log2;          // sm_scale * log2(e)
+};
+
+struct CombineArgs {
+  const int32_t* pair_first;
+  const int32_t* pair_count;
+  const float* o_part;
+  const float* lse_part;
+  void* out;                 // [B][Hq][128] bf16
+  int32_t batch, num_q_heads, num_kv_heads, group;
+};
+
+// Launchers (defined next to their kernels).  Each returns the HIP error of
+// the launch itself.
+hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
+hipError_t launch_attend(const AttendArgs& a, int kv_dtype, int num_bins, hipStream_t s);
+hipError_t launch_combine(const CombineArgs& a, int npairs, hipStream_t s);
+
+}  // namespace lbp

@@ -1,0 +1,191 @@
+"""Shared set-up for the GPU parity tests.
+
+Builds seeded workloads on the device, runs the HIP path through the C ABI
+(via the ctypes binding) and computes the CPU oracle's answer on host copies
+of the very same tensors.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+import math
+import sys
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+import load_balanced_paged_amd as lbp
+import oracle
+from workloads import WorkloadConfig, make_workload, poison_tail_slots
+
+BF16_MAX_ABS = 1e-2
+BF16_REL_RMS = 5e-3
+FP8_MAX_ABS = 3e-2
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@dataclasses.dataclass
+class Case:
+    wcfg: WorkloadConfig
+    wl: object
+    cfg: lbp.lbp_config
+    seq_lens: torch.Tensor
+    page_table: torch.Tensor
+    plan_ws: torch.Tensor
+    split_ws: torch.Tensor
+    info: Optional[lbp.lbp_plan_info] = None
+
+    @property
+    def G(self):
+        return self.wcfg.group
+
+
+def build_case(wcfg: WorkloadConfig, layers: int = 1, lengths: Optional[Sequence[int]] = None,
+               num_workgroups: int = 0, min_tiles: int = 4, poison: bool = True,
+               policy: int = lbp.LBP_POLICY_DYNAMIC, param: int = 0,
+               max_pages_per_seq: Optional[int] = None) -> Case:
+    say(f"[case] {wcfg.name} B={wcfg.batch if lengths is None else len(lengths)} "
+        f"Hq={wcfg.num_q_heads} Hkv={wcfg.num_kv_heads} kv={wcfg.kv_dtype} layers={layers} "
+        f"W={num_workgroups} F={min_tiles} policy={policy} param={param}")
+    wl = make_workload(wcfg, device="cuda", layers=layers, lengths=lengths)
+    if poison:
+        for layer in wl.layers:
+            poison_tail_slots(layer, wl.lengths, wl.page_table)
+    mp = max_pages_per_seq or wl.page_table.shape[1]
+    table = np.zeros((len(wl.lengths), mp), dtype=np.int32)
+    table[:, :wl.page_table.shape[1]] = wl.page_table
+    cfg = lbp.make_config(wcfg.num_q_heads, wcfg.num_kv_heads, len(wl.lengths), mp,
+                          kv_dtype=wcfg.kv_dtype, num_workgroups=num_workgroups,
+                          min_tiles_per_bin=min_tiles, sm_scale=wcfg.sm_scale)
+    pb, sb = lbp.lbp_query_workspace(cfg, policy, param)
+    case = Case(wcfg, wl, cfg,
+                torch.from_numpy(np.asarray(wl.lengths, dtype=np.int32)).cuda(),
+                torch.from_numpy(table).cuda(),
+                torch.zeros(pb, dtype=torch.uint8, device="cuda"),
+                torch.zeros(sb, dtype=torch.uint8, device="cuda"))
+    if policy == lbp.LBP_POLICY_DYNAMIC:
+        case.info = lbp.lbp_plan(cfg, case.seq_lens, case.page_table, case.plan_ws)
+    else:
+        case.info = lbp.lbp_plan_static(cfg, policy, param, case.seq_lens, case.page_table,
+                                        case.plan_ws)
+    return case
+
+
+def run_attend(case: Case, layer: int = 0, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    L = case.wl.layers[layer]
+    if out is None:
+        out = torch.empty_like(L.q)
+    lbp.lbp_attend(case.cfg, case.info, case.plan_ws, L.q, L.k_cache, L.v_cache, L.k_scale,
+                   L.v_scale, case.split_ws, out)
+    torch.cuda.synchronize()
+    return out
+
+
+def bf16_to_f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().to(torch.float64).cpu().numpy()
+
+
+def bits(t: torch.Tensor) -> np.ndarray:
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def oracle_taskmap(case: Case):
+    info = case.info
+    L = np.asarray(case.wl.lengths)
+    H = case.wcfg.num_kv_heads
+    if info.policy == lbp.LBP_POLICY_DYNAMIC:
+        return oracle.assign.assign_dynamic(L, H, info.num_bins, info.param)
+    if info.policy == lbp.LBP_POLICY_STATIC_SPLITS:
+        return oracle.assign.assign_static_splits(L, H, info.param)
+    return oracle.assign.assign_static_chunk(L, H, info.param, case.cfg.max_pages_per_seq)
+
+
+def assert_taskmap_matches(case: Case):
+    got = lbp.read_taskmap(case.plan_ws, case.info)
+    ref = oracle_taskmap(case)
+    assert got["magic"] == lbp.LBP_PLAN_MAGIC
+    assert got["status"] == 0
+    assert got["num_bins"] == ref.num_bins == case.info.num_bins
+    assert got["header"] == ref.header(), (got["header"], ref.header())
+    assert np.array_equal(got["bin_offset"], ref.bin_offset)
+    assert np.array_equal(got["desc"], ref.desc)
+    assert np.array_equal(got["pair_first"], ref.pair_first)
+    assert np.array_equal(got["pair_count"], ref.pair_count)
+    return got, ref
+
+
+def oracle_pairs(case: Case, layer: int, pairs):
+    """fp64 oracle output rows for (kv_head, request) pairs, from host copies.
+
+    The pages of each sampled request are gathered on the device into a
+    compact cache (identity page table) before the host copy, so only the
+    bytes the sampled pairs need cross PCIe; the oracle then does its own
+    per-token page and slot indexing on that cache.
+    """
+    Lyr = case.wl.layers[layer]
+    G = case.G
+    fp8 = case.wcfg.kv_dtype == "fp8_e4m3"
+    res = {}
+    for g, r in pairs:
+        Lr = int(case.wl.lengths[r])
+        n = max(1, (Lr + 63) // 64)
+        pages = case.page_table[r, :n].long()
+        kc = Lyr.k_cache.index_select(0, pages)[:, g:g + 1].contiguous()
+        vc = Lyr.v_cache.index_select(0, pages)[:, g:g + 1].contiguous()
+        q = oracle.attention.bf16_bits_to_f64(bits(Lyr.q[r:r + 1, g * G:(g + 1) * G]))
+        table = np.arange(n, dtype=np.int32)[None]
+        if fp8:
+            ks = Lyr.k_scale.index_select(0, pages)[:, g:g + 1].contiguous().cpu().numpy()
+            vs = Lyr.v_scale.index_select(0, pages)[:, g:g + 1].contiguous().cpu().numpy()
+            o, lse = oracle.attention.paged_decode_attention(
+                q, kc.cpu().numpy(), vc.cpu().numpy(), table, [Lr], 1, case.wcfg.sm_scale,
+                kv_dtype="fp8_e4m3", k_scale=ks, v_scale=vs)
+        else:
+            o, lse = oracle.attention.paged_decode_attention(
+                q, bits(kc), bits(vc), table, [Lr], 1, case.wcfg.sm_scale)
+        if Lr == 0:
+            o = np.zeros_like(o)   # a pair with no tokens outputs zeros
+        res[(g, r)] = o[0]
+    return res
+
+
+def compare(case: Case, got: torch.Tensor, ref_rows: dict, what=""):
+    """Stack the sampled pairs and apply the tolerance of the KV dtype."""
+    G = case.G
+    gv = bf16_to_f64(got)
+    a, b = [], []
+    for (g, r), ref in ref_rows.items():
+        a.append(gv[r, g * G:(g + 1) * G])
+        b.append(ref)
+    a, b = np.stack(a), np.stack(b)
+    assert np.all(np.isfinite(a)), f"{what}: non-finite output"
+    diff = a - b
+    max_abs = float(np.max(np.abs(diff)))
+    rel_rms = float(np.linalg.norm(diff) / max(np.linalg.norm(b), 1e-30))
+    say(f"[parity] {what}: pairs={len(ref_rows)} max_abs={max_abs:.3e} rel_rms={rel_rms:.3e}")
+    if case.wcfg.kv_dtype == "bf16":
+        assert max_abs <= BF16_MAX_ABS, (what, max_abs)
+        assert rel_rms <= BF16_REL_RMS, (what, rel_rms)
+    else:
+        assert max_abs <= FP8_MAX_ABS, (what, max_abs)
+    return max_abs, rel_rms
+
+
+def sample_pairs(case: Case, k: int, seed: int = 0):
+    """The longest and shortest requests of every KV head plus a seeded sample."""
+    L = np.asarray(case.wl.lengths)
+    H = case.wcfg.num_kv_heads
+    rng = np.random.default_rng(seed)
+    pairs = {(0, int(np.argmax(L))), (H - 1, int(np.argmin(L))), (H // 2, int(np.argmax(L)))}
+    while len(pairs) < min(k, H * len(L)):
+        pairs.add((int(rng.integers(H)), int(rng.integers(len(L)))))
+    return sorted(pairs)
+
+
+def all_pairs(case: Case):
+    return [(g, r) for g in range(case.wcfg.num_kv_heads) for r in range(len(case.wl.lengths))]

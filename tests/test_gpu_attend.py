@@ -1,0 +1,140 @@
+"""GPU parity of the attention path (persistent kernel + combine) against the oracle.
+
+Tolerances: BF16 KV max-abs <= 1e-2 and relative RMS <= 5e-3; FP8 KV max-abs
+<= 3e-2.  Unused slots of every request's last page hold NaN.
+"""
+
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import load_balanced_paged_amd as lbp
+import oracle
+from gpu_support import (all_pairs, assert_taskmap_matches, bf16_to_f64, bits, build_case,
+                         compare, oracle_pairs, run_attend, sample_pairs, say)
+from workloads import CONFIGS
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("name", ["tiny", "uniform", "skewed"])
+def test_attend_full_parity(gpu_lib, name):
+    """Every output row against the oracle (these three fit the oracle in seconds)."""
+    case = build_case(CONFIGS[name])
+    assert_taskmap_matches(case)
+    out = run_attend(case)
+    compare(case, out, oracle_pairs(case, 0, all_pairs(case)), name)
+
+
+def test_attend_mixed_eight_layers(gpu_lib):
+    """One task map reused by 8 layers with different KV; sampled pairs per layer."""
+    case = build_case(CONFIGS["mixed"], layers=8)
+    assert_taskmap_matches(case)
+    pairs = sample_pairs(case, 12)
+    outs = [run_attend(case, layer) for layer in range(8)]
+    for layer in (0, 3, 7):
+        compare(case, outs[layer], oracle_pairs(case, layer, pairs), f"mixed layer {layer}")
+    assert not torch.equal(outs[0], outs[7])
+
+
+def test_attend_fp8_parity(gpu_lib):
+    case = build_case(CONFIGS["fp8"])
+    assert_taskmap_matches(case)
+    out = run_attend(case)
+    compare(case, out, oracle_pairs(case, 0, sample_pairs(case, 12)), "fp8")
+
+
+def test_attend_fp8_small_full(gpu_lib):
+    """FP8 KV on a small ragged batch, every row."""
+    wcfg = dataclasses.replace(CONFIGS["fp8"], name="fp8-small", batch=6)
+    case = build_case(wcfg, lengths=[1, 17, 64, 65, 700, 3000])
+    out = run_attend(case)
+    compare(case, out, oracle_pairs(case, 0, all_pairs(case)), "fp8-small")
+
+
+@pytest.mark.parametrize("group,hkv", [(1, 4), (4, 2), (16, 1), (3, 3)])
+def test_attend_group_sizes(gpu_lib, group, hkv):
+    wcfg = dataclasses.replace(CONFIGS["tiny"], name=f"g{group}", batch=5,
+                               num_q_heads=group * hkv, num_kv_heads=hkv)
+    case = build_case(wcfg, lengths=[33, 1, 128, 129, 900], num_workgroups=7, min_tiles=1)
+    out = run_attend(case)
+    compare(case, out, oracle_pairs(case, 0, all_pairs(case)), f"group {group} hkv {hkv}")
+
+
+def test_attend_length_one_is_exact(gpu_lib):
+    """With one token the softmax weight is exactly 1, so out == v_0 bit for bit."""
+    wcfg = dataclasses.replace(CONFIGS["tiny"], name="len1", batch=3)
+    case = build_case(wcfg, lengths=[1, 1, 1])
+    out = run_attend(case)
+    lay = case.wl.layers[0]
+    for r in range(3):
+        page = int(case.wl.page_table[r, 0])
+        v0 = lay.v_cache[page, 0, 0]
+        assert torch.equal(out[r], v0.expand(8, -1)), r
+
+
+def test_attend_zero_length_requests(gpu_lib):
+    wcfg = dataclasses.replace(CONFIGS["tiny"], name="zeros", batch=4)
+    case = build_case(wcfg, lengths=[0, 300, 0, 5], num_workgroups=3, min_tiles=1)
+    assert_taskmap_matches(case)
+    out = run_attend(case)
+    assert torch.all(out[0] == 0) and torch.all(out[2] == 0)
+    compare(case, out, oracle_pairs(case, 0, all_pairs(case)), "zero-length")
+
+
+@pytest.mark.parametrize("W,F", [(1, 1), (5, 1), (64, 1), (256, 4), (1024, 1)])
+def test_attend_bin_shapes(gpu_lib, W, F):
+    """Many splits per pair, one bin for everything, more bins than tiles."""
+    case = build_case(CONFIGS["tiny"], num_workgroups=W, min_tiles=F)
+    assert_taskmap_matches(case)
+    out = run_attend(case)
+    compare(case, out, oracle_pairs(case, 0, all_pairs(case)), f"tiny W={W} F={F}")
+
+
+@pytest.mark.parametrize("policy,param", [(lbp.LBP_POLICY_STATIC_SPLITS, 1),
+                                          (lbp.LBP_POLICY_STATIC_SPLITS, 7),
+                                          (lbp.LBP_POLICY_STATIC_CHUNK, 2)])
+def test_attend_static_plans(gpu_lib, policy, param):
+    case = build_case(CONFIGS["skewed"], policy=policy, param=param)
+    assert_taskmap_matches(case)
+    out = run_attend(case)
+    compare(case, out, oracle_pairs(case, 0, all_pairs(case)), f"skewed static {policy}/{param}")
+
+
+def test_attend_deterministic(gpu_lib):
+    case = build_case(CONFIGS["skewed"])
+    a = run_attend(case).clone()
+    b = run_attend(case).clone()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_partials_match_oracle_ranges(gpu_lib):
+    """Split-buffer contents per descriptor against the oracle's per-range attention."""
+    case = build_case(CONFIGS["tiny"], num_workgroups=5, min_tiles=1)
+    lay = case.wl.layers[0]
+    lbp.lbp_attend_partials(case.cfg, case.info, case.plan_ws, lay.q, lay.k_cache, lay.v_cache,
+                            None, None, case.split_ws)
+    torch.cuda.synchronize()
+    tm = lbp.read_taskmap(case.plan_ws, case.info)
+    o_part, lse_part = lbp.split_views(case.split_ws, case.info, case.G)
+    o_part = o_part.cpu().numpy()
+    lse_part = lse_part.cpu().numpy()
+    q = oracle.attention.bf16_bits_to_f64(bits(lay.q))
+    kc, vc = bits(lay.k_cache), bits(lay.v_cache)
+    for d, (g, r, a, e) in enumerate(tm["desc"]):
+        K = oracle.attention.gather_pair_kv(kc, case.wl.page_table[r], g, e)[a:e]
+        V = oracle.attention.gather_pair_kv(vc, case.wl.page_table[r], g, e)[a:e]
+        o, lse = oracle.attention.attend_range(q[r, g * 8:(g + 1) * 8], K, V, case.wcfg.sm_scale)
+        assert np.max(np.abs(o_part[d] - o)) < 1e-2, d
+        # the split buffer keeps base-2 log-sum-exp of log2(e)-scaled scores
+        assert np.max(np.abs(lse_part[d] * np.log(2.0) - lse)) < 1e-3, d
+
+
+def test_workspace_reuse_across_batches(gpu_lib):
+    """A workspace sized for max_batch serves a smaller batch's plan."""
+    wcfg = dataclasses.replace(CONFIGS["tiny"], name="smallbatch", batch=2)
+    case = build_case(wcfg, lengths=[500, 70])
+    out = run_attend(case)
+    compare(case, out, oracle_pairs(case, 0, all_pairs(case)), "small batch")
