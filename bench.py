@@ -1,0 +1,426 @@
+#!/usr/bin/env python3
+"""Benchmark: mixed-length paged GQA decode attention on one MI355X.
+
+One step = one decode-attention layer: the persistent split-KV attention
+kernel plus the combine kernel (``lbp_attend``), reusing one task map built
+once per decode step (``lbp_plan``).  Inputs are seeded synthetic tensors
+already resident in HBM; layers rotate over distinct KV copies (at least
+1 GB in all) so the 256 MB Infinity Cache cannot serve the KV bytes.
+
+The headline workload is the mixed-length batch (64 requests, KV lengths
+log-uniform in [256, 65536], 64 query / 8 KV heads, head_dim 128, BF16 KV in
+64-token pages, 8 layers sharing one task map).  The uniform, skewed and FP8
+workloads are reported in the same JSON line under "other_workloads".
+
+Prints exactly one JSON line.
+"""
+
+from __future__ import annotations
+
+import argparse
+import concurrent.futures
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
+
+METRIC = "µs per decode-attention step + achieved KV HBM GB/s (% of peak), mixed-length"
+HBM_PEAK_GBS = 8000.0
+HEADLINE = "mixed"
+LAYERS = {"mixed": 8, "uniform": 4, "skewed": 16, "fp8": 1, "tiny": 1}
+ATTEND_KERNEL = {"bf16": "attend_kernel<Bf16Kv>", "fp8_e4m3": "attend_kernel<Fp8Kv>"}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attend_traffic.json")
+ATTEND_SRC = os.path.join(ROOT, "load_balanced_paged_amd", "csrc", "attend_kernel.hip")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup-seconds", type=float, default=0.5,
+                    help="before the W warmup steps, run steps for this long (GPU clocks ramp "
+                         "up over the first tens of milliseconds of load)")
+    ap.add_argument("--workloads", default="mixed,uniform,skewed,fp8",
+                    help="comma list; the first is the headline (default mixed)")
+    ap.add_argument("--no-static", action="store_true", help="skip the static split-KV comparison")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="wall-clock budget of the CPU oracle sample")
+    ap.add_argument("--copy-calib-mib", type=int, default=0,
+                    help="also run one torch copy of this many MiB (counter calibration)")
+    ap.add_argument("--eager", action="store_true", help="time stream launches, not a HIP graph")
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# workload set-up
+# ---------------------------------------------------------------------------
+
+class Bench:
+    def __init__(self, name, lbp):
+        from workloads import CONFIGS, make_workload
+        self.lbp = lbp
+        self.name = name
+        self.wcfg = CONFIGS[name]
+        self.layers = LAYERS[name]
+        t0 = time.time()
+        self.wl = make_workload(self.wcfg, device="cuda", layers=self.layers)
+        torch.cuda.synchronize()
+        log(f"{name}: generated {self.layers} layer(s), {self.wl.total_tokens} tokens, "
+            f"{self.wl.kv_bytes / 1e9:.3f} GB KV/layer in {time.time() - t0:.1f}s")
+        self.cfg = lbp.make_config(self.wcfg.num_q_heads, self.wcfg.num_kv_heads, self.wcfg.batch,
+                                   self.wl.page_table.shape[1], kv_dtype=self.wcfg.kv_dtype,
+                                   num_workgroups=0, min_tiles_per_bin=4,
+                                   sm_scale=self.wcfg.sm_scale)
+        self.seq = torch.from_numpy(np.asarray(self.wl.lengths, dtype=np.int32)).cuda()
+        self.table = torch.from_numpy(self.wl.page_table).cuda()
+        self.outs = [torch.empty_like(l.q) for l in self.wl.layers]
+        self.plans = {}
+
+    def plan(self, policy=0, param=0):
+        key = (policy, param)
+        if key not in self.plans:
+            lbp = self.lbp
+            pb, sb = lbp.lbp_query_workspace(self.cfg, policy, param)
+            plan_ws = torch.empty(pb, dtype=torch.uint8, device="cuda")
+            split_ws = torch.empty(sb, dtype=torch.uint8, device="cuda")
+            if policy == lbp.LBP_POLICY_DYNAMIC:
+                info = lbp.lbp_plan(self.cfg, self.seq, self.table, plan_ws)
+            else:
+                info = lbp.lbp_plan_static(self.cfg, policy, param, self.seq, self.table, plan_ws)
+            self.plans[key] = (info, plan_ws, split_ws)
+        return self.plans[key]
+
+    def step_fn(self, policy=0, param=0):
+        """A closure launching one attend on layer i with pre-marshalled arguments."""
+        import ctypes
+        lbp = self.lbp
+        lib = lbp.load()
+        info, plan_ws, split_ws = self.plan(policy, param)
+        stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        cfgp, infop = ctypes.byref(self.cfg), ctypes.byref(info)
+        P = ctypes.c_void_p
+        sbytes = split_ws.numel()
+        args = []
+        for i, L in enumerate(self.wl.layers):
+            ks = P(L.k_scale.data_ptr()) if L.k_scale is not None else None
+            vs = P(L.v_scale.data_ptr()) if L.v_scale is not None else None
+            args.append((cfgp, infop, P(plan_ws.data_ptr()), P(L.q.data_ptr()),
+                         P(L.k_cache.data_ptr()), P(L.v_cache.data_ptr()), ks, vs,
+                         P(split_ws.data_ptr()), sbytes, P(self.outs[i].data_ptr()), stream))
+
+        def run(i):
+            st = lib.lbp_attend(*args[i % self.layers])
+            if st != 0:
+                raise RuntimeError(f"lbp_attend: {lbp.status_name(st)}")
+        return run, args
+
+    # -- timing ------------------------------------------------------------
+
+    def warm(self, seconds):
+        run, _ = self.step_fn()
+        t0 = time.time()
+        i = 0
+        while time.time() - t0 < seconds:
+            for _ in range(4):
+                run(i)
+                i += 1
+            torch.cuda.synchronize()
+
+    def time_steps(self, steps, warmup, policy=0, param=0, eager=False):
+        run, _ = self.step_fn(policy, param)
+        for i in range(warmup):
+            run(i)
+        torch.cuda.synchronize()
+        mode = "eager"
+        graph = None
+        if not eager:
+            try:
+                graph = torch.cuda.CUDAGraph()
+                s = torch.cuda.Stream()
+                s.wait_stream(torch.cuda.current_stream())
+                with torch.cuda.stream(s):
+                    run_g, _ = self.step_fn(policy, param)   # args bound to the capture stream
+                    with torch.cuda.graph(graph, stream=s):
+                        for i in range(steps):
+                            run_g(i)
+                torch.cuda.current_stream().wait_stream(s)
+                graph.replay()                                # untimed warm replay
+                torch.cuda.synchronize()
+                mode = "hip_graph"
+            except Exception as e:  # graph capture unavailable: time stream launches
+                log(f"graph capture failed ({e}); timing stream launches")
+                graph = None
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record()
+        if graph is not None:
+            graph.replay()
+        else:
+            for i in range(steps):
+                run(i)
+        end.record()
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(end) / steps
+        return ms, mode
+
+    def time_attend_kernel(self, steps):
+        """Average duration of the persistent attention kernel alone (HIP events
+        recorded on the launch stream around each lbp_attend_partials)."""
+        lbp = self.lbp
+        lib = lbp.load()
+        _, args = self.step_fn()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        torch.cuda.synchronize()
+        for i in range(steps):
+            a = args[i % self.layers]
+            evs[i][0].record()
+            st = lib.lbp_attend_partials(*a)
+            evs[i][1].record()
+            if st != 0:
+                raise RuntimeError(lbp.status_name(st))
+            lib.lbp_combine(a[0], a[1], a[2], a[8], a[9], a[10], a[11])
+        torch.cuda.synchronize()
+        ts = np.array([e0.elapsed_time(e1) for e0, e1 in evs]) * 1e3
+        return float(ts.mean()), float(np.median(ts)), float(ts.min()), float(ts.max())
+
+    def time_plan(self, reps=20):
+        lbp = self.lbp
+        info, plan_ws, _ = self.plan()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            lbp.lbp_plan(self.cfg, self.seq, self.table, plan_ws)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+
+    def check_finite(self):
+        for o in self.outs:
+            if not torch.isfinite(o.float()).all():
+                raise RuntimeError(f"{self.name}: non-finite output")
+
+    def free(self):
+        self.plans.clear()
+        self.outs = None
+        self.wl = None
+        torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------------------
+# CPU oracle baseline
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(b: Bench, seconds: float):
+    """The fp64 oracle, unchanged, on a time-bounded sample of layer 0's pairs.
+
+    Pairs are visited in a seeded random order on a thread pool (one BLAS
+    thread per worker); a worker starts no new pair after the deadline.  The
+    rate is KV bytes of the completed pairs over the wall time.
+    """
+    import oracle
+    try:
+        from threadpoolctl import threadpool_limits
+    except Exception:  # pragma: no cover
+        threadpool_limits = None
+    wcfg = b.wcfg
+    L = np.asarray(b.wl.lengths)
+    H, G = wcfg.num_kv_heads, wcfg.group
+    lay = b.wl.layers[0]
+    rng = np.random.default_rng(123)
+    order = [(int(g), int(r)) for g, r in
+             zip(*np.unravel_index(rng.permutation(H * len(L)), (H, len(L))))]
+    cores = len(os.sched_getaffinity(0))
+    # host copies of the whole layer (outside the timed region)
+    q = oracle.attention.bf16_bits_to_f64(
+        lay.q.view(torch.int16).cpu().numpy().view(np.uint16))
+    kc = lay.k_cache.view(torch.int16).cpu().numpy().view(np.uint16)
+    vc = lay.v_cache.view(torch.int16).cpu().numpy().view(np.uint16)
+    table = b.wl.page_table
+    deadline = [None]
+    done = []
+
+    def work(pair):
+        if time.perf_counter() > deadline[0]:
+            return
+        g, r = pair
+        oracle.attention.paged_decode_attention(q, kc, vc, table, L, H, wcfg.sm_scale,
+                                                pairs=[(g, r)])
+        done.append(pair)
+
+    ctx = threadpool_limits(limits=1) if threadpool_limits else None
+    if ctx:
+        ctx.__enter__()
+    try:
+        t0 = time.perf_counter()
+        deadline[0] = t0 + seconds
+        with concurrent.futures.ThreadPoolExecutor(cores) as ex:
+            list(ex.map(work, order))
+        wall = time.perf_counter() - t0
+    finally:
+        if ctx:
+            ctx.__exit__(None, None, None)
+    tokens = int(sum(L[r] for _, r in done))
+    kv_bytes = tokens * wcfg.kv_bytes_per_token_head
+    gbs = kv_bytes / wall / 1e9
+    full_us = b.wl.kv_bytes / (gbs * 1e9) * 1e6
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"{len(done)} of {H * len(L)} (KV head, request) pairs of layer 0 "
+                      f"({tokens} tokens, {kv_bytes / 1e9:.3f} GB KV) in {wall:.1f}s wall; "
+                      f"fp64 NumPy oracle, one pair per task on a {cores}-thread pool",
+            "us_per_step_extrapolated": round(full_us, 1)}
+
+
+# ---------------------------------------------------------------------------
+
+def traffic_record(kv_dtype):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current attention kernel source; else None."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except Exception:
+        return None
+    src_hash = hashlib.sha256(open(ATTEND_SRC, "rb").read()).hexdigest()[:16]
+    entry = rec.get(HEADLINE if kv_dtype == "bf16" else "fp8")
+    if not entry or entry.get("attend_src_sha") != src_hash:
+        return None
+    return entry.get("hbm_bytes_per_launch")
+
+
+def bench_one(name, lbp, args, headline):
+    b = Bench(name, lbp)
+    res = {"workload": name}
+    info, _, _ = b.plan()
+    b.warm(args.warmup_seconds)
+    ms, mode = b.time_steps(args.steps, args.warmup, eager=args.eager)
+    b.check_finite()
+    us = ms * 1e3
+    gbs = b.wl.kv_bytes / (us * 1e-6) / 1e9
+    res.update(us_per_step=round(us, 2), kv_gbs=round(gbs, 1),
+               pct_of_hbm_peak=round(100 * gbs / HBM_PEAK_GBS, 1), timing=mode,
+               kv_bytes_per_layer=b.wl.kv_bytes, total_tokens=b.wl.total_tokens,
+               workgroups=info.num_bins, layers=b.layers)
+    k_mean, k_med, k_min, k_max = b.time_attend_kernel(max(20, min(args.steps, 100)))
+    res["attend_kernel_us"] = {"mean": round(k_mean, 2), "median": round(k_med, 2),
+                               "min": round(k_min, 2), "max": round(k_max, 2)}
+    res["plan_us"] = round(b.time_plan(), 2)
+    res["amortized_us_per_layer"] = round((res["plan_us"] + b.layers * us) / b.layers, 2)
+    if not args.no_static:
+        W = info.num_bins
+        s0 = max(1, math.ceil(W / (b.wcfg.num_kv_heads * b.wcfg.batch)))
+        static = {}
+        for S in sorted({s0, 1, 2, 4, 8, 16, 32, 64}):
+            sms, _ = b.time_steps(min(args.steps, 50), 2, lbp.LBP_POLICY_STATIC_SPLITS, S,
+                                  eager=args.eager)
+            static[S] = sms * 1e3
+        best = min(static, key=static.get)
+        res["static_splits"] = {"S_grid_matched": s0, "us_grid_matched": round(static[s0], 2),
+                                "best_S": best, "us_best": round(static[best], 2),
+                                "dynamic_speedup_vs_grid_matched": round(static[s0] / us, 3),
+                                "dynamic_speedup_vs_best": round(static[best] / us, 3),
+                                "us_by_S": {str(k): round(v, 2) for k, v in static.items()}}
+    if headline and not args.no_cpu_baseline:
+        log(f"{name}: CPU oracle baseline ({args.cpu_seconds:.0f}s budget)")
+        res["cpu_baseline"] = cpu_baseline(b, args.cpu_seconds)
+    traffic = traffic_record(b.wcfg.kv_dtype)
+    achieved = b.wl.kv_bytes / (k_mean * 1e-6) / 1e9
+    res["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                       "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                       "traffic": traffic, "kernel": ATTEND_KERNEL[b.wcfg.kv_dtype],
+                       "algorithmic_bytes_per_launch": b.wl.kv_bytes,
+                       "avg_kernel_us": round(k_mean, 2)}
+    log(f"{name}: {us:.1f} us/step ({mode}), {gbs:.0f} GB/s KV, kernel {k_mean:.1f} us "
+        f"({achieved:.0f} GB/s), plan {res['plan_us']:.1f} us")
+    b.free()
+    return res
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path is "
+              "single-GPU by design and has no multi-GPU mode", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    import load_balanced_paged_amd as lbp
+    lbp.load()
+    names = [n.strip() for n in args.workloads.split(",") if n.strip()]
+    torch.cuda.synchronize()
+
+    if args.copy_calib_mib:
+        n = args.copy_calib_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy calibration: {n} bytes read + {n} bytes written")
+        del src, dst
+
+    results = [bench_one(n, lbp, args, headline=(i == 0)) for i, n in enumerate(names)]
+    head = results[0]
+    wcfg = __import__("workloads").CONFIGS[names[0]]
+    out = {
+        "metric": METRIC,
+        "value": head["kv_gbs"],
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "warmup_seconds": args.warmup_seconds,
+        "ms_per_step": round(head["us_per_step"] / 1e3, 5),
+        "us_per_step": head["us_per_step"],
+        "pct_of_hbm_peak": head["pct_of_hbm_peak"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wcfg.kv_dtype == "bf16" else "fp8_e4m3-kv/bf16-q",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"{names[0]}: batch {wcfg.batch}, "
+                         + ("KV lengths log-uniform [%d, %d]" % (wcfg.length_lo, wcfg.length_hi)
+                            if wcfg.lengths_kind == "loguniform" else wcfg.lengths_kind)
+                         + f" (seed {wcfg.seed}), {wcfg.num_q_heads} query / {wcfg.num_kv_heads}"
+                         f" KV heads, head_dim 128, {wcfg.kv_dtype} paged KV (page 64), "
+                         f"{head['layers']} layers sharing one task map"),
+            "batch": wcfg.batch, "num_q_heads": wcfg.num_q_heads,
+            "num_kv_heads": wcfg.num_kv_heads, "head_dim": 128, "page_size": 64,
+            "layers": head["layers"], "total_tokens": head["total_tokens"],
+            "kv_bytes_per_layer": head["kv_bytes_per_layer"], "workgroups": head["workgroups"],
+            "min_tiles_per_bin": 4, "timing": head["timing"],
+        },
+        "roofline": head["roofline"],
+        "plan_us": head["plan_us"],
+        "amortized_us_per_layer": head["amortized_us_per_layer"],
+        "attend_kernel_us": head["attend_kernel_us"],
+    }
+    if "static_splits" in head:
+        out["static_splits"] = head["static_splits"]
+    if "cpu_baseline" in head:
+        out["cpu_baseline"] = head["cpu_baseline"]
+    if len(results) > 1:
+        out["other_workloads"] = {r["workload"]: {k: v for k, v in r.items() if k != "workload"}
+                                  for r in results[1:]}
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

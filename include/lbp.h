@@ -178,16 +178,36 @@ lbp_status lbp_attend(const lbp_config* cfg, const lbp_plan_info* info,
                       void* out_dev, void* stream);
 
 /* The two halves of lbp_attend, for callers that schedule or time them
- * separately.  lbp_attend_partials writes only the split buffer;
- * lbp_combine reads it and writes out_dev.  Split-buffer layout:
- * o_part[max_desc][G][128] fp32 at offset 0, then lse_part[max_desc][G]
- * fp32 (base-2 log-sum-exp of sm_scale*log2(e)-scaled scores) at offset
- * max_desc*G*128*4. */
+ * separately; lbp_combine must follow lbp_attend_partials on the same plan,
+ * split workspace and output.  lbp_attend_partials runs the persistent
+ * attention kernel: a pair whose tokens fit one descriptor is finished in
+ * place (its BF16 output is written to out_dev); every descriptor of a pair
+ * split over several bins writes its partial to the split buffer.
+ * lbp_combine merges the split pairs into out_dev and writes zeros for
+ * pairs with no tokens.  Split-buffer layout: o_part[max_desc][G][128] fp32
+ * (normalised partial outputs) at offset 0, then lse_part[max_desc][G] fp32
+ * (base-2 log-sum-exp of the sm_scale*log2(e)-scaled scores) at offset
+ * align256(max_desc*G*128*4). */
 lbp_status lbp_attend_partials(const lbp_config* cfg, const lbp_plan_info* info,
                                const void* plan_ws_dev, const void* q_dev,
                                const void* k_cache_dev, const void* v_cache_dev,
                                const float* k_scale_dev, const float* v_scale_dev,
-                               void* split_ws_dev, size_t split_ws_bytes, void* stream);
+                               void* split_ws_dev, size_t split_ws_bytes, void* out_dev,
+                               void* stream);
+
+/* lbp_attend_partials that also records, for every workgroup b of the
+ * attention kernel, four uint64 at trace_dev[4b .. 4b+3]: its start and end
+ * on the device's constant-rate real-time clock (s_memrealtime), the
+ * hardware-id register in the low and the XCC id in the high 32 bits, and
+ * the number of descriptors it drained.  For profiling the balance of the
+ * bins (the method's claim that equal bins finish together).  trace_dev
+ * must hold 4 * info->num_bins uint64; NULL is LBP_ERR_INVALID_ARG. */
+lbp_status lbp_attend_partials_traced(const lbp_config* cfg, const lbp_plan_info* info,
+                                      const void* plan_ws_dev, const void* q_dev,
+                                      const void* k_cache_dev, const void* v_cache_dev,
+                                      const float* k_scale_dev, const float* v_scale_dev,
+                                      void* split_ws_dev, size_t split_ws_bytes, void* out_dev,
+                                      uint64_t* trace_dev, void* stream);
 
 lbp_status lbp_combine(const lbp_config* cfg, const lbp_plan_info* info,
                        const void* plan_ws_dev, const void* split_ws_dev,

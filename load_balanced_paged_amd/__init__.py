@@ -37,7 +37,8 @@ PAGE_SIZE = 64
 
 EXPORTED_SYMBOLS = (
     "lbp_status_string", "lbp_version", "lbp_query_workspace", "lbp_plan", "lbp_plan_static",
-    "lbp_plan_layout", "lbp_attend", "lbp_attend_partials", "lbp_combine",
+    "lbp_plan_layout", "lbp_attend", "lbp_attend_partials", "lbp_attend_partials_traced",
+    "lbp_combine",
 )
 
 
@@ -112,7 +113,8 @@ def load(path: str = LIB_PATH):
         "lbp_plan_static": (I32, [cfgp, I32, I32, P, I32, P, I64, P, SZ, infop, P]),
         "lbp_plan_layout": (I32, [infop, ctypes.POINTER(lbp_plan_offsets)]),
         "lbp_attend": (I32, [cfgp, infop, P, P, P, P, P, P, P, SZ, P, P]),
-        "lbp_attend_partials": (I32, [cfgp, infop, P, P, P, P, P, P, P, SZ, P]),
+        "lbp_attend_partials": (I32, [cfgp, infop, P, P, P, P, P, P, P, SZ, P, P]),
+        "lbp_attend_partials_traced": (I32, [cfgp, infop, P, P, P, P, P, P, P, SZ, P, P, P]),
         "lbp_combine": (I32, [cfgp, infop, P, P, SZ, P, P]),
     }
     for name, (res, args) in sig.items():
@@ -237,14 +239,32 @@ def lbp_attend(cfg, info, plan_ws, q, k_cache, v_cache, k_scale, v_scale, split_
 
 
 def lbp_attend_partials(cfg, info, plan_ws, q, k_cache, v_cache, k_scale, v_scale, split_ws,
-                        stream=None):
+                        out, stream=None):
     import torch
     kp, vp, ksp, vsp = _kv_ptrs(cfg, k_cache, v_cache, k_scale, v_scale)
     _check(load().lbp_attend_partials(ctypes.byref(cfg), ctypes.byref(info),
                                       _ptr(plan_ws, "plan_ws"), _ptr(q, "q", torch.bfloat16),
                                       kp, vp, ksp, vsp, _ptr(split_ws, "split_ws"),
                                       split_ws.numel() * split_ws.element_size(),
-                                      _stream(stream)), "lbp_attend_partials")
+                                      _ptr(out, "out", torch.bfloat16), _stream(stream)),
+           "lbp_attend_partials")
+
+
+def lbp_attend_partials_traced(cfg, info, plan_ws, q, k_cache, v_cache, k_scale, v_scale,
+                               split_ws, out, trace, stream=None):
+    """``trace`` is an int64 device tensor of at least 4 * info.num_bins entries."""
+    import torch
+    if trace.numel() < 4 * info.num_bins:
+        raise ValueError("trace needs 4 * num_bins entries")
+    kp, vp, ksp, vsp = _kv_ptrs(cfg, k_cache, v_cache, k_scale, v_scale)
+    _check(load().lbp_attend_partials_traced(ctypes.byref(cfg), ctypes.byref(info),
+                                             _ptr(plan_ws, "plan_ws"),
+                                             _ptr(q, "q", torch.bfloat16), kp, vp, ksp, vsp,
+                                             _ptr(split_ws, "split_ws"),
+                                             split_ws.numel() * split_ws.element_size(),
+                                             _ptr(out, "out", torch.bfloat16),
+                                             _ptr(trace, "trace", torch.int64), _stream(stream)),
+           "lbp_attend_partials_traced")
 
 
 def lbp_combine(cfg, info, plan_ws, split_ws, out, stream=None):

@@ -30,7 +30,14 @@
 //    memory traffic, which both masks the unused slots of a request's last
 //    page (they may hold NaN) and lets the prefetch of nonexistent slices be
 //    issued unconditionally, keeping the wait counts static.
-//  * Three slices are in flight per wave (one computing, two loading).
+//  * Two slices are in flight per wave (one computing, one loading) with 8
+//    waves per workgroup for BF16; FP8 moves half the bytes per token for
+//    the same math, so it runs 12 waves (three per SIMD) to keep enough
+//    loads in flight.
+//  * A pair served by a single descriptor is finished in place: its
+//    normalised output goes straight to `out` in BF16 and the combine
+//    kernel skips it.  Only pairs split over several bins use the split
+//    buffer.
 //  * FP8 KV (OCP e4m3 codes with one fp32 scale per token and KV head): codes
 //    are widened to bf16 exactly in registers; the K scale multiplies the
 //    score of its token, the V scale is folded into the probability before
@@ -40,8 +47,23 @@
 namespace lbp {
 namespace {
 
-constexpr int kWaves = 8;
-constexpr int kThreads = kWaves * 64;
+// Tunables, fixed at build time per KV format (defaults: the measured best).
+#ifndef LBP_BF16_WAVES
+#define LBP_BF16_WAVES 8
+#endif
+#ifndef LBP_BF16_STAGES
+#define LBP_BF16_STAGES 2
+#endif
+#ifndef LBP_FP8_WAVES
+#define LBP_FP8_WAVES 12
+#endif
+#ifndef LBP_FP8_STAGES
+#define LBP_FP8_STAGES 2
+#endif
+#ifndef LBP_KV_LOAD_AUX
+#define LBP_KV_LOAD_AUX 2
+#endif
+constexpr int kLoadAux = LBP_KV_LOAD_AUX;  // KV loads: 2 = non-temporal (read once, stream)
 constexpr int kSlice = 16;
 constexpr int kRedRow = kHeadDim + 4;  // padded LDS row (floats) for the merge
 
@@ -88,6 +110,8 @@ struct SliceRsrc {
 struct Bf16Kv {
   static constexpr int kRowBytes = kHeadDim * 2;
   static constexpr bool kScaled = false;
+  static constexpr int kWaves = LBP_BF16_WAVES;    // waves per workgroup
+  static constexpr int kStages = LBP_BF16_STAGES;  // 16-token slices in flight per wave
   struct Buf {
     i32x4_t k[4];   // K A-operand, one per 32-dim k-step
     i32x4_t v[4];   // V rows 4*grp+i, dims [8c, 8c+8)
@@ -99,10 +123,10 @@ struct Bf16Kv {
     const int m = lane & 15, grp = lane >> 4;
 #pragma unroll
     for (int s = 0; s < 4; ++s)
-      b.k[s] = __builtin_amdgcn_raw_buffer_load_b128(rs.k, m * kRowBytes + 64 * s + 16 * grp, 0, 0);
+      b.k[s] = __builtin_amdgcn_raw_buffer_load_b128(rs.k, m * kRowBytes + 64 * s + 16 * grp, 0, kLoadAux);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      b.v[i] = __builtin_amdgcn_raw_buffer_load_b128(rs.v, (4 * grp + i) * kRowBytes + 16 * m, 0, 0);
+      b.v[i] = __builtin_amdgcn_raw_buffer_load_b128(rs.v, (4 * grp + i) * kRowBytes + 16 * m, 0, kLoadAux);
   }
 
   __device__ static f32x4_t scores(const Buf& b, const bf16x8_t* qb) {
@@ -136,6 +160,10 @@ struct Bf16Kv {
 struct Fp8Kv {
   static constexpr int kRowBytes = kHeadDim;
   static constexpr bool kScaled = true;
+  // FP8 moves half the bytes per token for the same MFMA and softmax work, so
+  // it needs more waves in flight per CU (three per SIMD) to stay on HBM.
+  static constexpr int kWaves = LBP_FP8_WAVES;
+  static constexpr int kStages = LBP_FP8_STAGES;
   struct Buf {
     i32x4_t k[2];   // 32 codes: dims [32grp, 32grp + 32) of token m
     i32x2_t v[4];   // 8 codes: dims [8c, 8c+8) of token 4grp+i
@@ -149,10 +177,10 @@ struct Fp8Kv {
     const int m = lane & 15, grp = lane >> 4;
 #pragma unroll
     for (int h = 0; h < 2; ++h)
-      b.k[h] = __builtin_amdgcn_raw_buffer_load_b128(rs.k, m * kRowBytes + 32 * grp + 16 * h, 0, 0);
+      b.k[h] = __builtin_amdgcn_raw_buffer_load_b128(rs.k, m * kRowBytes + 32 * grp + 16 * h, 0, kLoadAux);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      b.v[i] = __builtin_amdgcn_raw_buffer_load_b64(rs.v, (4 * grp + i) * kRowBytes + 8 * m, 0, 0);
+      b.v[i] = __builtin_amdgcn_raw_buffer_load_b64(rs.v, (4 * grp + i) * kRowBytes + 8 * m, 0, kLoadAux);
     b.ks = __builtin_amdgcn_raw_buffer_load_b128(rs.ks, 16 * grp, 0, 0);
     b.vs = __builtin_amdgcn_raw_buffer_load_b128(rs.vs, 16 * grp, 0, 0);
   }
@@ -240,24 +268,28 @@ __device__ inline void consume(WaveState& st, const typename Kv::Buf& b, const b
   const float m_new = fmaxf(st.m, mx);
   const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
   st.m = m_new;
+  st.l *= alpha;
+#pragma unroll
+  for (int mb = 0; mb < 8; ++mb) st.acc[mb] *= alpha;
   float p[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) p[j] = __builtin_amdgcn_exp2f(x[j] - m_new);
-  st.l = st.l * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+  for (int j = 0; j < 4; ++j) p[j] = __builtin_amdgcn_exp2f(x[j] - st.m);
+  st.l += (p[0] + p[1]) + (p[2] + p[3]);
   i32x2_t pb2 = {int(pack_bf16(p[0] * vs[0], p[1] * vs[1])),
                  int(pack_bf16(p[2] * vs[2], p[3] * vs[3]))};
   const i16x4_t pb = __builtin_bit_cast(i16x4_t, pb2);
 #pragma unroll
-  for (int mb = 0; mb < 8; ++mb) {
-    st.acc[mb] *= alpha;
+  for (int mb = 0; mb < 8; ++mb)
     st.acc[mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(Kv::v_operand(b, mb), pb, st.acc[mb],
                                                             0, 0, 0);
-  }
 }
 
+// Drains one bin: every descriptor in it, in order.
 template <class Kv>
-__global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a) {
-  extern __shared__ float smem[];
+__device__ inline void attend_bin(const AttendArgs& a, float* smem, int bin) {
+  constexpr int kWaves = Kv::kWaves;
+  constexpr int kStages = Kv::kStages;
+  constexpr int kThreads = kWaves * 64;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15;         // query head within the group (MFMA column)
@@ -265,14 +297,13 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a) {
   const int G = a.group;
   const int red_stride = 32 + G * kRedRow;
   float* red = smem + wave * red_stride;
-
-  const int bin = blockIdx.x;
   const int d_begin = a.bin_offset[bin];
   const int d_end = a.bin_offset[bin + 1];
 
   for (int d = d_begin; d < d_end; ++d) {
     const int4 ds = reinterpret_cast<const int4*>(a.desc)[d];
     const int g = ds.x, r = ds.y, t_begin = ds.z, t_end = ds.w;
+    const bool single = a.pair_count[g * a.batch + r] == 1;
 
     // query group of KV head g for request r as the MFMA B operand
     const rsrc_t qr = make_rsrc(static_cast<const char*>(a.q) +
@@ -290,26 +321,30 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a) {
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb) st.acc[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    const int step = kWaves * kSlice;
+    // ring of kStages slices in flight: slice i is consumed while slices
+    // i+1 .. i+kStages-1 load; a slice past t_end loads nothing
+    constexpr int step = kWaves * kSlice;
     int tok = t_begin + wave * kSlice;
-    typename Kv::Buf b0, b1, b2;
-    Kv::issue(b0, slice_rsrc<Kv>(a, g, r, tok, t_end), lane);
-    Kv::issue(b1, slice_rsrc<Kv>(a, g, r, tok + step, t_end), lane);
-    while (tok < t_end) {
-      Kv::issue(b2, slice_rsrc<Kv>(a, g, r, tok + 2 * step, t_end), lane);
-      consume<Kv>(st, b0, qb, tok, t_end, a.scale_log2, grp);
-      tok += step;
-      if (tok >= t_end) break;
-      Kv::issue(b0, slice_rsrc<Kv>(a, g, r, tok + 2 * step, t_end), lane);
-      consume<Kv>(st, b1, qb, tok, t_end, a.scale_log2, grp);
-      tok += step;
-      if (tok >= t_end) break;
-      Kv::issue(b1, slice_rsrc<Kv>(a, g, r, tok + 2 * step, t_end), lane);
-      consume<Kv>(st, b2, qb, tok, t_end, a.scale_log2, grp);
-      tok += step;
+    typename Kv::Buf buf[kStages];
+#pragma unroll
+    for (int u = 0; u + 1 < kStages; ++u)
+      Kv::issue(buf[u], slice_rsrc<Kv>(a, g, r, tok + u * step, t_end), lane);
+    bool more = tok < t_end;
+    while (more) {
+#pragma unroll
+      for (int u = 0; u < kStages; ++u) {
+        Kv::issue(buf[(u + kStages - 1) % kStages],
+                  slice_rsrc<Kv>(a, g, r, tok + (kStages - 1) * step, t_end), lane);
+        consume<Kv>(st, buf[u], qb, tok, t_end, a.scale_log2, grp);
+        tok += step;
+        if (tok >= t_end) {
+          more = false;
+          break;
+        }
+      }
     }
 
-    // merge the 8 wave states of this descriptor
+    // merge the wave states of this descriptor
     st.l = wave_sum_across_groups(st.l);
     if (n < G) {
       if (grp == 0) {
@@ -339,24 +374,79 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a) {
         L += rw[16 + q] * c;
         o += rw[32 + q * kRedRow + dim] * c;
       }
-      a.o_part[(int64_t(d) * G + q) * kHeadDim + dim] = o / L;
-      if (dim == 0) a.lse_part[int64_t(d) * G + q] = M + __builtin_amdgcn_logf(L);
+      if (single) {
+        // the pair's only descriptor: this is already the final output
+        const int64_t row = int64_t(r) * a.num_q_heads + int64_t(g) * G + q;
+        static_cast<__bf16*>(a.out)[row * kHeadDim + dim] = static_cast<__bf16>(o / L);
+      } else {
+        a.o_part[(int64_t(d) * G + q) * kHeadDim + dim] = o / L;
+        if (dim == 0) a.lse_part[int64_t(d) * G + q] = M + __builtin_amdgcn_logf(L);
+      }
     }
     __syncthreads();
+  }
+
+}
+
+// One workgroup per persistent slot.  With grab_counter == null workgroup b
+// drains bin b (the launch has one workgroup per bin).  Otherwise the launch
+// has fewer workgroups than bins and each takes the next bin in increasing
+// order from an atomic ticket counter until the bins run out, so a workgroup
+// on a faster CU simply drains more bins; every workgroup draws exactly one
+// ticket past the last bin, and the one holding the final ticket returns the
+// counter to zero for the next launch.
+template <class Kv>
+__global__ __launch_bounds__(Kv::kWaves * 64) void attend_kernel(AttendArgs a) {
+  extern __shared__ float smem[];
+  __shared__ int ticket_lds;
+  uint64_t t_start = 0;
+  if (a.trace) t_start = __builtin_amdgcn_s_memrealtime();
+  int drained = 0;
+  if (!a.grab_counter) {
+    const int bin = blockIdx.x;
+    attend_bin<Kv>(a, smem, bin);
+    drained = a.bin_offset[bin + 1] - a.bin_offset[bin];
+  } else {
+    for (;;) {
+      if (threadIdx.x == 0) ticket_lds = atomicAdd(a.grab_counter, 1);
+      __syncthreads();
+      const int ticket = ticket_lds;
+      __syncthreads();
+      if (ticket >= a.num_bins) {
+        if (threadIdx.x == 0 && ticket == a.num_bins + int(gridDim.x) - 1)
+          atomicExch(a.grab_counter, 0);
+        break;
+      }
+      attend_bin<Kv>(a, smem, ticket);
+      drained += a.bin_offset[ticket + 1] - a.bin_offset[ticket];
+    }
+  }
+
+  if (a.trace && threadIdx.x == 0) {
+    uint32_t hw, xcc;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_HW_ID)" : "=s"(hw));
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+    const uint64_t t_end = __builtin_amdgcn_s_memrealtime();
+    uint64_t* t = a.trace + 4 * int64_t(blockIdx.x);
+    t[0] = t_start;
+    t[1] = t_end;
+    t[2] = (uint64_t(xcc) << 32) | hw;
+    t[3] = uint64_t(drained);
   }
 }
 
 }  // namespace
 
-hipError_t launch_attend(const AttendArgs& a, int kv_dtype, int num_bins, hipStream_t s) {
+hipError_t launch_attend(const AttendArgs& a, int kv_dtype, int grid, hipStream_t s) {
   AttendArgs copy = a;
   void* args[] = {&copy};
-  const size_t lds = size_t(kWaves) * (32 + a.group * kRedRow) * sizeof(float);
-  const void* fn = kv_dtype == LBP_KV_FP8_E4M3
-                       ? reinterpret_cast<const void*>(&attend_kernel<Fp8Kv>)
+  const bool fp8 = kv_dtype == LBP_KV_FP8_E4M3;
+  const int waves = fp8 ? Fp8Kv::kWaves : Bf16Kv::kWaves;
+  const size_t lds = size_t(waves) * (32 + a.group * kRedRow) * sizeof(float);
+  const void* fn = fp8 ? reinterpret_cast<const void*>(&attend_kernel<Fp8Kv>)
                        : reinterpret_cast<const void*>(&attend_kernel<Bf16Kv>);
-  if (num_bins <= 0) return hipSuccess;
-  return hipLaunchKernel(fn, dim3(num_bins), dim3(kThreads), args, lds, s);
+  if (grid <= 0) return hipSuccess;
+  return hipLaunchKernel(fn, dim3(grid), dim3(waves * 64), args, lds, s);
 }
 
 }  // namespace lbp

@@ -215,15 +215,16 @@ lbp_status lbp_plan_layout(const lbp_plan_info* info, lbp_plan_offsets* offsets)
   return LBP_OK;
 }
 
-lbp_status lbp_attend_partials(const lbp_config* cfg, const lbp_plan_info* info,
-                               const void* plan_ws_dev, const void* q_dev,
-                               const void* k_cache_dev, const void* v_cache_dev,
-                               const float* k_scale_dev, const float* v_scale_dev,
-                               void* split_ws_dev, size_t split_ws_bytes, void* stream) {
+static lbp_status attend_partials_impl(const lbp_config* cfg, const lbp_plan_info* info,
+                                       const void* plan_ws_dev, const void* q_dev,
+                                       const void* k_cache_dev, const void* v_cache_dev,
+                                       const float* k_scale_dev, const float* v_scale_dev,
+                                       void* split_ws_dev, size_t split_ws_bytes, void* out_dev,
+                                       uint64_t* trace_dev, void* stream) {
   lbp_status st = check_config(cfg);
   if (st != LBP_OK) return st;
   if ((st = check_info(cfg, info)) != LBP_OK) return st;
-  if (!plan_ws_dev || !q_dev || !k_cache_dev || !v_cache_dev || !split_ws_dev)
+  if (!plan_ws_dev || !q_dev || !k_cache_dev || !v_cache_dev || !split_ws_dev || !out_dev)
     return LBP_ERR_INVALID_ARG;
   if (cfg->kv_dtype == LBP_KV_FP8_E4M3 && (!k_scale_dev || !v_scale_dev))
     return LBP_ERR_INVALID_ARG;
@@ -235,6 +236,7 @@ lbp_status lbp_attend_partials(const lbp_config* cfg, const lbp_plan_info* info,
   AttendArgs a;
   a.bin_offset = reinterpret_cast<const int32_t*>(pb + off.bin_offset);
   a.desc = reinterpret_cast<const int32_t*>(pb + off.desc);
+  a.pair_count = reinterpret_cast<const int32_t*>(pb + off.pair_count);
   a.page_table = info->page_table_dev;
   a.page_table_stride = info->page_table_stride;
   a.q = q_dev;
@@ -245,13 +247,54 @@ lbp_status lbp_attend_partials(const lbp_config* cfg, const lbp_plan_info* info,
   a.o_part = static_cast<float*>(split_ws_dev);
   a.lse_part = reinterpret_cast<float*>(static_cast<char*>(split_ws_dev) +
                                         split_lse_offset(info->max_desc, G));
+  a.out = out_dev;
+  a.trace = trace_dev;
+  a.num_bins = info->num_bins;
+  // Dynamic plans with more bins than CUs run one persistent workgroup per
+  // CU that takes bins in order from the ticket counter; otherwise (and for
+  // the static comparison plans, which are ordinary grids) one workgroup
+  // per bin.
+  int grid = info->num_bins;
+  a.grab_counter = nullptr;
+  if (info->policy == LBP_POLICY_DYNAMIC) {
+    int cus = 0;
+    if ((st = cu_count(&cus)) != LBP_OK) return st;
+    if (info->num_bins > cus) {
+      grid = cus;
+      a.grab_counter = reinterpret_cast<int32_t*>(const_cast<char*>(pb) + off.header) + kHdrTicket;
+    }
+  }
+  a.batch = info->batch;
   a.num_q_heads = cfg->num_q_heads;
   a.num_kv_heads = cfg->num_kv_heads;
   a.group = G;
   a.scale_log2 = cfg->sm_scale * 1.4426950408889634f;
-  if (launch_attend(a, cfg->kv_dtype, info->num_bins, static_cast<hipStream_t>(stream)) != hipSuccess)
+  if (launch_attend(a, cfg->kv_dtype, grid, static_cast<hipStream_t>(stream)) != hipSuccess)
     return LBP_ERR_HIP;
   return LBP_OK;
+}
+
+lbp_status lbp_attend_partials(const lbp_config* cfg, const lbp_plan_info* info,
+                               const void* plan_ws_dev, const void* q_dev,
+                               const void* k_cache_dev, const void* v_cache_dev,
+                               const float* k_scale_dev, const float* v_scale_dev,
+                               void* split_ws_dev, size_t split_ws_bytes, void* out_dev,
+                               void* stream) {
+  return attend_partials_impl(cfg, info, plan_ws_dev, q_dev, k_cache_dev, v_cache_dev,
+                              k_scale_dev, v_scale_dev, split_ws_dev, split_ws_bytes, out_dev,
+                              nullptr, stream);
+}
+
+lbp_status lbp_attend_partials_traced(const lbp_config* cfg, const lbp_plan_info* info,
+                                      const void* plan_ws_dev, const void* q_dev,
+                                      const void* k_cache_dev, const void* v_cache_dev,
+                                      const float* k_scale_dev, const float* v_scale_dev,
+                                      void* split_ws_dev, size_t split_ws_bytes, void* out_dev,
+                                      uint64_t* trace_dev, void* stream) {
+  if (!trace_dev) return LBP_ERR_INVALID_ARG;
+  return attend_partials_impl(cfg, info, plan_ws_dev, q_dev, k_cache_dev, v_cache_dev,
+                              k_scale_dev, v_scale_dev, split_ws_dev, split_ws_bytes, out_dev,
+                              trace_dev, stream);
 }
 
 lbp_status lbp_combine(const lbp_config* cfg, const lbp_plan_info* info, const void* plan_ws_dev,
@@ -289,7 +332,7 @@ lbp_status lbp_attend(const lbp_config* cfg, const lbp_plan_info* info, const vo
   if (!out_dev) return LBP_ERR_INVALID_ARG;
   lbp_status st = lbp_attend_partials(cfg, info, plan_ws_dev, q_dev, k_cache_dev, v_cache_dev,
                                       k_scale_dev, v_scale_dev, split_ws_dev, split_ws_bytes,
-                                      stream);
+                                      out_dev, stream);
   if (st != LBP_OK) return st;
   return lbp_combine(cfg, info, plan_ws_dev, split_ws_dev, split_ws_bytes, out_dev, stream);
 }

@@ -17,6 +17,7 @@ constexpr int kDefaultMinTiles = 4;         // F, the minimum-work floor (tiles 
 enum HeaderWord {
   kHdrMagic = 0, kHdrPolicy = 1, kHdrNumBins = 2, kHdrBatch = 3, kHdrKvHeads = 4,
   kHdrTiles = 5, kHdrBudget = 6, kHdrDesc = 7, kHdrUsedBins = 8, kHdrStatus = 9,
+  kHdrTicket = 10,  // bin ticket counter of the attention kernel (zero between launches)
   kHdrWords = 16
 };
 constexpr int kStatusClamped = 1;
@@ -60,6 +61,7 @@ struct PlanArgs {
 struct AttendArgs {
   const int32_t* bin_offset;
   const int32_t* desc;
+  const int32_t* pair_count;
   const int32_t* page_table;
   int64_t page_table_stride;
   const void* q;             // [B][Hq][128] bf16
@@ -69,7 +71,11 @@ struct AttendArgs {
   const float* v_scale;
   float* o_part;             // [max_desc][G][128]
   float* lse_part;           // [max_desc][G]
-  int32_t num_q_heads, num_kv_heads, group;
+  void* out;                 // [B][Hq][128] bf16: single-descriptor pairs land here
+  uint64_t* trace;           // optional [grid][4] workgroup records, or null
+  int32_t* grab_counter;     // null: workgroup b drains bin b; else the ticket counter
+  int32_t num_bins;
+  int32_t batch, num_q_heads, num_kv_heads, group;
   float scale_log2;          // sm_scale * log2(e)
 };
 
@@ -85,7 +91,7 @@ struct CombineArgs {
 // Launchers (defined next to their kernels).  Each returns the HIP error of
 // the launch itself.
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
-hipError_t launch_attend(const AttendArgs& a, int kv_dtype, int num_bins, hipStream_t s);
+hipError_t launch_attend(const AttendArgs& a, int kv_dtype, int grid, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, int npairs, hipStream_t s);
 
 }  // namespace lbp

@@ -111,25 +111,52 @@ def test_attend_deterministic(gpu_lib):
 
 
 def test_partials_match_oracle_ranges(gpu_lib):
-    """Split-buffer contents per descriptor against the oracle's per-range attention."""
+    """Split-buffer contents per descriptor of every split pair against the
+    oracle's per-range attention; single-descriptor pairs are finished in place."""
     case = build_case(CONFIGS["tiny"], num_workgroups=5, min_tiles=1)
     lay = case.wl.layers[0]
+    out = torch.zeros_like(lay.q)
     lbp.lbp_attend_partials(case.cfg, case.info, case.plan_ws, lay.q, lay.k_cache, lay.v_cache,
-                            None, None, case.split_ws)
+                            None, None, case.split_ws, out)
     torch.cuda.synchronize()
     tm = lbp.read_taskmap(case.plan_ws, case.info)
+    assert sorted(tm["pair_count"]) == [1, 1, 2, 4]
     o_part, lse_part = lbp.split_views(case.split_ws, case.info, case.G)
     o_part = o_part.cpu().numpy()
     lse_part = lse_part.cpu().numpy()
     q = oracle.attention.bf16_bits_to_f64(bits(lay.q))
     kc, vc = bits(lay.k_cache), bits(lay.v_cache)
+    got_out = bf16_to_f64(out)
     for d, (g, r, a, e) in enumerate(tm["desc"]):
         K = oracle.attention.gather_pair_kv(kc, case.wl.page_table[r], g, e)[a:e]
         V = oracle.attention.gather_pair_kv(vc, case.wl.page_table[r], g, e)[a:e]
         o, lse = oracle.attention.attend_range(q[r, g * 8:(g + 1) * 8], K, V, case.wcfg.sm_scale)
+        if tm["pair_count"][g * 4 + r] == 1:
+            assert np.max(np.abs(got_out[r, g * 8:(g + 1) * 8] - o)) < 1e-2, d
+            continue
         assert np.max(np.abs(o_part[d] - o)) < 1e-2, d
         # the split buffer keeps base-2 log-sum-exp of log2(e)-scaled scores
         assert np.max(np.abs(lse_part[d] * np.log(2.0) - lse)) < 1e-3, d
+
+
+def test_traced_run_records_every_workgroup(gpu_lib):
+    """The traced entry point gives the same output plus one record per workgroup."""
+    case = build_case(CONFIGS["skewed"])
+    lay = case.wl.layers[0]
+    ref = run_attend(case).clone()
+    out = torch.zeros_like(lay.q)
+    trace = torch.zeros(4 * case.info.num_bins, dtype=torch.int64, device="cuda")
+    lbp.lbp_attend_partials_traced(case.cfg, case.info, case.plan_ws, lay.q, lay.k_cache,
+                                   lay.v_cache, None, None, case.split_ws, out, trace)
+    lbp.lbp_combine(case.cfg, case.info, case.plan_ws, case.split_ws, out)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+    t = trace.view(-1, 4).cpu().numpy()
+    tm = lbp.read_taskmap(case.plan_ws, case.info)
+    assert np.all(t[:, 1] >= t[:, 0]) and np.all(t[:, 0] > 0)
+    assert np.array_equal(t[:, 3], np.diff(tm["bin_offset"]))
+    xcc = t[:, 2] >> 32
+    assert len(set(xcc.tolist())) >= 1
 
 
 def test_workspace_reuse_across_batches(gpu_lib):
@@ -138,3 +165,29 @@ def test_workspace_reuse_across_batches(gpu_lib):
     case = build_case(wcfg, lengths=[500, 70])
     out = run_attend(case)
     compare(case, out, oracle_pairs(case, 0, all_pairs(case)), "small batch")
+
+
+def test_graph_replay_matches_eager(gpu_lib):
+    """lbp_plan + lbp_attend captured into a HIP graph: every replay equals eager."""
+    case = build_case(CONFIGS["skewed"], layers=2)
+    eager = [run_attend(case, i).clone() for i in range(2)]
+    outs = [torch.zeros_like(e) for e in eager]
+    lay = case.wl.layers
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            lbp.lbp_plan(case.cfg, case.seq_lens, case.page_table, case.plan_ws, stream=s)
+            for i in range(2):
+                lbp.lbp_attend(case.cfg, case.info, case.plan_ws, lay[i].q, lay[i].k_cache,
+                               lay[i].v_cache, None, None, case.split_ws, outs[i], stream=s)
+    torch.cuda.current_stream().wait_stream(s)
+    for rep in range(4):
+        for o in outs:
+            o.zero_()
+        run_attend(case, 1 - rep % 2)          # unrelated eager work between replays
+        g.replay()
+        torch.cuda.synchronize()
+        for i in range(2):
+            assert torch.equal(outs[i].view(torch.int16), eager[i].view(torch.int16)), (rep, i)
