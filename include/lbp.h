@@ -110,13 +110,20 @@ typedef struct lbp_plan_info {
  *   header[16]: [0] magic [1] policy [2] num_bins [3] batch [4] num_kv_heads
  *               [5] T (tiles) [6] budget (F-floored for DYNAMIC, S or C for
  *               the static policies) [7] D (descriptors) [8] U (bins with
- *               work) [9] status bits (1 = a length was clamped)
+ *               work) [9] status bits (1 = a length was clamped) [10] bin
+ *               ticket counter of the attention kernel (0 between launches)
+ *               [11] number of split_list entries
  *   bin_offset[num_bins + 1]  descriptors of bin b: [bin_offset[b], bin_offset[b+1])
  *   desc[max_desc][4]         (kv_head, request, token_begin, token_end)
  *   pair_first[H_kv * batch], pair_count[H_kv * batch]; pair p = kv_head * batch + request
- *   scratch[H_kv * batch]     assign-kernel scratch */
+ *   scratch[H_kv * batch]     assign-kernel scratch
+ *   split_list[max_split][4]  (pair, pair_first, pair_count, 0) of every pair
+ *                             with pair_count >= 2, in pair order; max_split =
+ *                             min(H_kv * batch, num_bins - 1) for DYNAMIC (a
+ *                             pair is split only across one of the U - 1
+ *                             internal bin boundaries), H_kv * batch otherwise */
 typedef struct lbp_plan_offsets {
-  uint64_t header, bin_offset, desc, pair_first, pair_count, scratch, total;
+  uint64_t header, bin_offset, desc, pair_first, pair_count, scratch, split_list, total;
 } lbp_plan_offsets;
 
 /* Human-readable name of a status code (static storage). */
@@ -182,9 +189,9 @@ lbp_status lbp_attend(const lbp_config* cfg, const lbp_plan_info* info,
  * split workspace and output.  lbp_attend_partials runs the persistent
  * attention kernel: a pair whose tokens fit one descriptor is finished in
  * place (its BF16 output is written to out_dev); every descriptor of a pair
- * split over several bins writes its partial to the split buffer.
- * lbp_combine merges the split pairs into out_dev and writes zeros for
- * pairs with no tokens.  Split-buffer layout: o_part[max_desc][G][128] fp32
+ * split over several bins writes its partial to the split buffer, and a
+ * pair with no tokens gets zero rows.  lbp_combine merges the split pairs
+ * (the plan's split_list) into out_dev.  Split-buffer layout: o_part[max_desc][G][128] fp32
  * (normalised partial outputs) at offset 0, then lse_part[max_desc][G] fp32
  * (base-2 log-sum-exp of the sm_scale*log2(e)-scaled scores) at offset
  * align256(max_desc*G*128*4). */

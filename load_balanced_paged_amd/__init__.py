@@ -75,7 +75,8 @@ class lbp_plan_info(ctypes.Structure):
 
 class lbp_plan_offsets(ctypes.Structure):
     _fields_ = [(n, ctypes.c_uint64) for n in
-                ("header", "bin_offset", "desc", "pair_first", "pair_count", "scratch", "total")]
+                ("header", "bin_offset", "desc", "pair_first", "pair_count", "scratch", "split_list",
+                 "total")]
 
 
 class LbpError(RuntimeError):
@@ -299,6 +300,7 @@ def read_taskmap(plan_ws, info: lbp_plan_info) -> dict:
         "desc": sl(off.desc, 4 * D).reshape(D, 4),
         "pair_first": sl(off.pair_first, npairs),
         "pair_count": sl(off.pair_count, npairs),
+        "split_list": sl(off.split_list, 4 * int(h[11])).reshape(-1, 4),
     }
 
 

@@ -35,9 +35,9 @@
 //    the same math, so it runs 12 waves (three per SIMD) to keep enough
 //    loads in flight.
 //  * A pair served by a single descriptor is finished in place: its
-//    normalised output goes straight to `out` in BF16 and the combine
-//    kernel skips it.  Only pairs split over several bins use the split
-//    buffer.
+//    normalised output goes straight to `out` in BF16, and a pair without
+//    tokens gets zero rows here too.  Only pairs split over several bins use
+//    the split buffer and the combine kernel.
 //  * FP8 KV (OCP e4m3 codes with one fp32 scale per token and KV head): codes
 //    are widened to bf16 exactly in registers; the K scale multiplies the
 //    score of its token, the V scale is folded into the probability before
@@ -51,14 +51,8 @@ namespace {
 #ifndef LBP_BF16_WAVES
 #define LBP_BF16_WAVES 8
 #endif
-#ifndef LBP_BF16_STAGES
-#define LBP_BF16_STAGES 2
-#endif
 #ifndef LBP_FP8_WAVES
 #define LBP_FP8_WAVES 12
-#endif
-#ifndef LBP_FP8_STAGES
-#define LBP_FP8_STAGES 2
 #endif
 #ifndef LBP_KV_LOAD_AUX
 #define LBP_KV_LOAD_AUX 2
@@ -111,7 +105,6 @@ struct Bf16Kv {
   static constexpr int kRowBytes = kHeadDim * 2;
   static constexpr bool kScaled = false;
   static constexpr int kWaves = LBP_BF16_WAVES;    // waves per workgroup
-  static constexpr int kStages = LBP_BF16_STAGES;  // 16-token slices in flight per wave
   struct Buf {
     i32x4_t k[4];   // K A-operand, one per 32-dim k-step
     i32x4_t v[4];   // V rows 4*grp+i, dims [8c, 8c+8)
@@ -163,7 +156,6 @@ struct Fp8Kv {
   // FP8 moves half the bytes per token for the same MFMA and softmax work, so
   // it needs more waves in flight per CU (three per SIMD) to stay on HBM.
   static constexpr int kWaves = LBP_FP8_WAVES;
-  static constexpr int kStages = LBP_FP8_STAGES;
   struct Buf {
     i32x4_t k[2];   // 32 codes: dims [32grp, 32grp + 32) of token m
     i32x2_t v[4];   // 8 codes: dims [8c, 8c+8) of token 4grp+i
@@ -227,11 +219,18 @@ struct Fp8Kv {
 // the kernel
 // ---------------------------------------------------------------------------
 
+// The read-only tables (page table, descriptors, pair counts, bin offsets)
+// reach the kernel as separate `const __restrict__` parameters: proven
+// unaliased with the kernel's stores, their wave-uniform reads compile to
+// scalar loads, which complete on the scalar counter.  Looking up the next
+// slice's page then never waits for the KV loads still in flight (vector
+// loads complete in order, so a vector load of the page index would).
 template <class Kv>
-__device__ inline SliceRsrc slice_rsrc(const AttendArgs& a, int g, int r, int tok, int e) {
+__device__ inline SliceRsrc slice_rsrc(const AttendArgs& a, const int32_t* __restrict__ pt, int g,
+                                       int r, int tok, int e) {
   const bool valid = tok < e;
   const int pidx = (valid ? tok : e - 1) >> 6;
-  const int page = a.page_table[int64_t(r) * a.page_table_stride + pidx];
+  const int page = pt[int64_t(r) * a.page_table_stride + pidx];
   const int nvalid = valid ? min(kSlice, e - tok) : 0;
   const int64_t row = (int64_t(page) * a.num_kv_heads + g) * kPageTokens + (tok & (kPageTokens - 1));
   SliceRsrc rs;
@@ -284,12 +283,36 @@ __device__ inline void consume(WaveState& st, const typename Kv::Buf& b, const b
                                                             0, 0, 0);
 }
 
+__device__ inline void load_q(bf16x8_t* qb, const AttendArgs& a, int g, int r, int n, int grp,
+                              bool fp8_order) {
+  // query group of KV head g for request r as the MFMA B operand
+  const rsrc_t qr = make_rsrc(static_cast<const char*>(a.q) +
+                                  (int64_t(r) * a.num_q_heads + int64_t(g) * a.group) * kHeadDim * 2,
+                              a.group * kHeadDim * 2);
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+    qb[s] = __builtin_bit_cast(
+        bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(
+                      qr, fp8_order ? Fp8Kv::q_offset(n, grp, s) : Bf16Kv::q_offset(n, grp, s), 0, 0));
+}
+
 // Drains one bin: every descriptor in it, in order.
+//
+// Slice i of a descriptor goes to wave i % kWaves; each wave keeps two
+// slices in flight (one computing, one loading).  As soon as a wave has
+// consumed its last slice of descriptor d it issues its first slice of
+// d + 1 and d + 1's query group, before the cross-wave merge of d, so their
+// latency overlaps the merge and the wait for the slowest wave instead of
+// following them.
 template <class Kv>
-__device__ inline void attend_bin(const AttendArgs& a, float* smem, int bin) {
+__device__ inline void attend_bin(const AttendArgs& a, const int32_t* __restrict__ pt,
+                                  const int4* __restrict__ descs,
+                                  const int32_t* __restrict__ pair_count,
+                                  const int32_t* __restrict__ bin_offset, float* smem, int bin) {
   constexpr int kWaves = Kv::kWaves;
-  constexpr int kStages = Kv::kStages;
   constexpr int kThreads = kWaves * 64;
+  constexpr int step = kWaves * kSlice;
+  constexpr bool kFp8 = Kv::kScaled;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15;         // query head within the group (MFMA column)
@@ -297,23 +320,21 @@ __device__ inline void attend_bin(const AttendArgs& a, float* smem, int bin) {
   const int G = a.group;
   const int red_stride = 32 + G * kRedRow;
   float* red = smem + wave * red_stride;
-  const int d_begin = a.bin_offset[bin];
-  const int d_end = a.bin_offset[bin + 1];
+  const int d_begin = bin_offset[bin];
+  const int d_end = bin_offset[bin + 1];
+  if (d_begin >= d_end) return;
+
+  int4 ds = descs[d_begin];
+  bf16x8_t qb[4];
+  typename Kv::Buf buf[2];
+  load_q(qb, a, ds.x, ds.y, n, grp, kFp8);
+  Kv::issue(buf[0], slice_rsrc<Kv>(a, pt, ds.x, ds.y, ds.z + wave * kSlice, ds.w), lane);
 
   for (int d = d_begin; d < d_end; ++d) {
-    const int4 ds = reinterpret_cast<const int4*>(a.desc)[d];
     const int g = ds.x, r = ds.y, t_begin = ds.z, t_end = ds.w;
-    const bool single = a.pair_count[g * a.batch + r] == 1;
-
-    // query group of KV head g for request r as the MFMA B operand
-    const rsrc_t qr = make_rsrc(static_cast<const char*>(a.q) +
-                                    (int64_t(r) * a.num_q_heads + int64_t(g) * G) * kHeadDim * 2,
-                                G * kHeadDim * 2);
-    bf16x8_t qb[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-      qb[s] = __builtin_bit_cast(bf16x8_t,
-                                 __builtin_amdgcn_raw_buffer_load_b128(qr, Kv::q_offset(n, grp, s), 0, 0));
+    const bool single = pair_count[g * a.batch + r] == 1;
+    const bool has_next = d + 1 < d_end;
+    const int4 dn = descs[has_next ? d + 1 : d];
 
     WaveState st;
     st.m = -INFINITY;
@@ -321,20 +342,14 @@ __device__ inline void attend_bin(const AttendArgs& a, float* smem, int bin) {
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb) st.acc[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    // ring of kStages slices in flight: slice i is consumed while slices
-    // i+1 .. i+kStages-1 load; a slice past t_end loads nothing
-    constexpr int step = kWaves * kSlice;
+    // buf[0] already holds (or is loading) this wave's first slice of d; a
+    // slice past t_end loads nothing
     int tok = t_begin + wave * kSlice;
-    typename Kv::Buf buf[kStages];
-#pragma unroll
-    for (int u = 0; u + 1 < kStages; ++u)
-      Kv::issue(buf[u], slice_rsrc<Kv>(a, g, r, tok + u * step, t_end), lane);
     bool more = tok < t_end;
     while (more) {
 #pragma unroll
-      for (int u = 0; u < kStages; ++u) {
-        Kv::issue(buf[(u + kStages - 1) % kStages],
-                  slice_rsrc<Kv>(a, g, r, tok + (kStages - 1) * step, t_end), lane);
+      for (int u = 0; u < 2; ++u) {
+        Kv::issue(buf[u ^ 1], slice_rsrc<Kv>(a, pt, g, r, tok + step, t_end), lane);
         consume<Kv>(st, buf[u], qb, tok, t_end, a.scale_log2, grp);
         tok += step;
         if (tok >= t_end) {
@@ -342,6 +357,10 @@ __device__ inline void attend_bin(const AttendArgs& a, float* smem, int bin) {
           break;
         }
       }
+    }
+    if (has_next) {
+      Kv::issue(buf[0], slice_rsrc<Kv>(a, pt, dn.x, dn.y, dn.z + wave * kSlice, dn.w), lane);
+      load_q(qb, a, dn.x, dn.y, n, grp, kFp8);
     }
 
     // merge the wave states of this descriptor
@@ -384,8 +403,8 @@ __device__ inline void attend_bin(const AttendArgs& a, float* smem, int bin) {
       }
     }
     __syncthreads();
+    ds = dn;
   }
-
 }
 
 // One workgroup per persistent slot.  With grab_counter == null workgroup b
@@ -396,7 +415,9 @@ __device__ inline void attend_bin(const AttendArgs& a, float* smem, int bin) {
 // ticket past the last bin, and the one holding the final ticket returns the
 // counter to zero for the next launch.
 template <class Kv>
-__global__ __launch_bounds__(Kv::kWaves * 64) void attend_kernel(AttendArgs a) {
+__global__ __launch_bounds__(Kv::kWaves * 64) void attend_kernel(
+    AttendArgs a, const int32_t* __restrict__ page_table, const int4* __restrict__ descs,
+    const int32_t* __restrict__ pair_count, const int32_t* __restrict__ bin_offset) {
   extern __shared__ float smem[];
   __shared__ int ticket_lds;
   uint64_t t_start = 0;
@@ -404,8 +425,8 @@ __global__ __launch_bounds__(Kv::kWaves * 64) void attend_kernel(AttendArgs a) {
   int drained = 0;
   if (!a.grab_counter) {
     const int bin = blockIdx.x;
-    attend_bin<Kv>(a, smem, bin);
-    drained = a.bin_offset[bin + 1] - a.bin_offset[bin];
+    attend_bin<Kv>(a, page_table, descs, pair_count, bin_offset, smem, bin);
+    drained = bin_offset[bin + 1] - bin_offset[bin];
   } else {
     for (;;) {
       if (threadIdx.x == 0) ticket_lds = atomicAdd(a.grab_counter, 1);
@@ -417,9 +438,21 @@ __global__ __launch_bounds__(Kv::kWaves * 64) void attend_kernel(AttendArgs a) {
           atomicExch(a.grab_counter, 0);
         break;
       }
-      attend_bin<Kv>(a, smem, ticket);
-      drained += a.bin_offset[ticket + 1] - a.bin_offset[ticket];
+      attend_bin<Kv>(a, page_table, descs, pair_count, bin_offset, smem, ticket);
+      drained += bin_offset[ticket + 1] - bin_offset[ticket];
     }
+  }
+
+  // pairs without tokens: zero output rows (strided over the workgroups)
+  const int npairs = a.num_kv_heads * a.batch;
+  for (int p = blockIdx.x; p < npairs; p += gridDim.x) {
+    if (pair_count[p] != 0) continue;
+    const int g = p / a.batch, r = p % a.batch;
+    uint4* rows = reinterpret_cast<uint4*>(static_cast<char*>(a.out) +
+                                           (int64_t(r) * a.num_q_heads + int64_t(g) * a.group) *
+                                               kHeadDim * 2);
+    for (int i = threadIdx.x; i < a.group * kHeadDim * 2 / 16; i += Kv::kWaves * 64)
+      rows[i] = make_uint4(0, 0, 0, 0);
   }
 
   if (a.trace && threadIdx.x == 0) {
@@ -439,7 +472,11 @@ __global__ __launch_bounds__(Kv::kWaves * 64) void attend_kernel(AttendArgs a) {
 
 hipError_t launch_attend(const AttendArgs& a, int kv_dtype, int grid, hipStream_t s) {
   AttendArgs copy = a;
-  void* args[] = {&copy};
+  const int32_t* pt = a.page_table;
+  const int4* descs = reinterpret_cast<const int4*>(a.desc);
+  const int32_t* pc = a.pair_count;
+  const int32_t* bo = a.bin_offset;
+  void* args[] = {&copy, &pt, &descs, &pc, &bo};
   const bool fp8 = kv_dtype == LBP_KV_FP8_E4M3;
   const int waves = fp8 ? Fp8Kv::kWaves : Bf16Kv::kWaves;
   const size_t lds = size_t(waves) * (32 + a.group * kRedRow) * sizeof(float);

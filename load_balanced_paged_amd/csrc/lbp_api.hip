@@ -108,7 +108,7 @@ lbp_status build_plan(const lbp_config* cfg, int policy, int param, const int32_
   st = plan_shape(cfg, policy, param, batch, &num_bins, &max_desc, &spp, &used);
   if (st != LBP_OK) return st;
   const int npairs = cfg->num_kv_heads * batch;
-  const lbp_plan_offsets off = plan_layout(num_bins, max_desc, npairs);
+  const lbp_plan_offsets off = plan_layout(policy, num_bins, max_desc, npairs);
   if (ws_bytes < off.total) return LBP_ERR_WORKSPACE_TOO_SMALL;
 
   char* base = static_cast<char*>(ws);
@@ -127,6 +127,8 @@ lbp_status build_plan(const lbp_config* cfg, int policy, int param, const int32_
   a.pair_first = reinterpret_cast<int32_t*>(base + off.pair_first);
   a.pair_count = reinterpret_cast<int32_t*>(base + off.pair_count);
   a.scratch = reinterpret_cast<int32_t*>(base + off.scratch);
+  a.split_list = reinterpret_cast<int32_t*>(base + off.split_list);
+  a.max_split = max_split_pairs(policy, num_bins, npairs);
   if (launch_plan(a, static_cast<hipStream_t>(stream)) != hipSuccess) return LBP_ERR_HIP;
 
   lbp_plan_info out;
@@ -147,7 +149,7 @@ lbp_status build_plan(const lbp_config* cfg, int policy, int param, const int32_
 }
 
 lbp_plan_offsets offsets_of(const lbp_plan_info* info) {
-  return plan_layout(info->num_bins, info->max_desc, info->num_kv_heads * info->batch);
+  return plan_layout(info->policy, info->num_bins, info->max_desc, info->num_kv_heads * info->batch);
 }
 
 lbp_status check_split(const lbp_config* cfg, const lbp_plan_info* info, size_t bytes) {
@@ -184,7 +186,7 @@ lbp_status lbp_query_workspace(const lbp_config* cfg, int32_t policy, int32_t pa
   int num_bins, max_desc, spp, used;
   st = plan_shape(cfg, policy, param, cfg->max_batch, &num_bins, &max_desc, &spp, &used);
   if (st != LBP_OK) return st;
-  *plan_bytes = plan_layout(num_bins, max_desc, cfg->num_kv_heads * cfg->max_batch).total;
+  *plan_bytes = plan_layout(policy, num_bins, max_desc, cfg->num_kv_heads * cfg->max_batch).total;
   *split_ws = split_bytes(max_desc, cfg->num_q_heads / cfg->num_kv_heads);
   return LBP_OK;
 }
@@ -309,8 +311,8 @@ lbp_status lbp_combine(const lbp_config* cfg, const lbp_plan_info* info, const v
   const char* pb = static_cast<const char*>(plan_ws_dev);
   const int G = cfg->num_q_heads / cfg->num_kv_heads;
   CombineArgs a;
-  a.pair_first = reinterpret_cast<const int32_t*>(pb + off.pair_first);
-  a.pair_count = reinterpret_cast<const int32_t*>(pb + off.pair_count);
+  a.header = reinterpret_cast<const int32_t*>(pb + off.header);
+  a.split_list = reinterpret_cast<const int32_t*>(pb + off.split_list);
   a.o_part = static_cast<const float*>(split_ws_dev);
   a.lse_part = reinterpret_cast<const float*>(static_cast<const char*>(split_ws_dev) +
                                               split_lse_offset(info->max_desc, G));
@@ -319,8 +321,9 @@ lbp_status lbp_combine(const lbp_config* cfg, const lbp_plan_info* info, const v
   a.num_q_heads = cfg->num_q_heads;
   a.num_kv_heads = cfg->num_kv_heads;
   a.group = G;
-  if (launch_combine(a, cfg->num_kv_heads * info->batch, static_cast<hipStream_t>(stream)) !=
-      hipSuccess)
+  const int max_split =
+      max_split_pairs(info->policy, info->num_bins, cfg->num_kv_heads * info->batch);
+  if (launch_combine(a, max_split, static_cast<hipStream_t>(stream)) != hipSuccess)
     return LBP_ERR_HIP;
   return LBP_OK;
 }

@@ -18,14 +18,23 @@ enum HeaderWord {
   kHdrMagic = 0, kHdrPolicy = 1, kHdrNumBins = 2, kHdrBatch = 3, kHdrKvHeads = 4,
   kHdrTiles = 5, kHdrBudget = 6, kHdrDesc = 7, kHdrUsedBins = 8, kHdrStatus = 9,
   kHdrTicket = 10,  // bin ticket counter of the attention kernel (zero between launches)
+  kHdrSplits = 11,  // number of entries in the split-pair list
   kHdrWords = 16
 };
 constexpr int kStatusClamped = 1;
 
 inline uint64_t align_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
 
+// Capacity of the split-pair list.  In a dynamic plan a pair is split only
+// if one of the U - 1 <= W - 1 internal bin boundaries falls inside it, so at
+// most W - 1 pairs are split; a static plan may split every pair.
+inline int max_split_pairs(int policy, int num_bins, int npairs) {
+  if (policy == LBP_POLICY_DYNAMIC) return npairs < num_bins - 1 ? npairs : num_bins - 1;
+  return npairs;
+}
+
 // Byte layout of the task map for one plan.
-inline lbp_plan_offsets plan_layout(int num_bins, int max_desc, int npairs) {
+inline lbp_plan_offsets plan_layout(int policy, int num_bins, int max_desc, int npairs) {
   lbp_plan_offsets o;
   o.header = 0;
   o.bin_offset = align_up(o.header + kHdrWords * 4, 64);
@@ -33,7 +42,8 @@ inline lbp_plan_offsets plan_layout(int num_bins, int max_desc, int npairs) {
   o.pair_first = align_up(o.desc + uint64_t(max_desc) * 16, 64);
   o.pair_count = align_up(o.pair_first + uint64_t(npairs) * 4, 64);
   o.scratch = align_up(o.pair_count + uint64_t(npairs) * 4, 64);
-  o.total = align_up(o.scratch + uint64_t(npairs) * 4, 256);
+  o.split_list = align_up(o.scratch + uint64_t(npairs) * 4, 64);
+  o.total = align_up(o.split_list + uint64_t(max_split_pairs(policy, num_bins, npairs)) * 16, 256);
   return o;
 }
 
@@ -56,6 +66,8 @@ struct PlanArgs {
   int32_t* pair_first;
   int32_t* pair_count;
   int32_t* scratch;          // first flat tile of every pair (dynamic)
+  int32_t* split_list;       // [max_split][4]: (pair, first descriptor, count, 0)
+  int32_t max_split;
 };
 
 struct AttendArgs {
@@ -80,8 +92,8 @@ struct AttendArgs {
 };
 
 struct CombineArgs {
-  const int32_t* pair_first;
-  const int32_t* pair_count;
+  const int32_t* header;     // kHdrSplits = entries in split_list
+  const int32_t* split_list;
   const float* o_part;
   const float* lse_part;
   void* out;                 // [B][Hq][128] bf16
@@ -92,6 +104,6 @@ struct CombineArgs {
 // the launch itself.
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
 hipError_t launch_attend(const AttendArgs& a, int kv_dtype, int grid, hipStream_t s);
-hipError_t launch_combine(const CombineArgs& a, int npairs, hipStream_t s);
+hipError_t launch_combine(const CombineArgs& a, int max_split, hipStream_t s);
 
 }  // namespace lbp

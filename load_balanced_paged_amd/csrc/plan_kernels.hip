@@ -122,6 +122,16 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     a.pair_first[p] = first;
     first += a.pair_count[p];
   }
+  // pairs split over several descriptors, compacted in pair order
+  int nsplit_local = 0;
+  for (int p = p0; p < p1; ++p) nsplit_local += a.pair_count[p] >= 2;
+  int nsplit;
+  int sfirst = block_exclusive_scan(nsplit_local, scan_lds, &nsplit);
+  for (int p = p0; p < p1; ++p) {
+    const int cnt = a.pair_count[p];
+    if (cnt >= 2 && sfirst < a.max_split)
+      reinterpret_cast<int4*>(a.split_list)[sfirst++] = make_int4(p, a.pair_first[p], cnt, 0);
+  }
   __syncthreads();  // scratch / pair_first / pair_count visible to the block
 
   // descriptors, in parallel over descriptor slots
@@ -194,6 +204,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     h[kHdrUsedBins] = U;
     h[kHdrStatus] = flag_lds ? kStatusClamped : 0;
     for (int i = kHdrStatus + 1; i < kHdrWords; ++i) h[i] = 0;
+    h[kHdrSplits] = min(nsplit, a.max_split);
   }
 }
 

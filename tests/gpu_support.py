@@ -116,7 +116,14 @@ def assert_taskmap_matches(case: Case):
     assert np.array_equal(got["desc"], ref.desc)
     assert np.array_equal(got["pair_first"], ref.pair_first)
     assert np.array_equal(got["pair_count"], ref.pair_count)
+    assert np.array_equal(got["split_list"], expected_split_list(ref))
     return got, ref
+
+
+def expected_split_list(ref):
+    """(pair, first, count, 0) for every pair the oracle's map splits, in pair order."""
+    rows = [(p, ref.pair_first[p], c, 0) for p, c in enumerate(ref.pair_count) if c >= 2]
+    return np.asarray(rows, dtype=np.int32).reshape(-1, 4)
 
 
 def oracle_pairs(case: Case, layer: int, pairs):

@@ -205,7 +205,8 @@ def test_plan_layout(lib):
     assert off.desc % 16 == 0
     assert off.pair_first >= off.desc + 16 * info.max_desc
     assert off.pair_count >= off.pair_first + 4 * 32
-    assert off.total >= off.scratch + 4 * 32
+    assert off.split_list >= off.scratch + 4 * 32 and off.split_list % 16 == 0
+    assert off.total >= off.split_list + 16 * min(32, 256 - 1)
     bad = good_info(c)
     bad.magic = 1
     with pytest.raises(lbp.LbpError):

@@ -7,7 +7,7 @@ import pytest
 import torch
 
 import load_balanced_paged_amd as lbp
-from gpu_support import assert_taskmap_matches, build_case, say
+from gpu_support import assert_taskmap_matches, build_case, expected_split_list, say
 from workloads import CONFIGS
 
 pytestmark = pytest.mark.gpu
@@ -38,6 +38,9 @@ def check(got, ref):
     assert np.array_equal(got["desc"], ref.desc)
     assert np.array_equal(got["pair_first"], ref.pair_first)
     assert np.array_equal(got["pair_count"], ref.pair_count)
+    assert np.array_equal(got["split_list"], expected_split_list(ref))
+    if ref.num_bins and got["policy"] == lbp.LBP_POLICY_DYNAMIC:
+        assert len(got["split_list"]) <= ref.num_bins - 1
 
 
 @pytest.mark.parametrize("name", list(CONFIGS))
