@@ -9,7 +9,8 @@
  * of persistent workgroups; for every layer a persistent attention kernel
  * drains each workgroup's bin and writes one partial output plus its
  * log-sum-exp per task descriptor, and a light combine kernel merges each
- * (KV head, request) pair's partials into the final BF16 output.
+ * (KV head, request) pair's partials into the final BF16 output (or, in
+ * lbp_attend_fused, the attention kernel merges them itself).
  *
  * Conventions for every function below:
  *  - Pointers named *_dev are device pointers; everything else is host
@@ -121,9 +122,13 @@ typedef struct lbp_plan_info {
  *                             with pair_count >= 2, in pair order; max_split =
  *                             min(H_kv * batch, num_bins - 1) for DYNAMIC (a
  *                             pair is split only across one of the U - 1
- *                             internal bin boundaries), H_kv * batch otherwise */
+ *                             internal bin boundaries), H_kv * batch otherwise
+ *   arrive[2][max_desc]       DYNAMIC only (empty otherwise): arrival counters
+ *                             of the merge lbp_attend_fused performs inside
+ *                             the attention kernel; zeroed by the plan and
+ *                             back at zero after every completed launch */
 typedef struct lbp_plan_offsets {
-  uint64_t header, bin_offset, desc, pair_first, pair_count, scratch, split_list, total;
+  uint64_t header, bin_offset, desc, pair_first, pair_count, scratch, split_list, arrive, total;
 } lbp_plan_offsets;
 
 /* Human-readable name of a status code (static storage). */
@@ -167,34 +172,56 @@ lbp_status lbp_plan_static(const lbp_config* cfg, int32_t policy, int32_t param,
 /* Offsets of the task-map sections for a filled plan info (host only). */
 lbp_status lbp_plan_layout(const lbp_plan_info* info, lbp_plan_offsets* offsets);
 
-/* One decode-attention layer: the persistent attention kernel, then the
- * combine kernel, both on `stream` (SGLang x HPC-Ops page, "Scheduling
- * around live KV work", second paragraph; vLLM x HPC-Ops page, bullet
- * "Compute and combine").  Workgroup b drains bin b: for each descriptor it
- * computes softmax(sm_scale * q k^T) v over the descriptor's tokens for the
- * KV head's whole query group, writing the normalised partial output and its
- * log-sum-exp to the descriptor's slot of split_ws_dev; the combine kernel
- * merges each pair's partials under the global softmax normalisation and
- * writes out_dev in BF16 (round to nearest even).  A pair with no tokens
- * gets zeros.  k_scale_dev / v_scale_dev are required for FP8 KV and
- * ignored for BF16. */
+/* One decode-attention layer (SGLang x HPC-Ops page, "Scheduling around live
+ * KV work", second paragraph; vLLM x HPC-Ops page, bullet "Compute and
+ * combine"): the persistent attention kernel, then the combine kernel, both
+ * on `stream`.  Workgroup b drains bin b: for each descriptor it computes
+ * softmax(sm_scale * q k^T) v over the descriptor's tokens for the KV head's
+ * whole query group.  A pair with a single descriptor is written to out_dev
+ * directly; every descriptor of a pair split over several bins writes its
+ * normalised partial output and log-sum-exp to its slot of split_ws_dev, and
+ * the combine kernel merges each such pair under the global softmax
+ * normalisation into out_dev (BF16, round to nearest even).  A pair with no
+ * tokens gets zeros.  k_scale_dev / v_scale_dev are required for FP8 KV and
+ * ignored for BF16.  Concurrent calls that share a plan need their own split
+ * workspaces. */
 lbp_status lbp_attend(const lbp_config* cfg, const lbp_plan_info* info,
                       const void* plan_ws_dev, const void* q_dev, const void* k_cache_dev,
                       const void* v_cache_dev, const float* k_scale_dev,
                       const float* v_scale_dev, void* split_ws_dev, size_t split_ws_bytes,
                       void* out_dev, void* stream);
 
-/* The two halves of lbp_attend, for callers that schedule or time them
- * separately; lbp_combine must follow lbp_attend_partials on the same plan,
- * split workspace and output.  lbp_attend_partials runs the persistent
- * attention kernel: a pair whose tokens fit one descriptor is finished in
- * place (its BF16 output is written to out_dev); every descriptor of a pair
+/* lbp_attend as a single launch (DYNAMIC plans; a static plan runs the same
+ * two launches as lbp_attend): the workgroup that completes a split pair's
+ * last partial merges the pair itself, in split order, through arrival
+ * counters kept in the plan workspace (zeroed by the plan, back at zero
+ * after every completed launch); a pair of more than 16 partials is merged
+ * in two levels (groups of f >= 16 consecutive partials with f * f >= the
+ * count, then the group results).  Saves the second launch where pairs are
+ * split into few partials; a pair split into many partials puts the chain
+ * of the two levels at the end of the kernel, which then costs more than
+ * the combine launch.  Launches that share one plan workspace must be
+ * ordered on one stream (layers are); concurrent calls need their own plan
+ * and split workspaces.  Arguments and results as for lbp_attend (outputs
+ * equal up to the rounding of a differently associated merge). */
+lbp_status lbp_attend_fused(const lbp_config* cfg, const lbp_plan_info* info,
+                            const void* plan_ws_dev, const void* q_dev, const void* k_cache_dev,
+                            const void* v_cache_dev, const float* k_scale_dev,
+                            const float* v_scale_dev, void* split_ws_dev, size_t split_ws_bytes,
+                            void* out_dev, void* stream);
+
+/* The attention kernel and the combine kernel as two launches, for callers
+ * that schedule or time them separately (any policy); lbp_combine must
+ * follow lbp_attend_partials on the same plan, split workspace and output.
+ * lbp_attend_partials runs the persistent attention kernel without the
+ * in-kernel merge: a pair whose tokens fit one descriptor is finished in
+ * place (its BF16 output is written to out_dev), every descriptor of a pair
  * split over several bins writes its partial to the split buffer, and a
  * pair with no tokens gets zero rows.  lbp_combine merges the split pairs
- * (the plan's split_list) into out_dev.  Split-buffer layout: o_part[max_desc][G][128] fp32
- * (normalised partial outputs) at offset 0, then lse_part[max_desc][G] fp32
- * (base-2 log-sum-exp of the sm_scale*log2(e)-scaled scores) at offset
- * align256(max_desc*G*128*4). */
+ * (the plan's split_list) into out_dev.  Split-buffer layout:
+ * o_part[max_desc][G][128] fp32 (normalised partial outputs) at offset 0,
+ * then lse_part[max_desc][G] fp32 (base-2 log-sum-exp of the
+ * sm_scale*log2(e)-scaled scores) at offset align256(max_desc*G*128*4). */
 lbp_status lbp_attend_partials(const lbp_config* cfg, const lbp_plan_info* info,
                                const void* plan_ws_dev, const void* q_dev,
                                const void* k_cache_dev, const void* v_cache_dev,
@@ -202,19 +229,18 @@ lbp_status lbp_attend_partials(const lbp_config* cfg, const lbp_plan_info* info,
                                void* split_ws_dev, size_t split_ws_bytes, void* out_dev,
                                void* stream);
 
-/* lbp_attend_partials that also records, for every workgroup b of the
- * attention kernel, four uint64 at trace_dev[4b .. 4b+3]: its start and end
- * on the device's constant-rate real-time clock (s_memrealtime), the
- * hardware-id register in the low and the XCC id in the high 32 bits, and
- * the number of descriptors it drained.  For profiling the balance of the
- * bins (the method's claim that equal bins finish together).  trace_dev
- * must hold 4 * info->num_bins uint64; NULL is LBP_ERR_INVALID_ARG. */
-lbp_status lbp_attend_partials_traced(const lbp_config* cfg, const lbp_plan_info* info,
-                                      const void* plan_ws_dev, const void* q_dev,
-                                      const void* k_cache_dev, const void* v_cache_dev,
-                                      const float* k_scale_dev, const float* v_scale_dev,
-                                      void* split_ws_dev, size_t split_ws_bytes, void* out_dev,
-                                      uint64_t* trace_dev, void* stream);
+/* lbp_attend that also records, for every workgroup b of the attention
+ * kernel, four uint64 at trace_dev[4b .. 4b+3]: its start and end on the
+ * device's constant-rate real-time clock (s_memrealtime), the hardware-id
+ * register in the low and the XCC id in the high 32 bits, and the number of
+ * descriptors it drained.  For profiling the balance of the bins (the
+ * method's claim that equal bins finish together).  trace_dev must hold
+ * 4 * info->num_bins uint64; NULL is LBP_ERR_INVALID_ARG. */
+lbp_status lbp_attend_traced(const lbp_config* cfg, const lbp_plan_info* info,
+                             const void* plan_ws_dev, const void* q_dev, const void* k_cache_dev,
+                             const void* v_cache_dev, const float* k_scale_dev,
+                             const float* v_scale_dev, void* split_ws_dev, size_t split_ws_bytes,
+                             void* out_dev, uint64_t* trace_dev, void* stream);
 
 lbp_status lbp_combine(const lbp_config* cfg, const lbp_plan_info* info,
                        const void* plan_ws_dev, const void* split_ws_dev,

@@ -37,7 +37,8 @@ PAGE_SIZE = 64
 
 EXPORTED_SYMBOLS = (
     "lbp_status_string", "lbp_version", "lbp_query_workspace", "lbp_plan", "lbp_plan_static",
-    "lbp_plan_layout", "lbp_attend", "lbp_attend_partials", "lbp_attend_partials_traced",
+    "lbp_plan_layout", "lbp_attend", "lbp_attend_fused", "lbp_attend_partials",
+    "lbp_attend_traced",
     "lbp_combine",
 )
 
@@ -76,7 +77,7 @@ class lbp_plan_info(ctypes.Structure):
 class lbp_plan_offsets(ctypes.Structure):
     _fields_ = [(n, ctypes.c_uint64) for n in
                 ("header", "bin_offset", "desc", "pair_first", "pair_count", "scratch", "split_list",
-                 "total")]
+                 "arrive", "total")]
 
 
 class LbpError(RuntimeError):
@@ -114,8 +115,9 @@ def load(path: str = LIB_PATH):
         "lbp_plan_static": (I32, [cfgp, I32, I32, P, I32, P, I64, P, SZ, infop, P]),
         "lbp_plan_layout": (I32, [infop, ctypes.POINTER(lbp_plan_offsets)]),
         "lbp_attend": (I32, [cfgp, infop, P, P, P, P, P, P, P, SZ, P, P]),
+        "lbp_attend_fused": (I32, [cfgp, infop, P, P, P, P, P, P, P, SZ, P, P]),
         "lbp_attend_partials": (I32, [cfgp, infop, P, P, P, P, P, P, P, SZ, P, P]),
-        "lbp_attend_partials_traced": (I32, [cfgp, infop, P, P, P, P, P, P, P, SZ, P, P, P]),
+        "lbp_attend_traced": (I32, [cfgp, infop, P, P, P, P, P, P, P, SZ, P, P, P]),
         "lbp_combine": (I32, [cfgp, infop, P, P, SZ, P, P]),
     }
     for name, (res, args) in sig.items():
@@ -228,15 +230,26 @@ def _kv_ptrs(cfg, k_cache, v_cache, k_scale, v_scale):
             _ptr(v_scale, "v_scale", torch.float32, optional=not fp8))
 
 
-def lbp_attend(cfg, info, plan_ws, q, k_cache, v_cache, k_scale, v_scale, split_ws, out,
-               stream=None):
+def _attend(fn, name, cfg, info, plan_ws, q, k_cache, v_cache, k_scale, v_scale, split_ws, out,
+            stream):
     import torch
     kp, vp, ksp, vsp = _kv_ptrs(cfg, k_cache, v_cache, k_scale, v_scale)
-    _check(load().lbp_attend(ctypes.byref(cfg), ctypes.byref(info), _ptr(plan_ws, "plan_ws"),
-                             _ptr(q, "q", torch.bfloat16), kp, vp, ksp, vsp,
-                             _ptr(split_ws, "split_ws"),
-                             split_ws.numel() * split_ws.element_size(),
-                             _ptr(out, "out", torch.bfloat16), _stream(stream)), "lbp_attend")
+    _check(fn(ctypes.byref(cfg), ctypes.byref(info), _ptr(plan_ws, "plan_ws"),
+              _ptr(q, "q", torch.bfloat16), kp, vp, ksp, vsp, _ptr(split_ws, "split_ws"),
+              split_ws.numel() * split_ws.element_size(), _ptr(out, "out", torch.bfloat16),
+              _stream(stream)), name)
+
+
+def lbp_attend(cfg, info, plan_ws, q, k_cache, v_cache, k_scale, v_scale, split_ws, out,
+               stream=None):
+    _attend(load().lbp_attend, "lbp_attend", cfg, info, plan_ws, q, k_cache, v_cache, k_scale,
+            v_scale, split_ws, out, stream)
+
+
+def lbp_attend_fused(cfg, info, plan_ws, q, k_cache, v_cache, k_scale, v_scale, split_ws, out,
+                     stream=None):
+    _attend(load().lbp_attend_fused, "lbp_attend_fused", cfg, info, plan_ws, q, k_cache, v_cache,
+            k_scale, v_scale, split_ws, out, stream)
 
 
 def lbp_attend_partials(cfg, info, plan_ws, q, k_cache, v_cache, k_scale, v_scale, split_ws,
@@ -251,21 +264,20 @@ def lbp_attend_partials(cfg, info, plan_ws, q, k_cache, v_cache, k_scale, v_scal
            "lbp_attend_partials")
 
 
-def lbp_attend_partials_traced(cfg, info, plan_ws, q, k_cache, v_cache, k_scale, v_scale,
-                               split_ws, out, trace, stream=None):
+def lbp_attend_traced(cfg, info, plan_ws, q, k_cache, v_cache, k_scale, v_scale, split_ws, out,
+                      trace, stream=None):
     """``trace`` is an int64 device tensor of at least 4 * info.num_bins entries."""
     import torch
     if trace.numel() < 4 * info.num_bins:
         raise ValueError("trace needs 4 * num_bins entries")
     kp, vp, ksp, vsp = _kv_ptrs(cfg, k_cache, v_cache, k_scale, v_scale)
-    _check(load().lbp_attend_partials_traced(ctypes.byref(cfg), ctypes.byref(info),
-                                             _ptr(plan_ws, "plan_ws"),
-                                             _ptr(q, "q", torch.bfloat16), kp, vp, ksp, vsp,
-                                             _ptr(split_ws, "split_ws"),
-                                             split_ws.numel() * split_ws.element_size(),
-                                             _ptr(out, "out", torch.bfloat16),
-                                             _ptr(trace, "trace", torch.int64), _stream(stream)),
-           "lbp_attend_partials_traced")
+    _check(load().lbp_attend_traced(ctypes.byref(cfg), ctypes.byref(info),
+                                    _ptr(plan_ws, "plan_ws"), _ptr(q, "q", torch.bfloat16), kp,
+                                    vp, ksp, vsp, _ptr(split_ws, "split_ws"),
+                                    split_ws.numel() * split_ws.element_size(),
+                                    _ptr(out, "out", torch.bfloat16),
+                                    _ptr(trace, "trace", torch.int64), _stream(stream)),
+           "lbp_attend_traced")
 
 
 def lbp_combine(cfg, info, plan_ws, split_ws, out, stream=None):
@@ -301,6 +313,7 @@ def read_taskmap(plan_ws, info: lbp_plan_info) -> dict:
         "pair_first": sl(off.pair_first, npairs),
         "pair_count": sl(off.pair_count, npairs),
         "split_list": sl(off.split_list, 4 * int(h[11])).reshape(-1, 4),
+        "arrive": sl(off.arrive, 2 * info.max_desc if info.policy == LBP_POLICY_DYNAMIC else 0),
     }
 
 

@@ -37,12 +37,28 @@
 //  * A pair served by a single descriptor is finished in place: its
 //    normalised output goes straight to `out` in BF16, and a pair without
 //    tokens gets zero rows here too.  Only pairs split over several bins use
-//    the split buffer and the combine kernel.
+//    the split buffer.
+//  * Merging split pairs (the pages' combine step) can run inside this
+//    kernel instead of a second launch: after draining a bin, a workgroup
+//    counts one arrival per split pair it served on that pair's counter;
+//    the workgroup that completes the count merges the pair's partials in
+//    split order.  A pair of more than 16 partials is merged in two levels
+//    (groups of f >= 16 consecutive partials, f*f >= count, each merged by
+//    the group's last arriver into the group's first slot, then the group
+//    results), so no single workgroup reads more than max(16, f) partials
+//    per query row.  The eight XCDs keep separate L2 caches, and a
+//    device-scope fence would write back or invalidate a whole L2 (hundreds
+//    of such fences serialise and stall every workgroup's streaming), so
+//    split partials are instead written and read with device-coherent
+//    accesses (agent-scope atomic stores and loads, which bypass the
+//    non-coherent cache levels); a workgroup waits for its partial stores to
+//    complete before it counts its arrival.  The last arriver returns each
+//    counter to zero.
 //  * FP8 KV (OCP e4m3 codes with one fp32 scale per token and KV head): codes
 //    are widened to bf16 exactly in registers; the K scale multiplies the
 //    score of its token, the V scale is folded into the probability before
 //    the bf16 P.V product (sum_t p_t (c_t s_t) = sum_t (p_t s_t) c_t).
-#include "lbp_internal.h"
+#include "lse_merge.h"
 
 namespace lbp {
 namespace {
@@ -60,11 +76,11 @@ namespace {
 constexpr int kLoadAux = LBP_KV_LOAD_AUX;  // KV loads: 2 = non-temporal (read once, stream)
 constexpr int kSlice = 16;
 constexpr int kRedRow = kHeadDim + 4;  // padded LDS row (floats) for the merge
+// s_waitcnt operand (gfx9 encoding) waiting for vmcnt = 0 only
+constexpr int kWaitVmcnt0 = 0x0F70;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 typedef int i32x2_t __attribute__((ext_vector_type(2)));
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
@@ -80,6 +96,16 @@ __device__ inline rsrc_t make_rsrc(const void* base, int bytes) {
 __device__ inline uint32_t pack_bf16(float lo, float hi) {
   bf16x2_t v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
   return __builtin_bit_cast(uint32_t, v);
+}
+
+// Device-coherent accesses for everything one workgroup writes and another
+// merges: agent-scope relaxed atomics, i.e. stores that write through and
+// loads that bypass the per-XCD caches.
+__device__ inline void store_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline float load_coherent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __device__ inline float wave_max_across_groups(float x) {
@@ -398,12 +424,175 @@ __device__ inline void attend_bin(const AttendArgs& a, const int32_t* __restrict
         const int64_t row = int64_t(r) * a.num_q_heads + int64_t(g) * G + q;
         static_cast<__bf16*>(a.out)[row * kHeadDim + dim] = static_cast<__bf16>(o / L);
       } else {
-        a.o_part[(int64_t(d) * G + q) * kHeadDim + dim] = o / L;
-        if (dim == 0) a.lse_part[int64_t(d) * G + q] = M + __builtin_amdgcn_logf(L);
+        float* po = a.o_part + (int64_t(d) * G + q) * kHeadDim + dim;
+        float* pl = a.lse_part + int64_t(d) * G + q;
+        const float lse = M + __builtin_amdgcn_logf(L);
+        if (a.fuse) {
+          // merged inside this launch, possibly by a workgroup on another XCD
+          store_coherent(po, o / L);
+          if (dim == 0) store_coherent(pl, lse);
+        } else {
+          *po = o / L;
+          if (dim == 0) *pl = lse;
+        }
       }
     }
     __syncthreads();
     ds = dn;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// merge of split pairs inside the kernel
+// ---------------------------------------------------------------------------
+
+constexpr int kFanIn = 16;        // partials one workgroup merges per query row and level
+constexpr int kMergeUnroll = 8;   // partial rows in flight per thread
+
+// Group size of the merge tree of a pair with cnt >= 2 partials: one group of
+// all of them up to kFanIn, else the smallest f >= kFanIn with f*f >= cnt.
+__device__ inline int merge_group_size(int cnt) {
+  if (cnt <= kFanIn) return cnt;
+  int f = kFanIn;
+  while (f * f < cnt) ++f;
+  return f;
+}
+
+// LDS floats the merge needs: per (row group, head) a max, a sum and a row.
+constexpr int merge_lds_floats(int threads) { return 64 + (threads / 32) * kHeadDim; }
+
+// Merges the n partials in slots slot0, slot0 + stride, ... (in that order)
+// of pair (g, r).  dst < 0: the result is the pair's final output (BF16 to
+// `out`); otherwise it is written back as a partial (row and log-sum-exp)
+// to slot dst.  Thread t owns float4 column t % 32 of head (t / 32) % G and
+// partials i = row group (mod R), R = threads / (32 G); the R states are
+// merged through LDS in a fixed order, so the result is bitwise
+// reproducible.
+template <int kThreads>
+__device__ void merge_run(const AttendArgs& a, float* smem, int slot0, int stride, int n, int dst,
+                          int g, int r) {
+  const int G = a.group;
+  const int R = kThreads / (32 * G);
+  const int t = threadIdx.x;
+  const int c4 = t & 31;
+  const int q = (t >> 5) % G;
+  const int rg = (t >> 5) / G;
+  float m = -INFINITY, l = 0.f;
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  if (rg < R) {
+    for (int i0 = rg; i0 < n; i0 += kMergeUnroll * R) {
+      float ls[kMergeUnroll];
+      f32x4_t v[kMergeUnroll];
+#pragma unroll
+      for (int u = 0; u < kMergeUnroll; ++u) {
+        const int i = i0 + u * R;
+        if (i < n) {
+          const int64_t e = int64_t(slot0 + i * stride) * G + q;
+          const float* row = a.o_part + e * kHeadDim + 4 * c4;
+          ls[u] = load_coherent(a.lse_part + e);
+          v[u] = f32x4_t{load_coherent(row), load_coherent(row + 1), load_coherent(row + 2),
+                         load_coherent(row + 3)};
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kMergeUnroll; ++u)
+        if (i0 + u * R < n) merge_into(m, l, acc, ls[u], v[u]);
+    }
+  }
+  float* red_m = smem;         // [R * G] (R * G <= threads / 32 <= 32)
+  float* red_l = smem + 32;
+  f32x4_t* red_o = reinterpret_cast<f32x4_t*>(smem + 64);   // [R * G][32]
+  if (rg < R) {
+    const int s = rg * G + q;
+    if (c4 == 0) {
+      red_m[s] = m;
+      red_l[s] = l;
+    }
+    red_o[s * 32 + c4] = acc;
+  }
+  __syncthreads();
+  if (rg == 0) {
+    float M = -INFINITY;
+    for (int k = 0; k < R; ++k) M = fmaxf(M, red_m[k * G + q]);
+    float L = 0.f;
+    f32x4_t tot = {0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < R; ++k) {
+      const float c = __builtin_amdgcn_exp2f(red_m[k * G + q] - M);   // 0 for an empty state
+      L += red_l[k * G + q] * c;
+      tot += red_o[(k * G + q) * 32 + c4] * c;
+    }
+    if (dst < 0) {
+      store_bf16x4(a.out, int64_t(r) * a.num_q_heads + int64_t(g) * G + q, c4, tot / L);
+    } else {
+      const int64_t e = int64_t(dst) * G + q;
+      const f32x4_t o = tot / L;
+      float* row = a.o_part + e * kHeadDim + 4 * c4;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) store_coherent(row + j, o[j]);
+      if (c4 == 0) store_coherent(a.lse_part + e, M + __builtin_amdgcn_logf(L));
+    }
+  }
+  __syncthreads();
+}
+
+// Waits until every device-coherent store of the workgroup has completed
+// (each wave waits for its own vector memory operations, then all meet at
+// the barrier), so they are visible on every XCD.
+__device__ inline void publish_workgroup() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __syncthreads();
+}
+
+// One arrival on `counter` (after publish_workgroup).  True, in every thread,
+// for the workgroup whose arrival completes `target`; that workgroup resets
+// the counter for the next launch.  Its later coherent loads are issued
+// after the count has returned, so they see every arrived partial.
+__device__ inline bool arrive(int32_t* counter, int target, int* flag) {
+  if (threadIdx.x == 0) {
+    const int old = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const bool last = old == target - 1;
+    if (last) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *flag = last;
+  }
+  __syncthreads();
+  return *flag != 0;
+}
+
+// After a bin is drained: arrivals (and, for the last arriver, the merge)
+// for every split pair among its descriptors.
+template <int kThreads>
+__device__ void finish_split_pairs(const AttendArgs& a, const int4* __restrict__ descs,
+                                   const int32_t* __restrict__ pair_count,
+                                   const int32_t* __restrict__ pair_first, float* smem, int* flag,
+                                   int d_begin, int d_end) {
+  for (int d = d_begin; d < d_end; ++d) {
+    const int4 ds = descs[d];
+    const int p = ds.x * a.batch + ds.y;
+    const int cnt = pair_count[p];
+    if (cnt < 2) continue;
+    publish_workgroup();
+    const int first = pair_first[p];
+    const int f = merge_group_size(cnt);
+    const int ngroups = (cnt + f - 1) / f;
+    // level 1 (only with several groups): this descriptor's group, merged
+    // into the group's first slot; level 2: the pair, merged into `out`
+    const int lead = first + (d - first) / f * f;
+    const int members = min(f, first + cnt - lead);
+    bool grouped = ngroups > 1;
+    if (!(grouped ? arrive(a.arrive_group + lead, members, flag)
+                  : arrive(a.arrive_pair + first, cnt, flag)))
+      continue;
+    for (;;) {
+      merge_run<kThreads>(a, smem, grouped ? lead : first, grouped || ngroups == 1 ? 1 : f,
+                          grouped ? members : ngroups > 1 ? ngroups : cnt, grouped ? lead : -1,
+                          ds.x, ds.y);
+      if (!grouped) break;
+      grouped = false;
+      publish_workgroup();
+      if (!arrive(a.arrive_pair + first, ngroups, flag)) break;
+    }
   }
 }
 
@@ -417,30 +606,35 @@ __device__ inline void attend_bin(const AttendArgs& a, const int32_t* __restrict
 template <class Kv>
 __global__ __launch_bounds__(Kv::kWaves * 64) void attend_kernel(
     AttendArgs a, const int32_t* __restrict__ page_table, const int4* __restrict__ descs,
-    const int32_t* __restrict__ pair_count, const int32_t* __restrict__ bin_offset) {
-  extern __shared__ float smem[];
+    const int32_t* __restrict__ pair_count, const int32_t* __restrict__ bin_offset,
+    const int32_t* __restrict__ pair_first) {
+  constexpr int kThreads = Kv::kWaves * 64;
+  extern __shared__ __attribute__((aligned(16))) float smem[];   // f32x4 rows are stored in it
   __shared__ int ticket_lds;
+  __shared__ int arrive_lds;
   uint64_t t_start = 0;
   if (a.trace) t_start = __builtin_amdgcn_s_memrealtime();
   int drained = 0;
-  if (!a.grab_counter) {
-    const int bin = blockIdx.x;
+  // the first bin: this workgroup's own, or the first ticket
+  auto next_bin = [&]() {
+    if (threadIdx.x == 0) ticket_lds = atomicAdd(a.grab_counter, 1);
+    __syncthreads();
+    const int ticket = ticket_lds;
+    __syncthreads();
+    if (ticket >= a.num_bins && threadIdx.x == 0 && ticket == a.num_bins + int(gridDim.x) - 1)
+      atomicExch(a.grab_counter, 0);
+    return ticket;
+  };
+  int bin = a.grab_counter ? next_bin() : int(blockIdx.x);
+  while (bin < a.num_bins) {
     attend_bin<Kv>(a, page_table, descs, pair_count, bin_offset, smem, bin);
-    drained = bin_offset[bin + 1] - bin_offset[bin];
-  } else {
-    for (;;) {
-      if (threadIdx.x == 0) ticket_lds = atomicAdd(a.grab_counter, 1);
-      __syncthreads();
-      const int ticket = ticket_lds;
-      __syncthreads();
-      if (ticket >= a.num_bins) {
-        if (threadIdx.x == 0 && ticket == a.num_bins + int(gridDim.x) - 1)
-          atomicExch(a.grab_counter, 0);
-        break;
-      }
-      attend_bin<Kv>(a, page_table, descs, pair_count, bin_offset, smem, ticket);
-      drained += bin_offset[ticket + 1] - bin_offset[ticket];
-    }
+    const int d_begin = bin_offset[bin], d_end = bin_offset[bin + 1];
+    if (a.fuse)
+      finish_split_pairs<kThreads>(a, descs, pair_count, pair_first, smem, &arrive_lds, d_begin,
+                                   d_end);
+    drained += d_end - d_begin;
+    if (!a.grab_counter) break;
+    bin = next_bin();
   }
 
   // pairs without tokens: zero output rows (strided over the workgroups)
@@ -451,7 +645,7 @@ __global__ __launch_bounds__(Kv::kWaves * 64) void attend_kernel(
     uint4* rows = reinterpret_cast<uint4*>(static_cast<char*>(a.out) +
                                            (int64_t(r) * a.num_q_heads + int64_t(g) * a.group) *
                                                kHeadDim * 2);
-    for (int i = threadIdx.x; i < a.group * kHeadDim * 2 / 16; i += Kv::kWaves * 64)
+    for (int i = threadIdx.x; i < a.group * kHeadDim * 2 / 16; i += kThreads)
       rows[i] = make_uint4(0, 0, 0, 0);
   }
 
@@ -476,10 +670,13 @@ hipError_t launch_attend(const AttendArgs& a, int kv_dtype, int grid, hipStream_
   const int4* descs = reinterpret_cast<const int4*>(a.desc);
   const int32_t* pc = a.pair_count;
   const int32_t* bo = a.bin_offset;
-  void* args[] = {&copy, &pt, &descs, &pc, &bo};
+  const int32_t* pf = a.pair_first;
+  void* args[] = {&copy, &pt, &descs, &pc, &bo, &pf};
   const bool fp8 = kv_dtype == LBP_KV_FP8_E4M3;
   const int waves = fp8 ? Fp8Kv::kWaves : Bf16Kv::kWaves;
-  const size_t lds = size_t(waves) * (32 + a.group * kRedRow) * sizeof(float);
+  size_t lds = size_t(waves) * (32 + a.group * kRedRow) * sizeof(float);
+  const size_t merge_lds = size_t(merge_lds_floats(waves * 64)) * sizeof(float);
+  if (a.fuse && merge_lds > lds) lds = merge_lds;
   const void* fn = fp8 ? reinterpret_cast<const void*>(&attend_kernel<Fp8Kv>)
                        : reinterpret_cast<const void*>(&attend_kernel<Bf16Kv>);
   if (grid <= 0) return hipSuccess;

@@ -23,35 +23,15 @@
 // memory round trips (the list entry, then the rows) for up to 128 splits.
 // The eight per-thread states are merged in LDS in a fixed order (bitwise
 // deterministic).
-#include "lbp_internal.h"
+#include "lse_merge.h"
 
 namespace lbp {
 namespace {
 
 constexpr int kThreads = 256;
 constexpr int kLanesPerRow = kHeadDim / 4;              // 32 float4 per 128-dim row
-constexpr int kRowGroups = kThreads / kLanesPerRow;     // 32 partial rows per sweep
+constexpr int kRowGroups = kThreads / kLanesPerRow;     // 8 partial rows per sweep
 constexpr int kUnroll = 16;
-
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-
-__device__ inline void store_row4(void* out, int64_t row, int c4, f32x4_t v) {
-  bf16x2_t lo = {static_cast<__bf16>(v[0]), static_cast<__bf16>(v[1])};
-  bf16x2_t hi = {static_cast<__bf16>(v[2]), static_cast<__bf16>(v[3])};
-  uint2 packed = make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
-  reinterpret_cast<uint2*>(static_cast<char*>(out) + row * kHeadDim * 2)[c4] = packed;
-}
-
-// Online merge of one more (lse, row) into a (max, sum, acc) state.
-__device__ inline void merge_into(float& m, float& l, f32x4_t& acc, float lse, f32x4_t o) {
-  const float m_new = fmaxf(m, lse);
-  const float a = __builtin_amdgcn_exp2f(m - m_new);   // 0 while the state is empty
-  const float b = __builtin_amdgcn_exp2f(lse - m_new);
-  acc = acc * a + o * b;
-  l = l * a + b;
-  m = m_new;
-}
 
 __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
   __shared__ float red_m[kRowGroups];
@@ -109,7 +89,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
     L += red_l[i] * c;
     tot += red_o[i][c4] * c;
   }
-  store_row4(a.out, row, c4, tot / L);
+  store_bf16x4(a.out, row, c4, tot / L);
 }
 
 }  // namespace

@@ -129,6 +129,8 @@ lbp_status build_plan(const lbp_config* cfg, int policy, int param, const int32_
   a.scratch = reinterpret_cast<int32_t*>(base + off.scratch);
   a.split_list = reinterpret_cast<int32_t*>(base + off.split_list);
   a.max_split = max_split_pairs(policy, num_bins, npairs);
+  a.arrive = reinterpret_cast<int32_t*>(base + off.arrive);
+  a.arrive_words = arrive_words(policy, max_desc);
   if (launch_plan(a, static_cast<hipStream_t>(stream)) != hipSuccess) return LBP_ERR_HIP;
 
   lbp_plan_info out;
@@ -217,12 +219,13 @@ lbp_status lbp_plan_layout(const lbp_plan_info* info, lbp_plan_offsets* offsets)
   return LBP_OK;
 }
 
-static lbp_status attend_partials_impl(const lbp_config* cfg, const lbp_plan_info* info,
-                                       const void* plan_ws_dev, const void* q_dev,
-                                       const void* k_cache_dev, const void* v_cache_dev,
-                                       const float* k_scale_dev, const float* v_scale_dev,
-                                       void* split_ws_dev, size_t split_ws_bytes, void* out_dev,
-                                       uint64_t* trace_dev, void* stream) {
+// The attention kernel alone (fuse = false) or, for a dynamic plan with
+// fuse = true, the attention kernel that also merges the split pairs.
+static lbp_status attend_impl(const lbp_config* cfg, const lbp_plan_info* info,
+                              const void* plan_ws_dev, const void* q_dev, const void* k_cache_dev,
+                              const void* v_cache_dev, const float* k_scale_dev,
+                              const float* v_scale_dev, void* split_ws_dev, size_t split_ws_bytes,
+                              void* out_dev, uint64_t* trace_dev, bool fuse, void* stream) {
   lbp_status st = check_config(cfg);
   if (st != LBP_OK) return st;
   if ((st = check_info(cfg, info)) != LBP_OK) return st;
@@ -239,6 +242,7 @@ static lbp_status attend_partials_impl(const lbp_config* cfg, const lbp_plan_inf
   a.bin_offset = reinterpret_cast<const int32_t*>(pb + off.bin_offset);
   a.desc = reinterpret_cast<const int32_t*>(pb + off.desc);
   a.pair_count = reinterpret_cast<const int32_t*>(pb + off.pair_count);
+  a.pair_first = reinterpret_cast<const int32_t*>(pb + off.pair_first);
   a.page_table = info->page_table_dev;
   a.page_table_stride = info->page_table_stride;
   a.q = q_dev;
@@ -266,6 +270,10 @@ static lbp_status attend_partials_impl(const lbp_config* cfg, const lbp_plan_inf
       a.grab_counter = reinterpret_cast<int32_t*>(const_cast<char*>(pb) + off.header) + kHdrTicket;
     }
   }
+  a.fuse = fuse && info->policy == LBP_POLICY_DYNAMIC;
+  int32_t* arrive = reinterpret_cast<int32_t*>(const_cast<char*>(pb) + off.arrive);
+  a.arrive_pair = a.fuse ? arrive : nullptr;
+  a.arrive_group = a.fuse ? arrive + info->max_desc : nullptr;
   a.batch = info->batch;
   a.num_q_heads = cfg->num_q_heads;
   a.num_kv_heads = cfg->num_kv_heads;
@@ -282,21 +290,8 @@ lbp_status lbp_attend_partials(const lbp_config* cfg, const lbp_plan_info* info,
                                const float* k_scale_dev, const float* v_scale_dev,
                                void* split_ws_dev, size_t split_ws_bytes, void* out_dev,
                                void* stream) {
-  return attend_partials_impl(cfg, info, plan_ws_dev, q_dev, k_cache_dev, v_cache_dev,
-                              k_scale_dev, v_scale_dev, split_ws_dev, split_ws_bytes, out_dev,
-                              nullptr, stream);
-}
-
-lbp_status lbp_attend_partials_traced(const lbp_config* cfg, const lbp_plan_info* info,
-                                      const void* plan_ws_dev, const void* q_dev,
-                                      const void* k_cache_dev, const void* v_cache_dev,
-                                      const float* k_scale_dev, const float* v_scale_dev,
-                                      void* split_ws_dev, size_t split_ws_bytes, void* out_dev,
-                                      uint64_t* trace_dev, void* stream) {
-  if (!trace_dev) return LBP_ERR_INVALID_ARG;
-  return attend_partials_impl(cfg, info, plan_ws_dev, q_dev, k_cache_dev, v_cache_dev,
-                              k_scale_dev, v_scale_dev, split_ws_dev, split_ws_bytes, out_dev,
-                              trace_dev, stream);
+  return attend_impl(cfg, info, plan_ws_dev, q_dev, k_cache_dev, v_cache_dev, k_scale_dev,
+                     v_scale_dev, split_ws_dev, split_ws_bytes, out_dev, nullptr, false, stream);
 }
 
 lbp_status lbp_combine(const lbp_config* cfg, const lbp_plan_info* info, const void* plan_ws_dev,
@@ -328,16 +323,46 @@ lbp_status lbp_combine(const lbp_config* cfg, const lbp_plan_info* info, const v
   return LBP_OK;
 }
 
+// The attention kernel, then (unless it merged the split pairs itself, which
+// only the fused entry point on a dynamic plan asks for) the combine kernel.
+static lbp_status attend_full(const lbp_config* cfg, const lbp_plan_info* info,
+                              const void* plan_ws_dev, const void* q_dev, const void* k_cache_dev,
+                              const void* v_cache_dev, const float* k_scale_dev,
+                              const float* v_scale_dev, void* split_ws_dev, size_t split_ws_bytes,
+                              void* out_dev, uint64_t* trace_dev, bool fuse, void* stream) {
+  if (!info) return LBP_ERR_MISMATCH;
+  lbp_status st = attend_impl(cfg, info, plan_ws_dev, q_dev, k_cache_dev, v_cache_dev,
+                              k_scale_dev, v_scale_dev, split_ws_dev, split_ws_bytes, out_dev,
+                              trace_dev, fuse, stream);
+  if (st != LBP_OK || (fuse && info->policy == LBP_POLICY_DYNAMIC)) return st;
+  return lbp_combine(cfg, info, plan_ws_dev, split_ws_dev, split_ws_bytes, out_dev, stream);
+}
+
 lbp_status lbp_attend(const lbp_config* cfg, const lbp_plan_info* info, const void* plan_ws_dev,
                       const void* q_dev, const void* k_cache_dev, const void* v_cache_dev,
                       const float* k_scale_dev, const float* v_scale_dev, void* split_ws_dev,
                       size_t split_ws_bytes, void* out_dev, void* stream) {
-  if (!out_dev) return LBP_ERR_INVALID_ARG;
-  lbp_status st = lbp_attend_partials(cfg, info, plan_ws_dev, q_dev, k_cache_dev, v_cache_dev,
-                                      k_scale_dev, v_scale_dev, split_ws_dev, split_ws_bytes,
-                                      out_dev, stream);
-  if (st != LBP_OK) return st;
-  return lbp_combine(cfg, info, plan_ws_dev, split_ws_dev, split_ws_bytes, out_dev, stream);
+  return attend_full(cfg, info, plan_ws_dev, q_dev, k_cache_dev, v_cache_dev, k_scale_dev,
+                     v_scale_dev, split_ws_dev, split_ws_bytes, out_dev, nullptr, false, stream);
+}
+
+lbp_status lbp_attend_fused(const lbp_config* cfg, const lbp_plan_info* info,
+                            const void* plan_ws_dev, const void* q_dev, const void* k_cache_dev,
+                            const void* v_cache_dev, const float* k_scale_dev,
+                            const float* v_scale_dev, void* split_ws_dev, size_t split_ws_bytes,
+                            void* out_dev, void* stream) {
+  return attend_full(cfg, info, plan_ws_dev, q_dev, k_cache_dev, v_cache_dev, k_scale_dev,
+                     v_scale_dev, split_ws_dev, split_ws_bytes, out_dev, nullptr, true, stream);
+}
+
+lbp_status lbp_attend_traced(const lbp_config* cfg, const lbp_plan_info* info,
+                             const void* plan_ws_dev, const void* q_dev, const void* k_cache_dev,
+                             const void* v_cache_dev, const float* k_scale_dev,
+                             const float* v_scale_dev, void* split_ws_dev, size_t split_ws_bytes,
+                             void* out_dev, uint64_t* trace_dev, void* stream) {
+  if (!trace_dev) return LBP_ERR_INVALID_ARG;
+  return attend_full(cfg, info, plan_ws_dev, q_dev, k_cache_dev, v_cache_dev, k_scale_dev,
+                     v_scale_dev, split_ws_dev, split_ws_bytes, out_dev, trace_dev, false, stream);
 }
 
 }  // extern "C"

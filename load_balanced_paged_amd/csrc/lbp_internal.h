@@ -33,6 +33,12 @@ inline int max_split_pairs(int policy, int num_bins, int npairs) {
   return npairs;
 }
 
+// Arrival counters of the in-kernel merge of split pairs (dynamic plans):
+// one per descriptor slot for the pair level and one for the group level.
+inline int arrive_words(int policy, int max_desc) {
+  return policy == LBP_POLICY_DYNAMIC ? 2 * max_desc : 0;
+}
+
 // Byte layout of the task map for one plan.
 inline lbp_plan_offsets plan_layout(int policy, int num_bins, int max_desc, int npairs) {
   lbp_plan_offsets o;
@@ -43,7 +49,8 @@ inline lbp_plan_offsets plan_layout(int policy, int num_bins, int max_desc, int 
   o.pair_count = align_up(o.pair_first + uint64_t(npairs) * 4, 64);
   o.scratch = align_up(o.pair_count + uint64_t(npairs) * 4, 64);
   o.split_list = align_up(o.scratch + uint64_t(npairs) * 4, 64);
-  o.total = align_up(o.split_list + uint64_t(max_split_pairs(policy, num_bins, npairs)) * 16, 256);
+  o.arrive = align_up(o.split_list + uint64_t(max_split_pairs(policy, num_bins, npairs)) * 16, 64);
+  o.total = align_up(o.arrive + uint64_t(arrive_words(policy, max_desc)) * 4, 256);
   return o;
 }
 
@@ -68,12 +75,15 @@ struct PlanArgs {
   int32_t* scratch;          // first flat tile of every pair (dynamic)
   int32_t* split_list;       // [max_split][4]: (pair, first descriptor, count, 0)
   int32_t max_split;
+  int32_t* arrive;           // arrival counters, zeroed here
+  int32_t arrive_words;
 };
 
 struct AttendArgs {
   const int32_t* bin_offset;
   const int32_t* desc;
   const int32_t* pair_count;
+  const int32_t* pair_first;
   const int32_t* page_table;
   int64_t page_table_stride;
   const void* q;             // [B][Hq][128] bf16
@@ -86,6 +96,9 @@ struct AttendArgs {
   void* out;                 // [B][Hq][128] bf16: single-descriptor pairs land here
   uint64_t* trace;           // optional [grid][4] workgroup records, or null
   int32_t* grab_counter;     // null: workgroup b drains bin b; else the ticket counter
+  int32_t* arrive_pair;      // [max_desc] pair-level arrival counters (at pair_first)
+  int32_t* arrive_group;     // [max_desc] group-level arrival counters (at the group's first slot)
+  int32_t fuse;              // 1: merge split pairs in this kernel (dynamic plans)
   int32_t num_bins;
   int32_t batch, num_q_heads, num_kv_heads, group;
   float scale_log2;          // sm_scale * log2(e)

@@ -134,6 +134,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   }
   __syncthreads();  // scratch / pair_first / pair_count visible to the block
 
+  // arrival counters of the attention kernel's merge start at zero
+  for (int i = tid; i < a.arrive_words; i += kPlanThreads) a.arrive[i] = 0;
+
   // descriptors, in parallel over descriptor slots
   for (int d = tid; d < D; d += kPlanThreads) {
     int p = last_le(a.pair_first, npairs, d);

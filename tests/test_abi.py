@@ -206,7 +206,12 @@ def test_plan_layout(lib):
     assert off.pair_first >= off.desc + 16 * info.max_desc
     assert off.pair_count >= off.pair_first + 4 * 32
     assert off.split_list >= off.scratch + 4 * 32 and off.split_list % 16 == 0
-    assert off.total >= off.split_list + 16 * min(32, 256 - 1)
+    assert off.arrive >= off.split_list + 16 * min(32, 256 - 1)
+    assert off.total >= off.arrive + 4 * 2 * info.max_desc       # two counters per slot
+    static = good_info(c)
+    static.policy = lbp.LBP_POLICY_STATIC_SPLITS
+    soff = lbp.lbp_plan_layout(static)
+    assert soff.total - soff.arrive < 256                          # no counters
     bad = good_info(c)
     bad.magic = 1
     with pytest.raises(lbp.LbpError):

@@ -146,9 +146,8 @@ def test_traced_run_records_every_workgroup(gpu_lib):
     ref = run_attend(case).clone()
     out = torch.zeros_like(lay.q)
     trace = torch.zeros(4 * case.info.num_bins, dtype=torch.int64, device="cuda")
-    lbp.lbp_attend_partials_traced(case.cfg, case.info, case.plan_ws, lay.q, lay.k_cache,
-                                   lay.v_cache, None, None, case.split_ws, out, trace)
-    lbp.lbp_combine(case.cfg, case.info, case.plan_ws, case.split_ws, out)
+    lbp.lbp_attend_traced(case.cfg, case.info, case.plan_ws, lay.q, lay.k_cache, lay.v_cache,
+                          None, None, case.split_ws, out, trace)
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
     t = trace.view(-1, 4).cpu().numpy()
