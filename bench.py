@@ -3,7 +3,8 @@
 
 One step = one decode-attention layer: the persistent split-KV attention
 kernel plus the combine kernel (``lbp_attend``), reusing one task map built
-once per decode step (``lbp_plan``).  Inputs are seeded synthetic tensors
+once per decode step (``lbp_plan``).  The single-launch variant
+(``lbp_attend_fused``) is timed beside it as "fused_us_per_step".  Inputs are seeded synthetic tensors
 already resident in HBM; layers rotate over distinct KV copies (at least
 1 GB in all) so the 256 MB Infinity Cache cannot serve the KV bytes.
 
@@ -57,6 +58,9 @@ def parse_args():
     ap.add_argument("--workloads", default="mixed,uniform,skewed,fp8",
                     help="comma list; the first is the headline (default mixed)")
     ap.add_argument("--no-static", action="store_true", help="skip the static split-KV comparison")
+    ap.add_argument("--no-fused", action="store_true",
+                    help="skip the lbp_attend_fused timing (profiler runs: keeps every launch of "
+                         "the attention kernel a plain one)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="wall-clock budget of the CPU oracle sample")
@@ -105,8 +109,9 @@ class Bench:
             self.plans[key] = (info, plan_ws, split_ws)
         return self.plans[key]
 
-    def step_fn(self, policy=0, param=0):
-        """A closure launching one attend on layer i with pre-marshalled arguments."""
+    def step_fn(self, policy=0, param=0, fused=False):
+        """A closure launching one attend (lbp_attend, or lbp_attend_fused) on
+        layer i with pre-marshalled arguments."""
         import ctypes
         lbp = self.lbp
         lib = lbp.load()
@@ -123,10 +128,12 @@ class Bench:
                          P(L.k_cache.data_ptr()), P(L.v_cache.data_ptr()), ks, vs,
                          P(split_ws.data_ptr()), sbytes, P(self.outs[i].data_ptr()), stream))
 
+        fn = lib.lbp_attend_fused if fused else lib.lbp_attend
+
         def run(i):
-            st = lib.lbp_attend(*args[i % self.layers])
+            st = fn(*args[i % self.layers])
             if st != 0:
-                raise RuntimeError(f"lbp_attend: {lbp.status_name(st)}")
+                raise RuntimeError(f"attend: {lbp.status_name(st)}")
         return run, args
 
     # -- timing ------------------------------------------------------------
@@ -141,8 +148,8 @@ class Bench:
                 i += 1
             torch.cuda.synchronize()
 
-    def time_steps(self, steps, warmup, policy=0, param=0, eager=False):
-        run, _ = self.step_fn(policy, param)
+    def time_steps(self, steps, warmup, policy=0, param=0, eager=False, fused=False):
+        run, _ = self.step_fn(policy, param, fused)
         for i in range(warmup):
             run(i)
         torch.cuda.synchronize()
@@ -154,7 +161,7 @@ class Bench:
                 s = torch.cuda.Stream()
                 s.wait_stream(torch.cuda.current_stream())
                 with torch.cuda.stream(s):
-                    run_g, _ = self.step_fn(policy, param)   # args bound to the capture stream
+                    run_g, _ = self.step_fn(policy, param, fused)   # bound to the capture stream
                     with torch.cuda.graph(graph, stream=s):
                         for i in range(steps):
                             run_g(i)
@@ -316,6 +323,9 @@ def bench_one(name, lbp, args, headline):
                pct_of_hbm_peak=round(100 * gbs / HBM_PEAK_GBS, 1), timing=mode,
                kv_bytes_per_layer=b.wl.kv_bytes, total_tokens=b.wl.total_tokens,
                workgroups=info.num_bins, layers=b.layers)
+    if not args.no_fused:
+        fms, _ = b.time_steps(args.steps, args.warmup, eager=args.eager, fused=True)
+        res["fused_us_per_step"] = round(fms * 1e3, 2)      # lbp_attend_fused, one launch
     k_mean, k_med, k_min, k_max = b.time_attend_kernel(max(20, min(args.steps, 100)))
     res["attend_kernel_us"] = {"mean": round(k_mean, 2), "median": round(k_med, 2),
                                "min": round(k_min, 2), "max": round(k_max, 2)}
