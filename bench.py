@@ -422,6 +422,8 @@ def main():
         "amortized_us_per_layer": head["amortized_us_per_layer"],
         "attend_kernel_us": head["attend_kernel_us"],
     }
+    if "fused_us_per_step" in head:
+        out["fused_us_per_step"] = head["fused_us_per_step"]
     if "static_splits" in head:
         out["static_splits"] = head["static_splits"]
     if "cpu_baseline" in head:
