@@ -115,6 +115,9 @@ typedef struct lbp_plan_info {
  *               ticket counter of the attention kernel (0 between launches)
  *               [11] number of split_list entries
  *   bin_offset[num_bins + 1]  descriptors of bin b: [bin_offset[b], bin_offset[b+1])
+ *   bin_first[num_bins][4]    copy of desc[bin_offset[b]] (zeros for an empty bin),
+ *                             so a workgroup reads its bin's range and first
+ *                             descriptor in one round trip
  *   desc[max_desc][4]         (kv_head, request, token_begin, token_end)
  *   pair_first[H_kv * batch], pair_count[H_kv * batch]; pair p = kv_head * batch + request
  *   scratch[H_kv * batch]     assign-kernel scratch
@@ -128,7 +131,8 @@ typedef struct lbp_plan_info {
  *                             the attention kernel; zeroed by the plan and
  *                             back at zero after every completed launch */
 typedef struct lbp_plan_offsets {
-  uint64_t header, bin_offset, desc, pair_first, pair_count, scratch, split_list, arrive, total;
+  uint64_t header, bin_offset, bin_first, desc, pair_first, pair_count, scratch, split_list,
+      arrive, total;
 } lbp_plan_offsets;
 
 /* Human-readable name of a status code (static storage). */

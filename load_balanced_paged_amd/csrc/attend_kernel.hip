@@ -334,7 +334,8 @@ template <class Kv>
 __device__ inline void attend_bin(const AttendArgs& a, const int32_t* __restrict__ pt,
                                   const int4* __restrict__ descs,
                                   const int32_t* __restrict__ pair_count,
-                                  const int32_t* __restrict__ bin_offset, float* smem, int bin) {
+                                  const int32_t* __restrict__ bin_offset,
+                                  const int4* __restrict__ bin_first, float* smem, int bin) {
   constexpr int kWaves = Kv::kWaves;
   constexpr int kThreads = kWaves * 64;
   constexpr int step = kWaves * kSlice;
@@ -346,11 +347,13 @@ __device__ inline void attend_bin(const AttendArgs& a, const int32_t* __restrict
   const int G = a.group;
   const int red_stride = 32 + G * kRedRow;
   float* red = smem + wave * red_stride;
+  // range and first descriptor are independent loads: one round trip
   const int d_begin = bin_offset[bin];
   const int d_end = bin_offset[bin + 1];
+  int4 ds = bin_first[bin];
+  asm volatile("" ::"s"(ds.x), "s"(ds.y), "s"(ds.z), "s"(ds.w));   // keep the load above the exit
   if (d_begin >= d_end) return;
 
-  int4 ds = descs[d_begin];
   bf16x8_t qb[4];
   typename Kv::Buf buf[2];
   load_q(qb, a, ds.x, ds.y, n, grp, kFp8);
@@ -607,7 +610,7 @@ template <class Kv>
 __global__ __launch_bounds__(Kv::kWaves * 64) void attend_kernel(
     AttendArgs a, const int32_t* __restrict__ page_table, const int4* __restrict__ descs,
     const int32_t* __restrict__ pair_count, const int32_t* __restrict__ bin_offset,
-    const int32_t* __restrict__ pair_first) {
+    const int32_t* __restrict__ pair_first, const int4* __restrict__ bin_first) {
   constexpr int kThreads = Kv::kWaves * 64;
   extern __shared__ __attribute__((aligned(16))) float smem[];   // f32x4 rows are stored in it
   __shared__ int ticket_lds;
@@ -627,7 +630,7 @@ __global__ __launch_bounds__(Kv::kWaves * 64) void attend_kernel(
   };
   int bin = a.grab_counter ? next_bin() : int(blockIdx.x);
   while (bin < a.num_bins) {
-    attend_bin<Kv>(a, page_table, descs, pair_count, bin_offset, smem, bin);
+    attend_bin<Kv>(a, page_table, descs, pair_count, bin_offset, bin_first, smem, bin);
     const int d_begin = bin_offset[bin], d_end = bin_offset[bin + 1];
     if (a.fuse)
       finish_split_pairs<kThreads>(a, descs, pair_count, pair_first, smem, &arrive_lds, d_begin,
@@ -671,7 +674,8 @@ hipError_t launch_attend(const AttendArgs& a, int kv_dtype, int grid, hipStream_
   const int32_t* pc = a.pair_count;
   const int32_t* bo = a.bin_offset;
   const int32_t* pf = a.pair_first;
-  void* args[] = {&copy, &pt, &descs, &pc, &bo, &pf};
+  const int4* bf = reinterpret_cast<const int4*>(a.bin_first);
+  void* args[] = {&copy, &pt, &descs, &pc, &bo, &pf, &bf};
   const bool fp8 = kv_dtype == LBP_KV_FP8_E4M3;
   const int waves = fp8 ? Fp8Kv::kWaves : Bf16Kv::kWaves;
   size_t lds = size_t(waves) * (32 + a.group * kRedRow) * sizeof(float);

@@ -38,8 +38,12 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
   __shared__ float red_l[kRowGroups];
   __shared__ f32x4_t red_o[kRowGroups][kLanesPerRow];
 
-  if (int(blockIdx.x) >= a.header[kHdrSplits]) return;
+  // The grid never exceeds the list's capacity, so the entry can be loaded
+  // together with the entry count (one round trip instead of two).
+  const int nsplit = a.header[kHdrSplits];
   const int4 e = reinterpret_cast<const int4*>(a.split_list)[blockIdx.x];
+  asm volatile("" ::"s"(e.x), "s"(e.y), "s"(e.z));   // keeps the entry load above the exit
+  if (int(blockIdx.x) >= nsplit) return;
   const int p = e.x;             // pair = kv_head * batch + request
   const int first = e.y;
   const int cnt = e.z;           // >= 2

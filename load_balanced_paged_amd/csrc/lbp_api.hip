@@ -123,6 +123,7 @@ lbp_status build_plan(const lbp_config* cfg, int policy, int param, const int32_
   a.max_tokens = cfg->max_pages_per_seq * kPageTokens;
   a.header = reinterpret_cast<int32_t*>(base + off.header);
   a.bin_offset = reinterpret_cast<int32_t*>(base + off.bin_offset);
+  a.bin_first = reinterpret_cast<int32_t*>(base + off.bin_first);
   a.desc = reinterpret_cast<int32_t*>(base + off.desc);
   a.pair_first = reinterpret_cast<int32_t*>(base + off.pair_first);
   a.pair_count = reinterpret_cast<int32_t*>(base + off.pair_count);
@@ -240,6 +241,7 @@ static lbp_status attend_impl(const lbp_config* cfg, const lbp_plan_info* info,
   const int G = cfg->num_q_heads / cfg->num_kv_heads;
   AttendArgs a;
   a.bin_offset = reinterpret_cast<const int32_t*>(pb + off.bin_offset);
+  a.bin_first = reinterpret_cast<const int32_t*>(pb + off.bin_first);
   a.desc = reinterpret_cast<const int32_t*>(pb + off.desc);
   a.pair_count = reinterpret_cast<const int32_t*>(pb + off.pair_count);
   a.pair_first = reinterpret_cast<const int32_t*>(pb + off.pair_first);

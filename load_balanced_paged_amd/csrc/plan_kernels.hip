@@ -193,7 +193,14 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     }
   }
 
-  __syncthreads();
+  __syncthreads();  // descriptors and bin offsets visible to the block
+  // each bin's first descriptor, read by the attention kernel with its range
+  for (int b = tid; b < a.num_bins; b += kPlanThreads) {
+    const int d = a.bin_offset[b];
+    int4 v = make_int4(0, 0, 0, 0);
+    if (d < a.bin_offset[b + 1]) v = reinterpret_cast<const int4*>(a.desc)[d];
+    reinterpret_cast<int4*>(a.bin_first)[b] = v;
+  }
   if (tid == 0) {
     int32_t* h = a.header;
     h[kHdrMagic] = int32_t(LBP_PLAN_MAGIC);

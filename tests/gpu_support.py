@@ -117,6 +117,10 @@ def assert_taskmap_matches(case: Case):
     assert np.array_equal(got["pair_first"], ref.pair_first)
     assert np.array_equal(got["pair_count"], ref.pair_count)
     assert np.array_equal(got["split_list"], expected_split_list(ref))
+    for b in range(ref.num_bins):
+        d0, d1 = ref.bin_offset[b], ref.bin_offset[b + 1]
+        want = ref.desc[d0] if d1 > d0 else np.zeros(4, np.int32)
+        assert np.array_equal(got["bin_first"][b], want), b
     return got, ref
 
 

@@ -41,6 +41,10 @@ def check(got, ref):
     assert np.array_equal(got["split_list"], expected_split_list(ref))
     if ref.num_bins and got["policy"] == lbp.LBP_POLICY_DYNAMIC:
         assert len(got["split_list"]) <= ref.num_bins - 1
+    for b in range(ref.num_bins):
+        d0, d1 = ref.bin_offset[b], ref.bin_offset[b + 1]
+        want = ref.desc[d0] if d1 > d0 else np.zeros(4, np.int32)
+        assert np.array_equal(got["bin_first"][b], want), b
 
 
 @pytest.mark.parametrize("name", list(CONFIGS))
