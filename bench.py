@@ -62,6 +62,8 @@ def parse_args():
                     help="skip the lbp_attend_fused timing (profiler runs: keeps every launch of "
                          "the attention kernel a plain one)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-table3", action="store_true",
+                    help="skip the six FP8-KV length mixes of the vLLM x HPC-Ops page, Table 3")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="wall-clock budget of the CPU oracle sample")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
@@ -75,12 +77,12 @@ def parse_args():
 # ---------------------------------------------------------------------------
 
 class Bench:
-    def __init__(self, name, lbp):
+    def __init__(self, name, lbp, wcfg=None, layers=None):
         from workloads import CONFIGS, make_workload
         self.lbp = lbp
         self.name = name
-        self.wcfg = CONFIGS[name]
-        self.layers = LAYERS[name]
+        self.wcfg = wcfg if wcfg is not None else CONFIGS[name]
+        self.layers = layers if layers is not None else LAYERS[name]
         t0 = time.time()
         self.wl = make_workload(self.wcfg, device="cuda", layers=self.layers)
         torch.cuda.synchronize()
@@ -109,9 +111,10 @@ class Bench:
             self.plans[key] = (info, plan_ws, split_ws)
         return self.plans[key]
 
-    def step_fn(self, policy=0, param=0, fused=False):
-        """A closure launching one attend (lbp_attend, or lbp_attend_fused) on
-        layer i with pre-marshalled arguments."""
+    def step_fn(self, policy=0, param=0, fused=False, fp8q=False):
+        """A closure launching one attend (lbp_attend, lbp_attend_fused, or
+        lbp_attend_fp8q with the layer's query in e4m3) on layer i with
+        pre-marshalled arguments."""
         import ctypes
         lbp = self.lbp
         lib = lbp.load()
@@ -121,14 +124,19 @@ class Bench:
         P = ctypes.c_void_p
         sbytes = split_ws.numel()
         args = []
+        if fp8q and not hasattr(self, "q8"):
+            from workloads import quantize_query_e4m3
+            self.q8 = [quantize_query_e4m3(L.q) for L in self.wl.layers]
         for i, L in enumerate(self.wl.layers):
             ks = P(L.k_scale.data_ptr()) if L.k_scale is not None else None
             vs = P(L.v_scale.data_ptr()) if L.v_scale is not None else None
-            args.append((cfgp, infop, P(plan_ws.data_ptr()), P(L.q.data_ptr()),
-                         P(L.k_cache.data_ptr()), P(L.v_cache.data_ptr()), ks, vs,
+            q = (P(self.q8[i][0].data_ptr()), P(self.q8[i][1].data_ptr())) if fp8q else \
+                (P(L.q.data_ptr()),)
+            args.append((cfgp, infop, P(plan_ws.data_ptr())) + q +
+                        (P(L.k_cache.data_ptr()), P(L.v_cache.data_ptr()), ks, vs,
                          P(split_ws.data_ptr()), sbytes, P(self.outs[i].data_ptr()), stream))
 
-        fn = lib.lbp_attend_fused if fused else lib.lbp_attend
+        fn = lib.lbp_attend_fp8q if fp8q else lib.lbp_attend_fused if fused else lib.lbp_attend
 
         def run(i):
             st = fn(*args[i % self.layers])
@@ -148,8 +156,8 @@ class Bench:
                 i += 1
             torch.cuda.synchronize()
 
-    def time_steps(self, steps, warmup, policy=0, param=0, eager=False, fused=False):
-        run, _ = self.step_fn(policy, param, fused)
+    def time_steps(self, steps, warmup, policy=0, param=0, eager=False, fused=False, fp8q=False):
+        run, _ = self.step_fn(policy, param, fused, fp8q)
         for i in range(warmup):
             run(i)
         torch.cuda.synchronize()
@@ -161,7 +169,7 @@ class Bench:
                 s = torch.cuda.Stream()
                 s.wait_stream(torch.cuda.current_stream())
                 with torch.cuda.stream(s):
-                    run_g, _ = self.step_fn(policy, param, fused)   # bound to the capture stream
+                    run_g, _ = self.step_fn(policy, param, fused, fp8q)   # capture stream
                     with torch.cuda.graph(graph, stream=s):
                         for i in range(steps):
                             run_g(i)
@@ -326,6 +334,9 @@ def bench_one(name, lbp, args, headline):
     if not args.no_fused:
         fms, _ = b.time_steps(args.steps, args.warmup, eager=args.eager, fused=True)
         res["fused_us_per_step"] = round(fms * 1e3, 2)      # lbp_attend_fused, one launch
+    if b.wcfg.kv_dtype == "fp8_e4m3" and not args.no_fused:
+        qms, _ = b.time_steps(args.steps, args.warmup, eager=args.eager, fp8q=True)
+        res["fp8q_us_per_step"] = round(qms * 1e3, 2)       # lbp_attend_fp8q: e4m3 query
     k_mean, k_med, k_min, k_max = b.time_attend_kernel(max(20, min(args.steps, 100)))
     res["attend_kernel_us"] = {"mean": round(k_mean, 2), "median": round(k_med, 2),
                                "min": round(k_min, 2), "max": round(k_max, 2)}
@@ -359,6 +370,64 @@ def bench_one(name, lbp, args, headline):
         f"({achieved:.0f} GB/s), plan {res['plan_us']:.1f} us")
     b.free()
     return res
+
+
+# vLLM x HPC-Ops page, Table 3 (H20, FP8 KV): dynamic ms, static split-KV ms,
+# dynamic-vs-static ratio per A x B mix.  Context only: other hardware.
+H20_TABLE3 = {
+    "64x0.5K": (0.013, 0.013, 1.00),
+    "64x4K": (0.033, 0.043, 1.32),
+    "32x0.125K+32x4K": (0.020, 0.033, 1.59),
+    "2x32K+30x4K": (0.032, 0.056, 1.76),
+    "1x64K+15x4K": (0.042, 0.097, 2.32),
+    "1x128K+31x4K": (0.063, 0.186, 2.95),
+}
+ROTATE_BYTES = 1 << 30     # rotating KV set per mix: 4x the 256 MB Infinity Cache
+
+
+def bench_table3(lbp, args):
+    """Dynamic against static split-KV on the six Table 3 mixes (8/1 heads, FP8 KV)."""
+    from workloads import TABLE3
+    out = {}
+    for mix, wcfg in TABLE3.items():
+        tokens = sum(wcfg.fixed_lengths)
+        kv = tokens * wcfg.num_kv_heads * wcfg.kv_bytes_per_token_head
+        layers = max(1, min(128, math.ceil(ROTATE_BYTES / kv)))
+        b = Bench(wcfg.name, lbp, wcfg=wcfg, layers=layers)
+        info, _, _ = b.plan()
+        b.warm(0.1)
+        ms, mode = b.time_steps(args.steps, args.warmup, eager=args.eager)
+        fms, _ = b.time_steps(args.steps, args.warmup, eager=args.eager, fused=True)
+        qms, _ = b.time_steps(args.steps, args.warmup, eager=args.eager, fp8q=True)
+        b.check_finite()
+        us = ms * 1e3
+        W = info.num_bins
+        s_grid = max(1, math.ceil(W / (wcfg.num_kv_heads * wcfg.batch)))
+        static = {}
+        for S in sorted({s_grid, 1, 2, 4, 8, 16, 32, 64}):
+            sms, _ = b.time_steps(min(args.steps, 50), 2, lbp.LBP_POLICY_STATIC_SPLITS, S,
+                                  eager=args.eager)
+            static[S] = sms * 1e3
+        best = min(static, key=static.get)
+        h20 = H20_TABLE3[mix]
+        out[mix] = {
+            "us_per_step": round(us, 2), "fused_us_per_step": round(fms * 1e3, 2),
+            "fp8q_us_per_step": round(qms * 1e3, 2),
+            "kv_gbs": round(kv / (us * 1e-6) / 1e9, 1), "kv_bytes_per_layer": kv,
+            "layers": layers, "timing": mode,
+            "static_S_grid_matched": s_grid, "static_us_grid_matched": round(static[s_grid], 2),
+            "static_best_S": best, "static_us_best": round(static[best], 2),
+            "dynamic_vs_static_grid_matched": round(static[s_grid] / us, 3),
+            "dynamic_vs_static_best": round(static[best] / us, 3),
+            "static_us_by_S": {str(k): round(v, 2) for k, v in static.items()},
+            "h20_context": {"dynamic_us": h20[0] * 1e3, "static_us": h20[1] * 1e3,
+                            "dynamic_vs_static": h20[2]},
+        }
+        log(f"table3 {mix}: dynamic {us:.1f} us, static S={s_grid} {static[s_grid]:.1f} us "
+            f"({static[s_grid] / us:.2f}x), best static S={best} {static[best]:.1f} us "
+            f"({static[best] / us:.2f}x); H20: {h20[2]:.2f}x")
+        b.free()
+    return out
 
 
 def main():
@@ -422,8 +491,9 @@ def main():
         "amortized_us_per_layer": head["amortized_us_per_layer"],
         "attend_kernel_us": head["attend_kernel_us"],
     }
-    if "fused_us_per_step" in head:
-        out["fused_us_per_step"] = head["fused_us_per_step"]
+    for k in ("fused_us_per_step", "fp8q_us_per_step"):
+        if k in head:
+            out[k] = head[k]
     if "static_splits" in head:
         out["static_splits"] = head["static_splits"]
     if "cpu_baseline" in head:
@@ -431,6 +501,12 @@ def main():
     if len(results) > 1:
         out["other_workloads"] = {r["workload"]: {k: v for k, v in r.items() if k != "workload"}
                                   for r in results[1:]}
+    if not args.no_table3:
+        out["table3"] = {
+            "workload": "vLLM x HPC-Ops page Table 3 A x B mixes, FP8 e4m3 KV + fp32 scales, "
+                        "8 query / 1 KV head, head_dim 128, page 64",
+            "mixes": bench_table3(lbp, args),
+        }
     print(json.dumps(out), flush=True)
 
 

@@ -233,6 +233,24 @@ lbp_status lbp_attend_partials(const lbp_config* cfg, const lbp_plan_info* info,
                                void* split_ws_dev, size_t split_ws_bytes, void* out_dev,
                                void* stream);
 
+/* lbp_attend with an FP8 query, for FP8 KV (cfg->kv_dtype = LBP_KV_FP8_E4M3;
+ * otherwise LBP_ERR_UNSUPPORTED).  The SGLang x HPC-Ops page, "A fused
+ * attention prologue", has the prologue emit Q in FP8 with a per-token,
+ * per-head scale and hand both to the attention kernel without
+ * requantization; this entry point takes them in that form:
+ *  - q_codes_dev [batch][num_q_heads][128] uint8 OCP e4m3 codes,
+ *  - q_scale_dev [batch][num_q_heads] fp32; query element = e4m3(code) * scale.
+ * Scores are computed from the K and Q codes on the fp8 MFMA with fp32
+ * accumulation, then scaled by q_scale * k_scale * sm_scale; everything else
+ * (plan, split buffer, combine, output) is as for lbp_attend.
+ * q_scale_dev NULL is LBP_ERR_INVALID_ARG. */
+lbp_status lbp_attend_fp8q(const lbp_config* cfg, const lbp_plan_info* info,
+                           const void* plan_ws_dev, const uint8_t* q_codes_dev,
+                           const float* q_scale_dev, const void* k_cache_dev,
+                           const void* v_cache_dev, const float* k_scale_dev,
+                           const float* v_scale_dev, void* split_ws_dev, size_t split_ws_bytes,
+                           void* out_dev, void* stream);
+
 /* lbp_attend that also records, for every workgroup b of the attention
  * kernel, four uint64 at trace_dev[4b .. 4b+3]: its start and end on the
  * device's constant-rate real-time clock (s_memrealtime), the hardware-id

@@ -38,7 +38,7 @@ PAGE_SIZE = 64
 EXPORTED_SYMBOLS = (
     "lbp_status_string", "lbp_version", "lbp_query_workspace", "lbp_plan", "lbp_plan_static",
     "lbp_plan_layout", "lbp_attend", "lbp_attend_fused", "lbp_attend_partials",
-    "lbp_attend_traced",
+    "lbp_attend_traced", "lbp_attend_fp8q",
     "lbp_combine",
 )
 
@@ -118,6 +118,7 @@ def load(path: str = LIB_PATH):
         "lbp_attend_fused": (I32, [cfgp, infop, P, P, P, P, P, P, P, SZ, P, P]),
         "lbp_attend_partials": (I32, [cfgp, infop, P, P, P, P, P, P, P, SZ, P, P]),
         "lbp_attend_traced": (I32, [cfgp, infop, P, P, P, P, P, P, P, SZ, P, P, P]),
+        "lbp_attend_fp8q": (I32, [cfgp, infop, P, P, P, P, P, P, P, P, SZ, P, P]),
         "lbp_combine": (I32, [cfgp, infop, P, P, SZ, P, P]),
     }
     for name, (res, args) in sig.items():
@@ -250,6 +251,20 @@ def lbp_attend_fused(cfg, info, plan_ws, q, k_cache, v_cache, k_scale, v_scale, 
                      stream=None):
     _attend(load().lbp_attend_fused, "lbp_attend_fused", cfg, info, plan_ws, q, k_cache, v_cache,
             k_scale, v_scale, split_ws, out, stream)
+
+
+def lbp_attend_fp8q(cfg, info, plan_ws, q_codes, q_scale, k_cache, v_cache, k_scale, v_scale,
+                    split_ws, out, stream=None):
+    """FP8 query (uint8 e4m3 codes [B, Hq, 128] + fp32 scales [B, Hq]) over FP8 KV."""
+    import torch
+    kp, vp, ksp, vsp = _kv_ptrs(cfg, k_cache, v_cache, k_scale, v_scale)
+    _check(load().lbp_attend_fp8q(ctypes.byref(cfg), ctypes.byref(info), _ptr(plan_ws, "plan_ws"),
+                                  _ptr(q_codes, "q_codes", torch.uint8),
+                                  _ptr(q_scale, "q_scale", torch.float32), kp, vp, ksp, vsp,
+                                  _ptr(split_ws, "split_ws"),
+                                  split_ws.numel() * split_ws.element_size(),
+                                  _ptr(out, "out", torch.bfloat16), _stream(stream)),
+           "lbp_attend_fp8q")
 
 
 def lbp_attend_partials(cfg, info, plan_ws, q, k_cache, v_cache, k_scale, v_scale, split_ws,

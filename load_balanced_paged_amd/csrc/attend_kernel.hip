@@ -70,6 +70,9 @@ namespace {
 #ifndef LBP_FP8_WAVES
 #define LBP_FP8_WAVES 12
 #endif
+#ifndef LBP_FP8Q_WAVES
+#define LBP_FP8Q_WAVES 12
+#endif
 #ifndef LBP_KV_LOAD_AUX
 #define LBP_KV_LOAD_AUX 2
 #endif
@@ -127,6 +130,20 @@ struct SliceRsrc {
   rsrc_t k, v, ks, vs;
 };
 
+// BF16 query group of KV head g for request r as the MFMA B operand, in the
+// dim order of format Kv (clipped to the group's G rows: other heads read 0).
+template <class Kv>
+__device__ inline void load_q_bf16(bf16x8_t* qb, const AttendArgs& a, int g, int r, int n,
+                                   int grp) {
+  const rsrc_t qr = make_rsrc(static_cast<const char*>(a.q) +
+                                  (int64_t(r) * a.num_q_heads + int64_t(g) * a.group) * kHeadDim * 2,
+                              a.group * kHeadDim * 2);
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+    qb[s] = __builtin_bit_cast(
+        bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(qr, Kv::q_offset(n, grp, s), 0, 0));
+}
+
 struct Bf16Kv {
   static constexpr int kRowBytes = kHeadDim * 2;
   static constexpr bool kScaled = false;
@@ -137,6 +154,13 @@ struct Bf16Kv {
   };
   // Q B-operand for k-step s: dims [32s + 8grp, +8) of head n.
   __device__ static int q_offset(int n, int grp, int s) { return n * 256 + 64 * s + 16 * grp; }
+  struct Q {
+    bf16x8_t v[4];
+  };
+  __device__ static void load_q(Q& q, const AttendArgs& a, int g, int r, int n, int grp) {
+    load_q_bf16<Bf16Kv>(q.v, a, g, r, n, grp);
+  }
+  __device__ static float score_scale(const Q&, float scale_log2) { return scale_log2; }
 
   __device__ static void issue(Buf& b, const SliceRsrc& rs, int lane) {
     const int m = lane & 15, grp = lane >> 4;
@@ -148,11 +172,11 @@ struct Bf16Kv {
       b.v[i] = __builtin_amdgcn_raw_buffer_load_b128(rs.v, (4 * grp + i) * kRowBytes + 16 * m, 0, kLoadAux);
   }
 
-  __device__ static f32x4_t scores(const Buf& b, const bf16x8_t* qb) {
+  __device__ static f32x4_t scores(const Buf& b, const Q& q) {
     f32x4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int k = 0; k < 4; ++k)
-      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, b.k[k]), qb[k], s,
+      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, b.k[k]), q.v[k], s,
                                                   0, 0, 0);
     return s;
   }
@@ -190,6 +214,13 @@ struct Fp8Kv {
   };
   // Q B-operand for k-step s: dims [32grp + 8s, +8) of head n.
   __device__ static int q_offset(int n, int grp, int s) { return n * 256 + 64 * grp + 16 * s; }
+  struct Q {
+    bf16x8_t v[4];
+  };
+  __device__ static void load_q(Q& q, const AttendArgs& a, int g, int r, int n, int grp) {
+    load_q_bf16<Fp8Kv>(q.v, a, g, r, n, grp);
+  }
+  __device__ static float score_scale(const Q&, float scale_log2) { return scale_log2; }
 
   __device__ static void issue(Buf& b, const SliceRsrc& rs, int lane) {
     const int m = lane & 15, grp = lane >> 4;
@@ -210,14 +241,14 @@ struct Fp8Kv {
                               __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(int(codes), 1.0f, kHiWord));
   }
 
-  __device__ static f32x4_t scores(const Buf& b, const bf16x8_t* qb) {
+  __device__ static f32x4_t scores(const Buf& b, const Q& q) {
     f32x4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       uint32_t c0 = b.k[k >> 1][2 * (k & 1)], c1 = b.k[k >> 1][2 * (k & 1) + 1];
       i32x4_t w = {int(widen2<false>(c0)), int(widen2<true>(c0)), int(widen2<false>(c1)),
                    int(widen2<true>(c1))};
-      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, w), qb[k], s, 0,
+      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, w), q.v[k], s, 0,
                                                   0, 0);
     }
     return s;
@@ -238,6 +269,45 @@ struct Fp8Kv {
     else
       r = i32x2_t{int(widen2<false>(p01)), int(widen2<false>(p23))};
     return __builtin_bit_cast(i16x4_t, r);
+  }
+};
+
+
+// FP8 KV with an FP8 query (OCP e4m3 codes and one fp32 scale per request and
+// query head, as the fused attention prologue emits them): the score product
+// runs on the fp8 x fp8 MFMA straight from the K and Q codes, with no
+// widening; the Q scale joins the softmax scale per head.  V and the
+// probabilities take the FP8 KV path above.
+struct Fp8KvQ8 : Fp8Kv {
+  static constexpr int kWaves = LBP_FP8Q_WAVES;
+  struct Q {
+    i32x4_t c[2];   // codes of dims [32grp, 32grp + 32) of head n
+    float scale;    // the head's Q scale (0 for columns past the group)
+  };
+  __device__ static void load_q(Q& q, const AttendArgs& a, int g, int r, int n, int grp) {
+    const int64_t row0 = int64_t(r) * a.num_q_heads + int64_t(g) * a.group;
+    const rsrc_t qr = make_rsrc(static_cast<const char*>(a.q) + row0 * kHeadDim,
+                                a.group * kHeadDim);
+    const rsrc_t sr = make_rsrc(a.q_scale + row0, a.group * 4);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      q.c[h] = __builtin_amdgcn_raw_buffer_load_b128(qr, n * kHeadDim + 32 * grp + 16 * h, 0, 0);
+    q.scale = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sr, 4 * n, 0, 0));
+  }
+  __device__ static float score_scale(const Q& q, float scale_log2) { return q.scale * scale_log2; }
+
+  // 8 codes (one k-step of 32 dims split over the four lane groups) as an
+  // fp8 MFMA operand.
+  __device__ static long codes8(const i32x4_t* c, int k) {
+    typedef long i64x2_t __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(i64x2_t, c[k >> 1])[k & 1];
+  }
+  __device__ static f32x4_t scores(const Buf& b, const Q& q) {
+    f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      s = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(codes8(b.k, k), codes8(q.c, k), s, 0, 0, 0);
+    return s;
   }
 };
 
@@ -279,9 +349,9 @@ struct WaveState {
 };
 
 template <class Kv>
-__device__ inline void consume(WaveState& st, const typename Kv::Buf& b, const bf16x8_t* qb,
+__device__ inline void consume(WaveState& st, const typename Kv::Buf& b, const typename Kv::Q& q,
                                int tok, int e, float scale_log2, int grp) {
-  f32x4_t s = Kv::scores(b, qb);
+  f32x4_t s = Kv::scores(b, q);
   f32x4_t ks = Kv::k_scales(b);
   f32x4_t vs = Kv::v_scales(b);
   float x[4];
@@ -309,19 +379,6 @@ __device__ inline void consume(WaveState& st, const typename Kv::Buf& b, const b
                                                             0, 0, 0);
 }
 
-__device__ inline void load_q(bf16x8_t* qb, const AttendArgs& a, int g, int r, int n, int grp,
-                              bool fp8_order) {
-  // query group of KV head g for request r as the MFMA B operand
-  const rsrc_t qr = make_rsrc(static_cast<const char*>(a.q) +
-                                  (int64_t(r) * a.num_q_heads + int64_t(g) * a.group) * kHeadDim * 2,
-                              a.group * kHeadDim * 2);
-#pragma unroll
-  for (int s = 0; s < 4; ++s)
-    qb[s] = __builtin_bit_cast(
-        bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(
-                      qr, fp8_order ? Fp8Kv::q_offset(n, grp, s) : Bf16Kv::q_offset(n, grp, s), 0, 0));
-}
-
 // Drains one bin: every descriptor in it, in order.
 //
 // Slice i of a descriptor goes to wave i % kWaves; each wave keeps two
@@ -339,7 +396,6 @@ __device__ inline void attend_bin(const AttendArgs& a, const int32_t* __restrict
   constexpr int kWaves = Kv::kWaves;
   constexpr int kThreads = kWaves * 64;
   constexpr int step = kWaves * kSlice;
-  constexpr bool kFp8 = Kv::kScaled;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15;         // query head within the group (MFMA column)
@@ -354,9 +410,9 @@ __device__ inline void attend_bin(const AttendArgs& a, const int32_t* __restrict
   asm volatile("" ::"s"(ds.x), "s"(ds.y), "s"(ds.z), "s"(ds.w));   // keep the load above the exit
   if (d_begin >= d_end) return;
 
-  bf16x8_t qb[4];
+  typename Kv::Q qb;
   typename Kv::Buf buf[2];
-  load_q(qb, a, ds.x, ds.y, n, grp, kFp8);
+  Kv::load_q(qb, a, ds.x, ds.y, n, grp);
   Kv::issue(buf[0], slice_rsrc<Kv>(a, pt, ds.x, ds.y, ds.z + wave * kSlice, ds.w), lane);
 
   for (int d = d_begin; d < d_end; ++d) {
@@ -379,7 +435,7 @@ __device__ inline void attend_bin(const AttendArgs& a, const int32_t* __restrict
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         Kv::issue(buf[u ^ 1], slice_rsrc<Kv>(a, pt, g, r, tok + step, t_end), lane);
-        consume<Kv>(st, buf[u], qb, tok, t_end, a.scale_log2, grp);
+        consume<Kv>(st, buf[u], qb, tok, t_end, Kv::score_scale(qb, a.scale_log2), grp);
         tok += step;
         if (tok >= t_end) {
           more = false;
@@ -389,7 +445,7 @@ __device__ inline void attend_bin(const AttendArgs& a, const int32_t* __restrict
     }
     if (has_next) {
       Kv::issue(buf[0], slice_rsrc<Kv>(a, pt, dn.x, dn.y, dn.z + wave * kSlice, dn.w), lane);
-      load_q(qb, a, dn.x, dn.y, n, grp, kFp8);
+      Kv::load_q(qb, a, dn.x, dn.y, n, grp);
     }
 
     // merge the wave states of this descriptor
@@ -667,7 +723,7 @@ __global__ __launch_bounds__(Kv::kWaves * 64) void attend_kernel(
 
 }  // namespace
 
-hipError_t launch_attend(const AttendArgs& a, int kv_dtype, int grid, hipStream_t s) {
+hipError_t launch_attend(const AttendArgs& a, AttendKind kind, int grid, hipStream_t s) {
   AttendArgs copy = a;
   const int32_t* pt = a.page_table;
   const int4* descs = reinterpret_cast<const int4*>(a.desc);
@@ -676,13 +732,24 @@ hipError_t launch_attend(const AttendArgs& a, int kv_dtype, int grid, hipStream_
   const int32_t* pf = a.pair_first;
   const int4* bf = reinterpret_cast<const int4*>(a.bin_first);
   void* args[] = {&copy, &pt, &descs, &pc, &bo, &pf, &bf};
-  const bool fp8 = kv_dtype == LBP_KV_FP8_E4M3;
-  const int waves = fp8 ? Fp8Kv::kWaves : Bf16Kv::kWaves;
+  int waves;
+  const void* fn;
+  switch (kind) {
+    case kAttendFp8:
+      waves = Fp8Kv::kWaves;
+      fn = reinterpret_cast<const void*>(&attend_kernel<Fp8Kv>);
+      break;
+    case kAttendFp8Q8:
+      waves = Fp8KvQ8::kWaves;
+      fn = reinterpret_cast<const void*>(&attend_kernel<Fp8KvQ8>);
+      break;
+    default:
+      waves = Bf16Kv::kWaves;
+      fn = reinterpret_cast<const void*>(&attend_kernel<Bf16Kv>);
+  }
   size_t lds = size_t(waves) * (32 + a.group * kRedRow) * sizeof(float);
   const size_t merge_lds = size_t(merge_lds_floats(waves * 64)) * sizeof(float);
   if (a.fuse && merge_lds > lds) lds = merge_lds;
-  const void* fn = fp8 ? reinterpret_cast<const void*>(&attend_kernel<Fp8Kv>)
-                       : reinterpret_cast<const void*>(&attend_kernel<Bf16Kv>);
   if (grid <= 0) return hipSuccess;
   return hipLaunchKernel(fn, dim3(grid), dim3(waves * 64), args, lds, s);
 }

@@ -226,7 +226,8 @@ static lbp_status attend_impl(const lbp_config* cfg, const lbp_plan_info* info,
                               const void* plan_ws_dev, const void* q_dev, const void* k_cache_dev,
                               const void* v_cache_dev, const float* k_scale_dev,
                               const float* v_scale_dev, void* split_ws_dev, size_t split_ws_bytes,
-                              void* out_dev, uint64_t* trace_dev, bool fuse, void* stream) {
+                              void* out_dev, uint64_t* trace_dev, bool fuse, void* stream,
+                              const float* q_scale_dev = nullptr) {
   lbp_status st = check_config(cfg);
   if (st != LBP_OK) return st;
   if ((st = check_info(cfg, info)) != LBP_OK) return st;
@@ -248,6 +249,7 @@ static lbp_status attend_impl(const lbp_config* cfg, const lbp_plan_info* info,
   a.page_table = info->page_table_dev;
   a.page_table_stride = info->page_table_stride;
   a.q = q_dev;
+  a.q_scale = q_scale_dev;
   a.k_cache = k_cache_dev;
   a.v_cache = v_cache_dev;
   a.k_scale = cfg->kv_dtype == LBP_KV_FP8_E4M3 ? k_scale_dev : nullptr;
@@ -281,7 +283,9 @@ static lbp_status attend_impl(const lbp_config* cfg, const lbp_plan_info* info,
   a.num_kv_heads = cfg->num_kv_heads;
   a.group = G;
   a.scale_log2 = cfg->sm_scale * 1.4426950408889634f;
-  if (launch_attend(a, cfg->kv_dtype, grid, static_cast<hipStream_t>(stream)) != hipSuccess)
+  const AttendKind kind = q_scale_dev ? kAttendFp8Q8
+                          : cfg->kv_dtype == LBP_KV_FP8_E4M3 ? kAttendFp8 : kAttendBf16;
+  if (launch_attend(a, kind, grid, static_cast<hipStream_t>(stream)) != hipSuccess)
     return LBP_ERR_HIP;
   return LBP_OK;
 }
@@ -365,6 +369,22 @@ lbp_status lbp_attend_traced(const lbp_config* cfg, const lbp_plan_info* info,
   if (!trace_dev) return LBP_ERR_INVALID_ARG;
   return attend_full(cfg, info, plan_ws_dev, q_dev, k_cache_dev, v_cache_dev, k_scale_dev,
                      v_scale_dev, split_ws_dev, split_ws_bytes, out_dev, trace_dev, false, stream);
+}
+
+lbp_status lbp_attend_fp8q(const lbp_config* cfg, const lbp_plan_info* info,
+                           const void* plan_ws_dev, const uint8_t* q_codes_dev,
+                           const float* q_scale_dev, const void* k_cache_dev,
+                           const void* v_cache_dev, const float* k_scale_dev,
+                           const float* v_scale_dev, void* split_ws_dev, size_t split_ws_bytes,
+                           void* out_dev, void* stream) {
+  if (!cfg) return LBP_ERR_INVALID_ARG;
+  if (cfg->kv_dtype != LBP_KV_FP8_E4M3) return LBP_ERR_UNSUPPORTED;
+  if (!q_scale_dev || !info) return LBP_ERR_INVALID_ARG;
+  lbp_status st = attend_impl(cfg, info, plan_ws_dev, q_codes_dev, k_cache_dev, v_cache_dev,
+                              k_scale_dev, v_scale_dev, split_ws_dev, split_ws_bytes, out_dev,
+                              nullptr, false, stream, q_scale_dev);
+  if (st != LBP_OK) return st;
+  return lbp_combine(cfg, info, plan_ws_dev, split_ws_dev, split_ws_bytes, out_dev, stream);
 }
 
 }  // extern "C"

@@ -89,7 +89,8 @@ struct AttendArgs {
   const int32_t* pair_first;
   const int32_t* page_table;
   int64_t page_table_stride;
-  const void* q;             // [B][Hq][128] bf16
+  const void* q;             // [B][Hq][128] bf16, or e4m3 codes with q_scale
+  const float* q_scale;      // [B][Hq] fp32 scale of FP8 queries, else null
   const void* k_cache;       // [P][H_kv][64][128] bf16 or e4m3
   const void* v_cache;
   const float* k_scale;      // [P][H_kv][64] (FP8 only)
@@ -119,7 +120,9 @@ struct CombineArgs {
 // Launchers (defined next to their kernels).  Each returns the HIP error of
 // the launch itself.
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
-hipError_t launch_attend(const AttendArgs& a, int kv_dtype, int grid, hipStream_t s);
+// Kernel instance: KV format and query precision.
+enum AttendKind { kAttendBf16 = 0, kAttendFp8 = 1, kAttendFp8Q8 = 2 };
+hipError_t launch_attend(const AttendArgs& a, AttendKind kind, int grid, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, int max_split, hipStream_t s);
 
 }  // namespace lbp

@@ -31,3 +31,9 @@ E4M3_TABLE = np.array([decode_code(c) for c in range(256)], dtype=np.float64)
 def decode(codes: np.ndarray) -> np.ndarray:
     """Decode an array of uint8 e4m3 codes to fp64."""
     return E4M3_TABLE[np.asarray(codes, dtype=np.uint8)]
+
+
+def dequantize(codes: np.ndarray, scale: np.ndarray) -> np.ndarray:
+    """Values of e4m3 codes with one scale per row of the last axis:
+    decode(codes) * scale[..., None], in fp64 (exact)."""
+    return decode(codes) * np.asarray(scale, dtype=np.float64)[..., None]

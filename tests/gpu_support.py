@@ -130,8 +130,11 @@ def expected_split_list(ref):
     return np.asarray(rows, dtype=np.int32).reshape(-1, 4)
 
 
-def oracle_pairs(case: Case, layer: int, pairs):
+def oracle_pairs(case: Case, layer: int, pairs, q64: Optional[np.ndarray] = None):
     """fp64 oracle output rows for (kv_head, request) pairs, from host copies.
+
+    q64, if given, replaces the layer's BF16 query ([B, Hq, 128] fp64, e.g.
+    the values of an FP8 query).
 
     The pages of each sampled request are gathered on the device into a
     compact cache (identity page table) before the host copy, so only the
@@ -148,7 +151,10 @@ def oracle_pairs(case: Case, layer: int, pairs):
         pages = case.page_table[r, :n].long()
         kc = Lyr.k_cache.index_select(0, pages)[:, g:g + 1].contiguous()
         vc = Lyr.v_cache.index_select(0, pages)[:, g:g + 1].contiguous()
-        q = oracle.attention.bf16_bits_to_f64(bits(Lyr.q[r:r + 1, g * G:(g + 1) * G]))
+        if q64 is None:
+            q = oracle.attention.bf16_bits_to_f64(bits(Lyr.q[r:r + 1, g * G:(g + 1) * G]))
+        else:
+            q = q64[r:r + 1, g * G:(g + 1) * G]
         table = np.arange(n, dtype=np.int32)[None]
         if fp8:
             ks = Lyr.k_scale.index_select(0, pages)[:, g:g + 1].contiguous().cpu().numpy()

@@ -27,7 +27,7 @@ def lib():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(lbp_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(lbp_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -194,6 +194,25 @@ def test_attend_guards(lib):
     assert attend(cfg(head_dim=256), info) == lbp.LBP_ERR_UNSUPPORTED
     st = lib.lbp_combine(ctypes.byref(c), ctypes.byref(bad), FAKE, FAKE, 1 << 34, FAKE, None)
     assert st == lbp.LBP_ERR_MISMATCH
+
+
+def test_fp8q_guards(lib):
+    c = cfg()
+    info = good_info(c)
+    args = (FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 34, FAKE, None)
+    assert lib.lbp_attend_fp8q(ctypes.byref(c), ctypes.byref(info), *args) == \
+        lbp.LBP_ERR_UNSUPPORTED                                   # BF16 KV
+    c8 = cfg(kv_dtype="fp8_e4m3")
+    i8 = good_info(c8)
+    no_scale = (FAKE, FAKE, None) + args[3:]
+    assert lib.lbp_attend_fp8q(ctypes.byref(c8), ctypes.byref(i8), *no_scale) == \
+        lbp.LBP_ERR_INVALID_ARG
+    no_kv_scale = args[:5] + (None, None) + args[7:]
+    assert lib.lbp_attend_fp8q(ctypes.byref(c8), ctypes.byref(i8), *no_kv_scale) == \
+        lbp.LBP_ERR_INVALID_ARG
+    bad = good_info(c8)
+    bad.magic = 0
+    assert lib.lbp_attend_fp8q(ctypes.byref(c8), ctypes.byref(bad), *args) == lbp.LBP_ERR_MISMATCH
 
 
 def test_plan_layout(lib):

@@ -6,19 +6,21 @@ arithmetic, so both the CPU oracle and the HIP path can consume its output
 without sharing any of the method's code.
 """
 
-from .configs import CONFIGS, WorkloadConfig, get_config
+from .configs import CONFIGS, TABLE3, WorkloadConfig, get_config
 from .gen import (
     draw_lengths,
     draw_page_table,
     make_layer,
     make_workload,
     poison_tail_slots,
+    quantize_query_e4m3,
     Workload,
     Layer,
 )
 
 __all__ = [
     "CONFIGS",
+    "TABLE3",
     "WorkloadConfig",
     "get_config",
     "draw_lengths",
@@ -26,6 +28,7 @@ __all__ = [
     "make_layer",
     "make_workload",
     "poison_tail_slots",
+    "quantize_query_e4m3",
     "Workload",
     "Layer",
 ]

@@ -72,8 +72,37 @@ CONFIGS = {
 }
 
 
+def _mix(*parts):
+    """Lengths of an A x B mix: `count` requests at KV length `length` per part."""
+    return tuple(length for count, length in parts for _ in range(count))
+
+
+K = 1024
+
+# The six FP8-KV length mixes of the vLLM x HPC-Ops page, Table 3 (decode
+# latency across KV-length distributions; "A x B" = A requests of KV length
+# B, K = 1024 tokens), at one GPU's tensor-parallel share of the Hy3 shape:
+# 8 query heads, 1 KV head.  The page does not state the head count; one KV
+# head is the share that makes its H20 timings possible (at 8 KV heads the
+# 1 x 128K + 31 x 4K mix would need more than twice the H20's bandwidth).
+TABLE3 = {
+    name: WorkloadConfig(name=f"t3-{name}", seed=10 + i, batch=len(lengths), num_q_heads=8,
+                         num_kv_heads=1, kv_dtype="fp8_e4m3", lengths_kind="fixed",
+                         fixed_lengths=lengths)
+    for i, (name, lengths) in enumerate([
+        ("64x0.5K", _mix((64, K // 2))),
+        ("64x4K", _mix((64, 4 * K))),
+        ("32x0.125K+32x4K", _mix((32, K // 8), (32, 4 * K))),
+        ("2x32K+30x4K", _mix((2, 32 * K), (30, 4 * K))),
+        ("1x64K+15x4K", _mix((1, 64 * K), (15, 4 * K))),
+        ("1x128K+31x4K", _mix((1, 128 * K), (31, 4 * K))),
+    ])
+}
+
+
 def get_config(name: str) -> WorkloadConfig:
-    try:
+    if name in CONFIGS:
         return CONFIGS[name]
-    except KeyError as e:
-        raise KeyError(f"unknown workload {name!r}; known: {sorted(CONFIGS)}") from e
+    if name in TABLE3:
+        return TABLE3[name]
+    raise KeyError(f"unknown workload {name!r}; known: {sorted(CONFIGS) + sorted(TABLE3)}")

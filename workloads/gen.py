@@ -14,6 +14,9 @@ Recipe (stated once here and relied on by tests and the benchmark):
   the target device: first ``q [B, Hq, D]`` bf16 ~ N(0, 1); then the caches
   page-chunk by page-chunk (``PAGE_CHUNK`` pages at a time), K before V in
   each chunk.  KV caches are ``[P, H_kv, 64, D]`` (page, head, slot, dim).
+* FP8 queries (``quantize_query_e4m3``) are derived from the BF16 ``q``:
+  per (request, query head) scale = max |q| / 448, codes = e4m3 RNE of
+  ``q / scale``.
 * FP8 caches: ``x ~ N(0, 1)`` fp32 and a scale ``s ~ U[lo, hi]`` per
   (page, head, slot); the stored code is the OCP e4m3 round-to-nearest-even
   of ``clamp(x / s, -448, 448)`` (torch's e4m3 cast does not saturate, so the
@@ -105,6 +108,17 @@ class Workload:
 def _fp8_codes(x: torch.Tensor, s: torch.Tensor) -> torch.Tensor:
     y = torch.clamp(x / s.unsqueeze(-1), -E4M3_MAX, E4M3_MAX)
     return y.to(torch.float8_e4m3fn).view(torch.uint8)
+
+
+def quantize_query_e4m3(q: torch.Tensor):
+    """An FP8 query in the form the fused attention prologue hands it over:
+    one fp32 scale per (request, query head) = max |q| over the head's dims
+    / 448 (1 for an all-zero row), codes = e4m3 RNE of q / scale.  Returns
+    (codes uint8 [B, Hq, D], scale fp32 [B, Hq]) on q's device."""
+    x = q.float()
+    amax = x.abs().amax(dim=-1)
+    scale = torch.where(amax > 0, amax / E4M3_MAX, torch.ones_like(amax))
+    return _fp8_codes(x, scale), scale
 
 
 def make_layer(*, batch: int, num_q_heads: int, num_kv_heads: int, num_pages: int,
