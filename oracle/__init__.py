@@ -29,4 +29,4 @@ brute force on tiny inputs, closed forms, invariants and library routines;
 none is marked "parity unpinned".
 """
 
-from . import assign, attention, e4m3  # noqa: F401
+from . import assign, attention, e4m3, prologue  # noqa: F401

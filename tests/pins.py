@@ -439,3 +439,97 @@ def pins_e4m3(mod):
     assert mod.decode(np.array([0x08]))[0] == 2.0 ** -6
     assert mod.decode(np.array([0x38]))[0] == 1.0
     assert mod.decode(np.array([0xB8]))[0] == -1.0
+
+
+# --------------------------------------------------------------------------
+# fused attention prologue
+# --------------------------------------------------------------------------
+
+def _brute_prologue(qkv, seq_lens, Hq, Hkv, qw, kw, eps, cos_sin):
+    """Per-element loops with the math module: RMSNorm, then rotate-half RoPE."""
+    B = len(qkv)
+    D = len(cos_sin[0])
+    h = D // 2
+    out = {"q": [], "k": [], "v": []}
+    for r in range(B):
+        p = max(0, min(int(seq_lens[r]) - 1, len(cos_sin) - 1))
+        for head in range(Hq + 2 * Hkv):
+            x = [float(qkv[r][head * D + i]) for i in range(D)]
+            if head >= Hq + Hkv:
+                out["v"].append(x)
+                continue
+            w = qw if head < Hq else kw
+            ms = sum(t * t for t in x) / D
+            y = [x[i] / math.sqrt(ms + eps) * float(w[i]) for i in range(D)]
+            z = [0.0] * D
+            for i in range(h):
+                c, s = float(cos_sin[p][i]), float(cos_sin[p][h + i])
+                z[i] = y[i] * c - y[h + i] * s
+                z[h + i] = y[h + i] * c + y[i] * s
+            out["q" if head < Hq else "k"].append(z)
+    return {k: np.array(v).reshape(B, -1, D) for k, v in out.items()}
+
+
+def pins_prologue(pro):
+    from transformers.models.llama.modeling_llama import apply_rotary_pos_emb
+    rng = np.random.default_rng(5)
+    # 1. RMSNorm is torch's rms_norm (fp64), eps inside the square root
+    x = rng.normal(size=(3, 5, 128)) * 3
+    w = 1 + 0.1 * rng.normal(size=128)
+    for eps in (1e-6, 0.5):
+        ref = torch.nn.functional.rms_norm(torch.from_numpy(x), (128,), torch.from_numpy(w),
+                                           eps).numpy()
+        assert np.allclose(pro.rms_norm(x, w, eps), ref, rtol=1e-12, atol=1e-12)
+    # 2. RoPE is the rotate-half convention of HF transformers' apply_rotary_pos_emb
+    theta = rng.uniform(-10, 10, size=(3, 64))
+    cos, sin = np.cos(theta), np.sin(theta)
+    q = rng.normal(size=(3, 4, 128))
+    c2 = torch.from_numpy(np.concatenate([cos, cos], -1))[:, None, :]
+    s2 = torch.from_numpy(np.concatenate([sin, sin], -1))[:, None, :]
+    qt = torch.from_numpy(q)[:, :, None, :]
+    ref, _ = apply_rotary_pos_emb(qt, qt, c2, s2, unsqueeze_dim=1)
+    got = pro.rope_rotate_half(q, cos[:, None, :], sin[:, None, :])
+    assert np.allclose(got, ref[:, :, 0].numpy(), rtol=1e-12, atol=1e-12)
+    # a quarter turn maps dim i onto dim i + 64; pair norms are kept
+    e0 = np.zeros((1, 128))
+    e0[0, 3] = 1.0
+    qt_ = pro.rope_rotate_half(e0, np.zeros((1, 64)), np.ones((1, 64)))
+    assert qt_[0, 67] == 1.0 and np.sum(np.abs(qt_)) == 1.0
+    pn = got[..., :64] ** 2 + got[..., 64:] ** 2
+    assert np.allclose(pn, q[..., :64] ** 2 + q[..., 64:] ** 2)
+    # 3. e4m3 rounding: torch's float8_e4m3fn cast (nearest, ties to even) in range
+    y = np.concatenate([rng.uniform(-448, 448, 20000), rng.normal(size=20000) * 0.01,
+                        [0.0, -0.0, 448.0, -448.0, 2.0 ** -10, -(2.0 ** -10), 3 * 2.0 ** -10]])
+    ref = torch.from_numpy(y.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(pro.e4m3_round(y.astype(np.float32).astype(np.float64)), ref)
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    from oracle.e4m3 import decode
+    assert np.array_equal(pro.e4m3_round(decode(finite)), finite)      # every code round-trips
+    # 4. row quantization: the row maximum maps to +-448 exactly; zero row -> scale 1, codes 0
+    rows = rng.normal(size=(6, 128))
+    rows[2] = 0
+    codes, scale, _ = pro.quantize_rows_e4m3(rows)
+    vals = decode(codes) * scale[:, None]
+    assert np.allclose(np.abs(vals).max(1)[[0, 1, 3, 4, 5]], np.abs(rows).max(1)[[0, 1, 3, 4, 5]],
+                       rtol=1e-15)
+    assert scale[2] == 1.0 and not np.any(codes[2] & 0x7F)
+    nz = [0, 1, 3, 4, 5]
+    assert np.all(np.abs(decode(codes[nz])).max(1) == 448.0)      # the full e4m3 range is used
+    assert np.all(np.abs(vals - rows) <= np.abs(rows) / 16 + scale[:, None] * 2.0 ** -9)
+    # 5. BF16 rounding: torch's fp32 -> bf16 cast (nearest, ties to even)
+    f = np.concatenate([rng.normal(size=5000).astype(np.float32),
+                        np.array([1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, -(1 + 2.0 ** -8)], np.float32)])
+    ref = torch.from_numpy(f).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(pro.bf16_round(f.astype(np.float64)), ref)
+    # 6. the whole step against per-element loops on a tiny case (D = 8)
+    D, Hq, Hkv = 8, 3, 1
+    cs_t = rng.uniform(-3, 3, size=(5, D // 2))
+    cos_sin = np.concatenate([np.cos(cs_t), np.sin(cs_t)], -1)
+    qkv = rng.normal(size=(4, (Hq + 2 * Hkv) * D))
+    L = [1, 3, 9, 0]                       # position 8 is past the table: its last row
+    qw, kw = rng.normal(size=D), rng.normal(size=D)
+    got = pro.prologue(qkv, L, Hq, Hkv, qw, kw, 1e-5, cos_sin)
+    ref = _brute_prologue(qkv, L, Hq, Hkv, qw, kw, 1e-5, cos_sin)
+    for key in ("q", "k", "v"):
+        assert np.allclose(got[key], ref[key], rtol=1e-12, atol=1e-12), key
+    assert list(got["pos"]) == [0, 2, 8, -1]

@@ -68,6 +68,20 @@ E4M3_MUTATIONS = [
 ]
 
 
+PROLOGUE_MUTATIONS = [
+    ("eps outside the root", "np.sqrt(ms + eps)", "(np.sqrt(ms) + eps)"),
+    ("sum for mean", "np.mean(x * x, axis=-1, keepdims=True)", "np.sum(x * x, axis=-1, keepdims=True)"),
+    ("rope sine sign", "a * cos - b * sin", "a * cos + b * sin"),
+    ("rope halves swapped", "[a * cos - b * sin, b * cos + a * sin]", "[b * cos + a * sin, a * cos - b * sin]"),
+    ("ties away from even", "(_POS_CODES[hi] % 2 == 0)", "True"),
+    ("scale max 240", "amax / E4M3_MAX", "amax / 240.0"),
+    ("negative zero lost", "np.signbit(y)", "(y < 0)"),
+    ("position is the length", "pos = np.where(L > 0, L - 1, -1)", "pos = np.where(L > 0, L, -1)"),
+    ("key normed with query weight", "rms_norm(k, k_norm_w, eps)", "rms_norm(k, q_norm_w, eps)"),
+    ("bf16 seven bits", "np.rint(np.ldexp(m, 8)), e - 8", "np.rint(np.ldexp(m, 7)), e - 7"),
+]
+
+
 @pytest.mark.parametrize("what,old,new", ASSIGN_MUTATIONS, ids=[m[0] for m in ASSIGN_MUTATIONS])
 def test_assign_mutant_is_caught(what, old, new):
     mut = load_mutant("assign", old, new)
@@ -88,3 +102,14 @@ def test_e4m3_mutant_is_caught(what, old, new):
     mut = load_mutant("e4m3", old, new)
     with pytest.raises(Exception):
         pins.pins_e4m3(mut)
+
+
+def test_prologue_pins_pass():
+    pins.pins_prologue(oracle.prologue)
+
+
+@pytest.mark.parametrize("what,old,new", PROLOGUE_MUTATIONS, ids=[m[0] for m in PROLOGUE_MUTATIONS])
+def test_prologue_mutant_is_caught(what, old, new):
+    mut = load_mutant("prologue", old, new)
+    with pytest.raises(Exception):
+        pins.pins_prologue(mut)
