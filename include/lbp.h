@@ -135,6 +135,31 @@ typedef struct lbp_plan_offsets {
       arrive, total;
 } lbp_plan_offsets;
 
+/* Arguments of lbp_prologue (all pointers are device pointers). */
+typedef struct lbp_prologue_args {
+  const void* qkv;             /* [batch][(Hq + 2 * H_kv) * 128] bf16: the fused QKV
+                                  projection of the new token, query heads, then key
+                                  heads, then value heads */
+  const int32_t* seq_lens;     /* [batch] lengths including the new token, which sits at
+                                  position seq_lens[r] - 1; <= 0: no token (row skipped) */
+  const int32_t* page_table;   /* [batch][page_table_stride], as for lbp_plan */
+  int64_t page_table_stride;   /* in int32 entries, >= cfg->max_pages_per_seq */
+  const float* q_norm_weight;  /* [128] QK-Norm weight of the query heads */
+  const float* k_norm_weight;  /* [128] QK-Norm weight of the key heads */
+  const float* rope_cos_sin;   /* [max_position][128] fp32: row p holds cos(p * f_i) for
+                                  the 64 rotation frequencies f_i, then sin(p * f_i) */
+  int32_t max_position;        /* rows of rope_cos_sin (>= 1); later positions use the last */
+  float norm_eps;              /* RMSNorm epsilon (>= 0) */
+  int32_t q_fp8;               /* 1: q_out receives e4m3 codes and q_scale_out one fp32
+                                  scale per (request, query head); 0: q_out is bf16 */
+  void* q_out;                 /* [batch][Hq][128] bf16 or uint8 */
+  float* q_scale_out;          /* [batch][Hq] (q_fp8 = 1 only) */
+  void* k_cache;               /* the paged caches of lbp_attend, in cfg->kv_dtype */
+  void* v_cache;
+  float* k_scale;              /* [num_pages][H_kv][64] (FP8 cache only) */
+  float* v_scale;
+} lbp_prologue_args;
+
 /* Human-readable name of a status code (static storage). */
 const char* lbp_status_string(lbp_status s);
 
@@ -250,6 +275,32 @@ lbp_status lbp_attend_fp8q(const lbp_config* cfg, const lbp_plan_info* info,
                            const void* v_cache_dev, const float* k_scale_dev,
                            const float* v_scale_dev, void* split_ws_dev, size_t split_ws_bytes,
                            void* out_dev, void* stream);
+
+/* The fused attention prologue of one decode step (SGLang x HPC-Ops page, "A
+ * fused attention prologue"; vLLM x HPC-Ops page, the HpcRopeNorm paragraph
+ * of the Attention backend section), one launch on `stream`.  For every
+ * request with a token, from its QKV projection:
+ *  - query and key heads: RMSNorm over the head's 128 dims
+ *    (x / sqrt(mean(x^2) + norm_eps) * weight), then RoPE that rotates each
+ *    dim pair (i, i + 64) by the angle of the token's position p =
+ *    seq_lens[r] - 1 (cos/sin from row min(p, max_position - 1) of
+ *    rope_cos_sin): (a, b) -> (a cos - b sin, b cos + a sin);
+ *  - the query goes to q_out: BF16 (nearest even), or with q_fp8 = 1 as e4m3
+ *    codes with q_scale_out = max|q| / 448 per (request, head) (1 for a zero
+ *    row), code = e4m3 nearest to q * 448 / max|q| — the input of
+ *    lbp_attend_fp8q;
+ *  - the normed, rotated key and the value are written into the paged cache
+ *    at page page_table[r][p / 64], slot p % 64, KV head h: BF16 (the value
+ *    unchanged), or for an FP8 cache e4m3 codes with k_scale / v_scale =
+ *    max|x| / 448 per (token, head).  Positions at or past
+ *    64 * cfg->max_pages_per_seq write nothing to the cache.
+ * Nothing else in the caches changes.  Host guards: a bad config, batch
+ * outside [1, cfg->max_batch], a missing pointer (q_scale_out with q_fp8,
+ * k_scale / v_scale with an FP8 cache), max_position < 1, a negative or
+ * non-finite norm_eps or a short page-table stride return an error and
+ * launch nothing. */
+lbp_status lbp_prologue(const lbp_config* cfg, int32_t batch, const lbp_prologue_args* args,
+                        void* stream);
 
 /* lbp_attend that also records, for every workgroup b of the attention
  * kernel, four uint64 at trace_dev[4b .. 4b+3]: its start and end on the

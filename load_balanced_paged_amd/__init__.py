@@ -38,7 +38,7 @@ PAGE_SIZE = 64
 EXPORTED_SYMBOLS = (
     "lbp_status_string", "lbp_version", "lbp_query_workspace", "lbp_plan", "lbp_plan_static",
     "lbp_plan_layout", "lbp_attend", "lbp_attend_fused", "lbp_attend_partials",
-    "lbp_attend_traced", "lbp_attend_fp8q",
+    "lbp_attend_traced", "lbp_attend_fp8q", "lbp_prologue",
     "lbp_combine",
 )
 
@@ -71,6 +71,27 @@ class lbp_plan_info(ctypes.Structure):
         ("plan_bytes", ctypes.c_uint64),
         ("page_table_dev", ctypes.c_void_p),
         ("page_table_stride", ctypes.c_int64),
+    ]
+
+
+class lbp_prologue_args(ctypes.Structure):
+    _fields_ = [
+        ("qkv", ctypes.c_void_p),
+        ("seq_lens", ctypes.c_void_p),
+        ("page_table", ctypes.c_void_p),
+        ("page_table_stride", ctypes.c_int64),
+        ("q_norm_weight", ctypes.c_void_p),
+        ("k_norm_weight", ctypes.c_void_p),
+        ("rope_cos_sin", ctypes.c_void_p),
+        ("max_position", ctypes.c_int32),
+        ("norm_eps", ctypes.c_float),
+        ("q_fp8", ctypes.c_int32),
+        ("q_out", ctypes.c_void_p),
+        ("q_scale_out", ctypes.c_void_p),
+        ("k_cache", ctypes.c_void_p),
+        ("v_cache", ctypes.c_void_p),
+        ("k_scale", ctypes.c_void_p),
+        ("v_scale", ctypes.c_void_p),
     ]
 
 
@@ -119,6 +140,7 @@ def load(path: str = LIB_PATH):
         "lbp_attend_partials": (I32, [cfgp, infop, P, P, P, P, P, P, P, SZ, P, P]),
         "lbp_attend_traced": (I32, [cfgp, infop, P, P, P, P, P, P, P, SZ, P, P, P]),
         "lbp_attend_fp8q": (I32, [cfgp, infop, P, P, P, P, P, P, P, P, SZ, P, P]),
+        "lbp_prologue": (I32, [cfgp, I32, ctypes.POINTER(lbp_prologue_args), P]),
         "lbp_combine": (I32, [cfgp, infop, P, P, SZ, P, P]),
     }
     for name, (res, args) in sig.items():
@@ -265,6 +287,35 @@ def lbp_attend_fp8q(cfg, info, plan_ws, q_codes, q_scale, k_cache, v_cache, k_sc
                                   split_ws.numel() * split_ws.element_size(),
                                   _ptr(out, "out", torch.bfloat16), _stream(stream)),
            "lbp_attend_fp8q")
+
+
+def lbp_prologue(cfg, qkv, seq_lens, page_table, q_norm_weight, k_norm_weight, rope_cos_sin,
+                 q_out, k_cache, v_cache, k_scale=None, v_scale=None, q_scale_out=None,
+                 norm_eps=1e-6, stream=None):
+    """Fused QK-Norm + RoPE + KV-cache write (+ FP8 query when q_scale_out is given)."""
+    import torch
+    fp8_kv = cfg.kv_dtype == LBP_KV_FP8_E4M3
+    kv_t = torch.uint8 if fp8_kv else torch.bfloat16
+    q_fp8 = q_scale_out is not None
+    a = lbp_prologue_args()
+    a.qkv = _ptr(qkv, "qkv", torch.bfloat16)
+    a.seq_lens = _ptr(seq_lens, "seq_lens", torch.int32)
+    a.page_table = _ptr(page_table, "page_table", torch.int32)
+    a.page_table_stride = int(page_table.shape[1])
+    a.q_norm_weight = _ptr(q_norm_weight, "q_norm_weight", torch.float32)
+    a.k_norm_weight = _ptr(k_norm_weight, "k_norm_weight", torch.float32)
+    a.rope_cos_sin = _ptr(rope_cos_sin, "rope_cos_sin", torch.float32)
+    a.max_position = int(rope_cos_sin.shape[0])
+    a.norm_eps = float(norm_eps)
+    a.q_fp8 = int(q_fp8)
+    a.q_out = _ptr(q_out, "q_out", torch.uint8 if q_fp8 else torch.bfloat16)
+    a.q_scale_out = _ptr(q_scale_out, "q_scale_out", torch.float32, optional=True)
+    a.k_cache = _ptr(k_cache, "k_cache", kv_t)
+    a.v_cache = _ptr(v_cache, "v_cache", kv_t)
+    a.k_scale = _ptr(k_scale, "k_scale", torch.float32, optional=not fp8_kv)
+    a.v_scale = _ptr(v_scale, "v_scale", torch.float32, optional=not fp8_kv)
+    _check(load().lbp_prologue(ctypes.byref(cfg), int(seq_lens.numel()), ctypes.byref(a),
+                               _stream(stream)), "lbp_prologue")
 
 
 def lbp_attend_partials(cfg, info, plan_ws, q, k_cache, v_cache, k_scale, v_scale, split_ws,

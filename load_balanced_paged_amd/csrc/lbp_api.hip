@@ -387,4 +387,46 @@ lbp_status lbp_attend_fp8q(const lbp_config* cfg, const lbp_plan_info* info,
   return lbp_combine(cfg, info, plan_ws_dev, split_ws_dev, split_ws_bytes, out_dev, stream);
 }
 
+lbp_status lbp_prologue(const lbp_config* cfg, int32_t batch, const lbp_prologue_args* args,
+                        void* stream) {
+  lbp_status st = check_config(cfg);
+  if (st != LBP_OK) return st;
+  if (!args || batch < 1 || batch > cfg->max_batch) return LBP_ERR_INVALID_ARG;
+  const lbp_prologue_args& p = *args;
+  const bool kv_fp8 = cfg->kv_dtype == LBP_KV_FP8_E4M3;
+  if (!p.qkv || !p.seq_lens || !p.page_table || !p.q_norm_weight || !p.k_norm_weight ||
+      !p.rope_cos_sin || !p.q_out || !p.k_cache || !p.v_cache)
+    return LBP_ERR_INVALID_ARG;
+  if (p.q_fp8 != 0 && p.q_fp8 != 1) return LBP_ERR_INVALID_ARG;
+  if (p.q_fp8 && !p.q_scale_out) return LBP_ERR_INVALID_ARG;
+  if (kv_fp8 && (!p.k_scale || !p.v_scale)) return LBP_ERR_INVALID_ARG;
+  if (p.max_position < 1 || !(p.norm_eps >= 0.f) || !isfinite(p.norm_eps))
+    return LBP_ERR_INVALID_ARG;
+  if (p.page_table_stride < cfg->max_pages_per_seq) return LBP_ERR_INVALID_ARG;
+  PrologueArgs a;
+  a.qkv = p.qkv;
+  a.seq_lens = p.seq_lens;
+  a.page_table = p.page_table;
+  a.page_table_stride = p.page_table_stride;
+  a.q_norm_weight = p.q_norm_weight;
+  a.k_norm_weight = p.k_norm_weight;
+  a.rope_cos_sin = p.rope_cos_sin;
+  a.max_position = p.max_position;
+  a.norm_eps = p.norm_eps;
+  a.q_fp8 = p.q_fp8;
+  a.kv_fp8 = kv_fp8;
+  a.q_out = p.q_out;
+  a.q_scale_out = p.q_scale_out;
+  a.k_cache = p.k_cache;
+  a.v_cache = p.v_cache;
+  a.k_scale = kv_fp8 ? p.k_scale : nullptr;
+  a.v_scale = kv_fp8 ? p.v_scale : nullptr;
+  a.batch = batch;
+  a.num_q_heads = cfg->num_q_heads;
+  a.num_kv_heads = cfg->num_kv_heads;
+  a.max_tokens = cfg->max_pages_per_seq * kPageTokens;
+  if (launch_prologue(a, static_cast<hipStream_t>(stream)) != hipSuccess) return LBP_ERR_HIP;
+  return LBP_OK;
+}
+
 }  // extern "C"

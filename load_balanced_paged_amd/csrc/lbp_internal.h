@@ -117,6 +117,27 @@ struct CombineArgs {
   int32_t batch, num_q_heads, num_kv_heads, group;
 };
 
+struct PrologueArgs {
+  const void* qkv;           // [B][(Hq + 2 Hkv) * 128] bf16
+  const int32_t* seq_lens;
+  const int32_t* page_table;
+  int64_t page_table_stride;
+  const float* q_norm_weight;
+  const float* k_norm_weight;
+  const float* rope_cos_sin; // [max_position][128]
+  int32_t max_position;
+  float norm_eps;
+  int32_t q_fp8, kv_fp8;
+  void* q_out;
+  float* q_scale_out;
+  void* k_cache;
+  void* v_cache;
+  float* k_scale;
+  float* v_scale;
+  int32_t batch, num_q_heads, num_kv_heads;
+  int32_t max_tokens;        // 64 * max_pages_per_seq
+};
+
 // Launchers (defined next to their kernels).  Each returns the HIP error of
 // the launch itself.
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
@@ -124,5 +145,6 @@ hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
 enum AttendKind { kAttendBf16 = 0, kAttendFp8 = 1, kAttendFp8Q8 = 2 };
 hipError_t launch_attend(const AttendArgs& a, AttendKind kind, int grid, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, int max_split, hipStream_t s);
+hipError_t launch_prologue(const PrologueArgs& a, hipStream_t s);
 
 }  // namespace lbp

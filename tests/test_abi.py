@@ -54,6 +54,8 @@ int main(void) {
   printf("%zu %zu %zu %zu\\n", sizeof(lbp_plan_info), offsetof(lbp_plan_info, plan_bytes),
          offsetof(lbp_plan_info, page_table_dev), offsetof(lbp_plan_info, page_table_stride));
   printf("%zu\\n", sizeof(lbp_plan_offsets));
+  printf("%zu %zu %zu %zu\\n", sizeof(lbp_prologue_args), offsetof(lbp_prologue_args, max_position),
+         offsetof(lbp_prologue_args, q_out), offsetof(lbp_prologue_args, v_scale));
   return 0;
 }
 ''')
@@ -70,6 +72,9 @@ int main(void) {
                  lbp.lbp_plan_info.page_table_dev.offset,
                  lbp.lbp_plan_info.page_table_stride.offset]
     assert c == ctypes.sizeof(lbp.lbp_plan_offsets)
+    d = [int(x) for x in lines[3].split()]
+    P = lbp.lbp_prologue_args
+    assert d == [ctypes.sizeof(P), P.max_position.offset, P.q_out.offset, P.v_scale.offset]
 
 
 def cfg(**kw):
@@ -244,3 +249,40 @@ def test_binding_rejects_host_tensors(lib):
     with pytest.raises(ValueError):
         lbp.lbp_plan(c, torch.zeros(4, dtype=torch.int32), torch.zeros(4, 1024, dtype=torch.int32),
                      torch.zeros(1 << 20, dtype=torch.uint8))
+
+
+def prologue_args(**kw):
+    a = lbp.lbp_prologue_args()
+    for f, _ in lbp.lbp_prologue_args._fields_:
+        setattr(a, f, FAKE.value if f not in ("page_table_stride", "max_position", "norm_eps",
+                                              "q_fp8") else 0)
+    a.page_table_stride = 1024
+    a.max_position = 4096
+    a.norm_eps = 1e-6
+    a.q_fp8 = 0
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_prologue_guards(lib):
+    c = cfg()
+
+    def st(args, batch=4, config=c):
+        return lib.lbp_prologue(ctypes.byref(config), batch, ctypes.byref(args), None)
+    assert st(prologue_args(), batch=0) == lbp.LBP_ERR_INVALID_ARG
+    assert st(prologue_args(), batch=65) == lbp.LBP_ERR_INVALID_ARG
+    for f in ("qkv", "seq_lens", "page_table", "q_norm_weight", "k_norm_weight", "rope_cos_sin",
+              "q_out", "k_cache", "v_cache"):
+        assert st(prologue_args(**{f: None})) == lbp.LBP_ERR_INVALID_ARG, f
+    assert st(prologue_args(q_fp8=1, q_scale_out=None)) == lbp.LBP_ERR_INVALID_ARG
+    assert st(prologue_args(q_fp8=2)) == lbp.LBP_ERR_INVALID_ARG
+    assert st(prologue_args(max_position=0)) == lbp.LBP_ERR_INVALID_ARG
+    assert st(prologue_args(norm_eps=-1.0)) == lbp.LBP_ERR_INVALID_ARG
+    assert st(prologue_args(norm_eps=float("inf"))) == lbp.LBP_ERR_INVALID_ARG
+    assert st(prologue_args(page_table_stride=1000)) == lbp.LBP_ERR_INVALID_ARG
+    c8 = cfg(kv_dtype="fp8_e4m3")
+    assert st(prologue_args(k_scale=None), config=c8) == lbp.LBP_ERR_INVALID_ARG
+    assert st(prologue_args(v_scale=None), config=c8) == lbp.LBP_ERR_INVALID_ARG
+    assert st(prologue_args(), config=cfg(head_dim=64)) == lbp.LBP_ERR_UNSUPPORTED
+    assert lib.lbp_prologue(ctypes.byref(c), 4, None, None) == lbp.LBP_ERR_INVALID_ARG

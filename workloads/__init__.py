@@ -14,6 +14,8 @@ from .gen import (
     make_workload,
     poison_tail_slots,
     quantize_query_e4m3,
+    rope_cos_sin_table,
+    make_prologue_inputs,
     Workload,
     Layer,
 )
@@ -29,6 +31,8 @@ __all__ = [
     "make_workload",
     "poison_tail_slots",
     "quantize_query_e4m3",
+    "rope_cos_sin_table",
+    "make_prologue_inputs",
     "Workload",
     "Layer",
 ]

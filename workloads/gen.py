@@ -121,6 +121,32 @@ def quantize_query_e4m3(q: torch.Tensor):
     return _fp8_codes(x, scale), scale
 
 
+def rope_cos_sin_table(max_position: int, head_dim: int = 128, theta: float = 1.0e6,
+                       device="cpu") -> torch.Tensor:
+    """The caller-side RoPE table the prologue reads: row p holds cos(p * f_i)
+    for the head_dim / 2 frequencies f_i = theta^(-2i / head_dim), then
+    sin(p * f_i); computed in fp64 and stored as fp32."""
+    h = head_dim // 2
+    f = theta ** (-2.0 * np.arange(h) / head_dim)
+    ang = np.arange(max_position, dtype=np.float64)[:, None] * f[None, :]
+    tab = np.concatenate([np.cos(ang), np.sin(ang)], axis=1).astype(np.float32)
+    return torch.from_numpy(tab).to(device)
+
+
+def make_prologue_inputs(batch: int, num_q_heads: int, num_kv_heads: int, seed: int,
+                         device="cpu", head_dim: int = 128):
+    """Seeded inputs of the fused prologue: the QKV projection of one token per
+    request (bf16 ~ N(0, 1) * 2, query heads then key then value heads) and the
+    two QK-Norm weight vectors (fp32 ~ 1 + 0.1 N(0, 1))."""
+    g = torch.Generator(device=torch.device(device))
+    g.manual_seed(7000 + seed)
+    H3 = num_q_heads + 2 * num_kv_heads
+    qkv = (2 * torch.randn((batch, H3 * head_dim), generator=g, device=device)).to(torch.bfloat16)
+    qw = 1 + 0.1 * torch.randn(head_dim, generator=g, device=device)
+    kw = 1 + 0.1 * torch.randn(head_dim, generator=g, device=device)
+    return qkv, qw, kw
+
+
 def make_layer(*, batch: int, num_q_heads: int, num_kv_heads: int, num_pages: int,
                kv_dtype: str, seed: int, layer: int, device="cpu", head_dim: int = 128,
                page_size: int = 64, fp8_scale_lo: float = 0.01,
