@@ -214,6 +214,61 @@ class Bench:
         ts = np.array([e0.elapsed_time(e1) for e0, e1 in evs]) * 1e3
         return float(ts.mean()), float(np.median(ts)), float(ts.min()), float(ts.max())
 
+    def time_prologue(self, steps):
+        """lbp_prologue for the workload's batch (one new token per request into
+        layer 0's cache), HIP-graph timed; FP8 query and cache for FP8 KV."""
+        import ctypes
+        from workloads import make_prologue_inputs, rope_cos_sin_table
+        lbp = self.lbp
+        lib = lbp.load()
+        w = self.wcfg
+        B, Hq, Hkv = w.batch, w.num_q_heads, w.num_kv_heads
+        fp8 = w.kv_dtype == "fp8_e4m3"
+        qkv, qw, kw = make_prologue_inputs(B, Hq, Hkv, w.seed, device="cuda")
+        cs = rope_cos_sin_table(int(max(self.wl.lengths)), device="cuda")
+        L = self.wl.layers[0]
+        q_out = torch.empty((B, Hq, 128), dtype=torch.uint8 if fp8 else torch.bfloat16,
+                            device="cuda")
+        q_scale = torch.empty((B, Hq), dtype=torch.float32, device="cuda") if fp8 else None
+        a = lbp.lbp_prologue_args()
+        P = lambda t: t.data_ptr() if t is not None else None   # noqa: E731
+        a.qkv, a.seq_lens, a.page_table = P(qkv), P(self.seq), P(self.table)
+        a.page_table_stride = int(self.table.shape[1])
+        a.q_norm_weight, a.k_norm_weight, a.rope_cos_sin = P(qw), P(kw), P(cs)
+        a.max_position, a.norm_eps, a.q_fp8 = int(cs.shape[0]), 1e-6, int(fp8)
+        a.q_out, a.q_scale_out = P(q_out), P(q_scale)
+        a.k_cache, a.v_cache, a.k_scale, a.v_scale = (P(L.k_cache), P(L.v_cache), P(L.k_scale),
+                                                      P(L.v_scale))
+        cfgp, ap = ctypes.byref(self.cfg), ctypes.byref(a)
+
+        def launch(stream):
+            st = lib.lbp_prologue(cfgp, B, ap, ctypes.c_void_p(stream))
+            if st != 0:
+                raise RuntimeError(f"lbp_prologue: {lbp.status_name(st)}")
+        for _ in range(3):
+            launch(torch.cuda.current_stream().cuda_stream)
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                for _ in range(steps):
+                    launch(s.cuda_stream)
+        torch.cuda.current_stream().wait_stream(s)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / steps
+        out_row = 128 + 4 if fp8 else 256           # one head row out (codes + scale, or bf16)
+        nbytes = (B * (Hq + 2 * Hkv) * 256 + B * 512     # QKV in, one cos/sin row per request
+                  + B * Hq * out_row + B * 2 * Hkv * out_row)
+        return {"us": round(us, 2), "bytes": nbytes, "gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
+                "query": "e4m3 + scale" if fp8 else "bf16"}
+
     def time_plan(self, reps=20):
         lbp = self.lbp
         info, plan_ws, _ = self.plan()
@@ -341,6 +396,7 @@ def bench_one(name, lbp, args, headline):
     res["attend_kernel_us"] = {"mean": round(k_mean, 2), "median": round(k_med, 2),
                                "min": round(k_min, 2), "max": round(k_max, 2)}
     res["plan_us"] = round(b.time_plan(), 2)
+    res["prologue"] = b.time_prologue(min(args.steps, 100))
     res["amortized_us_per_layer"] = round((res["plan_us"] + b.layers * us) / b.layers, 2)
     if not args.no_static:
         W = info.num_bins
@@ -491,7 +547,7 @@ def main():
         "amortized_us_per_layer": head["amortized_us_per_layer"],
         "attend_kernel_us": head["attend_kernel_us"],
     }
-    for k in ("fused_us_per_step", "fp8q_us_per_step"):
+    for k in ("fused_us_per_step", "fp8q_us_per_step", "prologue"):
         if k in head:
             out[k] = head[k]
     if "static_splits" in head:
