@@ -118,6 +118,30 @@ def paged_decode_attention(q, k_cache, v_cache, page_table, seq_lens, num_kv_hea
     return out, lse
 
 
+def paged_verify_attention(q, k_cache, v_cache, page_table, seq_lens, num_kv_heads: int,
+                           sm_scale: float, kv_dtype: str = "bf16", k_scale=None,
+                           v_scale=None, pairs=None):
+    """Multi-token decode (speculative verification): out [B, T, Hq, D] and
+    lse [B, T, Hq] for T query tokens per request.
+
+    ``q`` is float64 [B, T, Hq, D].  Token j of request r sits at position
+    L_r - T + j and attends causally to the KV positions up to and including
+    its own, i.e. to the first max(0, L_r - T + j + 1) tokens of the request
+    (no position: zeros and lse -inf).  T = 1 is plain decode.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    B, T, Hq, D = q.shape
+    L = np.asarray(seq_lens, dtype=np.int64)
+    out = np.full((B, T, Hq, D), np.nan)
+    lse = np.full((B, T, Hq), np.nan)
+    for j in range(T):
+        visible = np.clip(L - T + j + 1, 0, L)
+        out[:, j], lse[:, j] = paged_decode_attention(q[:, j], k_cache, v_cache, page_table,
+                                                      visible, num_kv_heads, sm_scale, kv_dtype,
+                                                      k_scale, v_scale, pairs)
+    return out, lse
+
+
 def split_decode_attention(q, k_cache, v_cache, page_table, seq_lens, num_kv_heads: int,
                            sm_scale: float, desc, kv_dtype: str = "bf16", k_scale=None,
                            v_scale=None):

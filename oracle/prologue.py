@@ -17,8 +17,9 @@ pages are silent:
 * RoPE rotates dim pairs (i, i + 64) ("rotate half") by the angles of the
   token's position, taken from a caller-supplied table whose row p holds
   cos(p * f_i) for i < 64 followed by sin(p * f_i).
-* The new token of request r sits at position seq_lens[r] - 1 (the lengths
-  already count it); positions past the table use its last row.
+* The T new tokens of request r (T = 1 for plain decode) sit at positions
+  seq_lens[r] - T + j (the lengths already count them); negative positions
+  have no token; positions past the table use its last row.
 * FP8 outputs (the query; K and V in an FP8 cache) use one scale per
   (token, head) = max |x| / 448 (1 for an all-zero row); the code is the
   e4m3 value nearest to x / scale, ties to even.
@@ -98,29 +99,36 @@ def bf16_round(x: np.ndarray) -> np.ndarray:
 
 def prologue(qkv: np.ndarray, seq_lens, num_q_heads: int, num_kv_heads: int,
              q_norm_w: np.ndarray, k_norm_w: np.ndarray, eps: float, cos_sin: np.ndarray):
-    """The exact (unrounded) outputs of the prologue for one decode token per
-    request.
+    """The exact (unrounded) outputs of the prologue for the new tokens of one
+    step.
 
-    qkv: [B, (Hq + 2 Hkv) * D] values (query heads, then key heads, then
-    value heads); cos_sin: [max_position, D] (cos of the D/2 frequencies,
-    then their sin).  Returns dict with
-      q [B, Hq, D] (normed and rotated), k [B, Hkv, D] (normed and rotated),
-      v [B, Hkv, D], pos [B] (position used, -1 for a request without a
-      token).
+    qkv: [B, (Hq + 2 Hkv) * D] (one new token per request) or
+    [B, T, (Hq + 2 Hkv) * D] (T new tokens, token j of request r at position
+    seq_lens[r] - T + j): query heads, then key heads, then value heads.
+    cos_sin: [max_position, D] (cos of the D/2 frequencies, then their sin).
+    Returns dict with q [..., Hq, D] and k [..., Hkv, D] (normed and
+    rotated), v [..., Hkv, D], and pos (the position used; negative: no
+    token), where ... is [B] or [B, T] like qkv.
     """
     qkv = np.asarray(qkv, dtype=np.float64)
-    B = qkv.shape[0]
+    single = qkv.ndim == 2
+    if single:
+        qkv = qkv[:, None, :]
+    B, T = qkv.shape[:2]
     D = cos_sin.shape[1]
     H3 = num_q_heads + 2 * num_kv_heads
-    x = qkv.reshape(B, H3, D)
-    q = x[:, :num_q_heads]
-    k = x[:, num_q_heads:num_q_heads + num_kv_heads]
-    v = x[:, num_q_heads + num_kv_heads:]
+    x = qkv.reshape(B, T, H3, D)
+    q = x[:, :, :num_q_heads]
+    k = x[:, :, num_q_heads:num_q_heads + num_kv_heads]
+    v = x[:, :, num_q_heads + num_kv_heads:]
     L = np.asarray(seq_lens, dtype=np.int64)
-    pos = np.where(L > 0, L - 1, -1)
+    pos = L[:, None] - T + np.arange(T)[None, :]          # [B, T]
     row = np.clip(pos, 0, cos_sin.shape[0] - 1)
-    cos = cos_sin[row, :D // 2][:, None, :]
-    sin = cos_sin[row, D // 2:][:, None, :]
+    cos = cos_sin[row, :D // 2][:, :, None, :]
+    sin = cos_sin[row, D // 2:][:, :, None, :]
     qn = rope_rotate_half(rms_norm(q, q_norm_w, eps), cos, sin)
     kn = rope_rotate_half(rms_norm(k, k_norm_w, eps), cos, sin)
-    return {"q": qn, "k": kn, "v": v.copy(), "pos": pos}
+    out = {"q": qn, "k": kn, "v": v.copy(), "pos": np.where(pos >= 0, pos, -1)}
+    if single:
+        out = {key: val[:, 0] for key, val in out.items()}
+    return out

@@ -533,3 +533,51 @@ def pins_prologue(pro):
     for key in ("q", "k", "v"):
         assert np.allclose(got[key], ref[key], rtol=1e-12, atol=1e-12), key
     assert list(got["pos"]) == [0, 2, 8, -1]
+    # T = 3 new tokens per request at positions L - 3 + j
+    qkv3 = rng.normal(size=(4, 3, (Hq + 2 * Hkv) * D))
+    got3 = pro.prologue(qkv3, L, Hq, Hkv, qw, kw, 1e-5, cos_sin)
+    for j in range(3):
+        Lj = [x - 3 + j + 1 for x in L]        # a table row lookup at Lj - 1 = L - 3 + j
+        ref = _brute_prologue(qkv3[:, j], Lj, Hq, Hkv, qw, kw, 1e-5, cos_sin)
+        for key in ("q", "k", "v"):
+            ok = np.array([x - 3 + j >= 0 for x in L])
+            assert np.allclose(got3[key][ok, j], ref[key][ok], rtol=1e-12, atol=1e-12), (key, j)
+    assert got3["pos"].tolist() == [[-1, -1, 0], [0, 1, 2], [6, 7, 8], [-1, -1, -1]]
+
+
+# --------------------------------------------------------------------------
+# multi-token verification (causal attention of T query tokens per request)
+# --------------------------------------------------------------------------
+
+def pins_verify(att):
+    """Against torch's fp64 SDPA with an explicit causal mask over unpaged rows."""
+    H, G, D, T = 2, 3, 16, 4
+    lengths = [1, 3, 4, 70, 129, 200]
+    q1, Klog, Vlog, kc, vc, table = make_tiny_paged(21, lengths, H, G, D)
+    g = torch.Generator().manual_seed(22)
+    qb = to_bf16_bits(torch.randn(len(lengths), T, H * G, D, generator=g))
+    q = att.bf16_bits_to_f64(qb)
+    sm = 1.0 / math.sqrt(D)
+    out, lse = att.paged_verify_attention(q, kc, vc, table, lengths, H, sm)
+    for r, L in enumerate(lengths):
+        for h in range(H):
+            K = att.bf16_bits_to_f64(np.asarray(Klog[r][h]))
+            V = att.bf16_bits_to_f64(np.asarray(Vlog[r][h]))
+            qr = q[r, :, h * G:(h + 1) * G]                        # [T, G, D]
+            qt = torch.from_numpy(np.ascontiguousarray(qr.transpose(1, 0, 2)))[None]   # [1,G,T,D]
+            kt = torch.from_numpy(K)[None, None].expand(1, G, -1, -1).contiguous()
+            vt = torch.from_numpy(V)[None, None].expand(1, G, -1, -1).contiguous()
+            pos = np.arange(T)[:, None] + L - T                    # query positions
+            mask = torch.from_numpy(np.arange(L)[None, :] <= pos)  # [T, L]
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                qt, kt, vt, attn_mask=mask, scale=sm)[0].numpy().transpose(1, 0, 2)
+            for j in range(T):
+                got = out[r, j, h * G:(h + 1) * G]
+                if L - T + j < 0:                                  # no visible position
+                    assert np.all(got == 0) and np.all(np.isneginf(lse[r, j, h * G:(h + 1) * G]))
+                else:
+                    assert rel_err(got, ref[j]) < 1e-12, (r, h, j)
+    # one query token is plain decode
+    o1, l1 = att.paged_verify_attention(q[:, :1], kc, vc, table, lengths, H, sm)
+    o0, l0 = att.paged_decode_attention(q[:, 0], kc, vc, table, lengths, H, sm)
+    assert np.array_equal(o1[:, 0], o0) and np.array_equal(l1[:, 0], l0)

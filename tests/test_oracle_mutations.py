@@ -68,6 +68,12 @@ E4M3_MUTATIONS = [
 ]
 
 
+VERIFY_MUTATIONS = [
+    ("causal limit off by one", "visible = np.clip(L - T + j + 1, 0, L)", "visible = np.clip(L - T + j, 0, L)"),
+    ("tokens in reverse order", "visible = np.clip(L - T + j + 1, 0, L)", "visible = np.clip(L - j, 0, L)"),
+    ("no causal limit", "visible = np.clip(L - T + j + 1, 0, L)", "visible = L"),
+]
+
 PROLOGUE_MUTATIONS = [
     ("eps outside the root", "np.sqrt(ms + eps)", "(np.sqrt(ms) + eps)"),
     ("sum for mean", "np.mean(x * x, axis=-1, keepdims=True)", "np.sum(x * x, axis=-1, keepdims=True)"),
@@ -76,7 +82,8 @@ PROLOGUE_MUTATIONS = [
     ("ties away from even", "(_POS_CODES[hi] % 2 == 0)", "True"),
     ("scale max 240", "amax / E4M3_MAX", "amax / 240.0"),
     ("negative zero lost", "np.signbit(y)", "(y < 0)"),
-    ("position is the length", "pos = np.where(L > 0, L - 1, -1)", "pos = np.where(L > 0, L, -1)"),
+    ("position is the length", "pos = L[:, None] - T + np.arange(T)[None, :]", "pos = L[:, None] - T + 1 + np.arange(T)[None, :]"),
+    ("tokens in reverse", "pos = L[:, None] - T + np.arange(T)[None, :]", "pos = L[:, None] - 1 - np.arange(T)[None, :]"),
     ("key normed with query weight", "rms_norm(k, k_norm_w, eps)", "rms_norm(k, q_norm_w, eps)"),
     ("bf16 seven bits", "np.rint(np.ldexp(m, 8)), e - 8", "np.rint(np.ldexp(m, 7)), e - 7"),
 ]
@@ -113,3 +120,14 @@ def test_prologue_mutant_is_caught(what, old, new):
     mut = load_mutant("prologue", old, new)
     with pytest.raises(Exception):
         pins.pins_prologue(mut)
+
+
+def test_verify_pins_pass():
+    pins.pins_verify(oracle.attention)
+
+
+@pytest.mark.parametrize("what,old,new", VERIFY_MUTATIONS, ids=[m[0] for m in VERIFY_MUTATIONS])
+def test_verify_mutant_is_caught(what, old, new):
+    mut = load_mutant("attention", old, new)
+    with pytest.raises(Exception):
+        pins.pins_verify(mut)
