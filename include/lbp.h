@@ -26,8 +26,9 @@
  *    call.  No C++ exception crosses this interface.
  *
  * Fixed data layouts (all contiguous, row-major):
- *  - q        [batch][num_q_heads][128]                 bf16
- *  - out      [batch][num_q_heads][128]                 bf16
+ *  - q        [batch][q_len][num_q_heads][128]          bf16
+ *  - out      [batch][q_len][num_q_heads][128]          bf16
+ *             (q_len = cfg->q_len, 1 for plain decode)
  *  - k_cache, v_cache [num_pages][num_kv_heads][64][128] bf16, or uint8
  *             OCP e4m3 codes for LBP_KV_FP8_E4M3 (page, KV head, slot, dim)
  *  - k_scale, v_scale [num_pages][num_kv_heads][64]     fp32 (FP8 only);
@@ -47,7 +48,7 @@
 extern "C" {
 #endif
 
-#define LBP_VERSION 1
+#define LBP_VERSION 2
 #define LBP_HEAD_DIM 128
 #define LBP_PAGE_SIZE 64
 #define LBP_MAX_GROUP 16
@@ -56,7 +57,7 @@ extern "C" {
 typedef enum lbp_status {
   LBP_OK = 0,
   LBP_ERR_INVALID_ARG = 1,         /* NULL pointer, non-positive size, ... */
-  LBP_ERR_UNSUPPORTED = 2,         /* head_dim != 128, page != 64, group > 16 */
+  LBP_ERR_UNSUPPORTED = 2,         /* head_dim != 128, page != 64, group * q_len > 16 */
   LBP_ERR_WORKSPACE_TOO_SMALL = 3, /* a caller workspace is below the query */
   LBP_ERR_MISMATCH = 4,            /* plan info does not match the config */
   LBP_ERR_HIP = 5                  /* the HIP runtime refused a launch/query */
@@ -88,6 +89,11 @@ typedef struct lbp_config {
   int32_t min_tiles_per_bin; /* F, the minimum-work floor in tiles; 0 = 4 */
   int32_t kv_dtype;          /* lbp_kv_dtype */
   float sm_scale;            /* softmax scale, > 0 (1/sqrt(128) typically) */
+  int32_t q_len;             /* query tokens per request per step (0 = 1): > 1 for
+                                speculative verification, where token j of request r
+                                sits at position L_r - q_len + j and attends causally
+                                to KV positions <= its own; requires
+                                (Hq / H_kv) * q_len <= 16 */
 } lbp_config;
 
 /* Host-side record of a built plan, filled by lbp_plan / lbp_plan_static and
@@ -137,11 +143,12 @@ typedef struct lbp_plan_offsets {
 
 /* Arguments of lbp_prologue (all pointers are device pointers). */
 typedef struct lbp_prologue_args {
-  const void* qkv;             /* [batch][(Hq + 2 * H_kv) * 128] bf16: the fused QKV
-                                  projection of the new token, query heads, then key
-                                  heads, then value heads */
-  const int32_t* seq_lens;     /* [batch] lengths including the new token, which sits at
-                                  position seq_lens[r] - 1; <= 0: no token (row skipped) */
+  const void* qkv;             /* [batch][q_len][(Hq + 2 * H_kv) * 128] bf16: the fused
+                                  QKV projection of the new tokens, query heads, then key
+                                  heads, then value heads (q_len = cfg->q_len, 1 for
+                                  plain decode) */
+  const int32_t* seq_lens;     /* [batch] lengths including the new tokens; token j sits at
+                                  position seq_lens[r] - q_len + j (< 0: skipped) */
   const int32_t* page_table;   /* [batch][page_table_stride], as for lbp_plan */
   int64_t page_table_stride;   /* in int32 entries, >= cfg->max_pages_per_seq */
   const float* q_norm_weight;  /* [128] QK-Norm weight of the query heads */
@@ -152,8 +159,8 @@ typedef struct lbp_prologue_args {
   float norm_eps;              /* RMSNorm epsilon (>= 0) */
   int32_t q_fp8;               /* 1: q_out receives e4m3 codes and q_scale_out one fp32
                                   scale per (request, query head); 0: q_out is bf16 */
-  void* q_out;                 /* [batch][Hq][128] bf16 or uint8 */
-  float* q_scale_out;          /* [batch][Hq] (q_fp8 = 1 only) */
+  void* q_out;                 /* [batch][q_len][Hq][128] bf16 or uint8 */
+  float* q_scale_out;          /* [batch][q_len][Hq] (q_fp8 = 1 only) */
   void* k_cache;               /* the paged caches of lbp_attend, in cfg->kv_dtype */
   void* v_cache;
   float* k_scale;              /* [num_pages][H_kv][64] (FP8 cache only) */
@@ -168,7 +175,8 @@ int32_t lbp_version(void);
 
 /* Workspace sizes a (config, policy, param) needs at batch = max_batch.
  * plan_bytes: the task map; split_bytes: the partial-output buffer
- * (max_desc x G x 128 fp32 plus max_desc x G fp32 log-sum-exp).  Host only;
+ * (max_desc x C x 128 fp32 plus max_desc x C fp32 log-sum-exp, with
+ * C = G * q_len query rows per KV head).  Host only;
  * may query the current device's CU count when num_workgroups == 0. */
 lbp_status lbp_query_workspace(const lbp_config* cfg, int32_t policy, int32_t param,
                                size_t* plan_bytes, size_t* split_bytes);
@@ -247,10 +255,12 @@ lbp_status lbp_attend_fused(const lbp_config* cfg, const lbp_plan_info* info,
  * place (its BF16 output is written to out_dev), every descriptor of a pair
  * split over several bins writes its partial to the split buffer, and a
  * pair with no tokens gets zero rows.  lbp_combine merges the split pairs
- * (the plan's split_list) into out_dev.  Split-buffer layout:
- * o_part[max_desc][G][128] fp32 (normalised partial outputs) at offset 0,
- * then lse_part[max_desc][G] fp32 (base-2 log-sum-exp of the
- * sm_scale*log2(e)-scaled scores) at offset align256(max_desc*G*128*4). */
+ * (the plan's split_list) into out_dev.  Split-buffer layout, with
+ * C = G * q_len columns per descriptor (column c = query token c / G, head
+ * c % G of the KV head's group): o_part[max_desc][C][128] fp32 (normalised
+ * partial outputs) at offset 0, then lse_part[max_desc][C] fp32 (base-2
+ * log-sum-exp of the sm_scale*log2(e)-scaled scores; -inf for a column with
+ * no visible token in the descriptor) at offset align256(max_desc*C*128*4). */
 lbp_status lbp_attend_partials(const lbp_config* cfg, const lbp_plan_info* info,
                                const void* plan_ws_dev, const void* q_dev,
                                const void* k_cache_dev, const void* v_cache_dev,
@@ -263,8 +273,9 @@ lbp_status lbp_attend_partials(const lbp_config* cfg, const lbp_plan_info* info,
  * attention prologue", has the prologue emit Q in FP8 with a per-token,
  * per-head scale and hand both to the attention kernel without
  * requantization; this entry point takes them in that form:
- *  - q_codes_dev [batch][num_q_heads][128] uint8 OCP e4m3 codes,
- *  - q_scale_dev [batch][num_q_heads] fp32; query element = e4m3(code) * scale.
+ *  - q_codes_dev [batch][q_len][num_q_heads][128] uint8 OCP e4m3 codes,
+ *  - q_scale_dev [batch][q_len][num_q_heads] fp32; query element =
+ *    e4m3(code) * scale.
  * Scores are computed from the K and Q codes on the fp8 MFMA with fp32
  * accumulation, then scaled by q_scale * k_scale * sm_scale; everything else
  * (plan, split buffer, combine, output) is as for lbp_attend.
@@ -278,13 +289,14 @@ lbp_status lbp_attend_fp8q(const lbp_config* cfg, const lbp_plan_info* info,
 
 /* The fused attention prologue of one decode step (SGLang x HPC-Ops page, "A
  * fused attention prologue"; vLLM x HPC-Ops page, the HpcRopeNorm paragraph
- * of the Attention backend section), one launch on `stream`.  For every
- * request with a token, from its QKV projection:
+ * of the Attention backend section), one launch on `stream`.  For every new
+ * token (q_len per request; token j of request r at position
+ * p = seq_lens[r] - q_len + j, skipped if p < 0), from its QKV projection:
  *  - query and key heads: RMSNorm over the head's 128 dims
  *    (x / sqrt(mean(x^2) + norm_eps) * weight), then RoPE that rotates each
- *    dim pair (i, i + 64) by the angle of the token's position p =
- *    seq_lens[r] - 1 (cos/sin from row min(p, max_position - 1) of
- *    rope_cos_sin): (a, b) -> (a cos - b sin, b cos + a sin);
+ *    dim pair (i, i + 64) by the angle of the token's position p (cos/sin
+ *    from row min(p, max_position - 1) of rope_cos_sin):
+ *    (a, b) -> (a cos - b sin, b cos + a sin);
  *  - the query goes to q_out: BF16 (nearest even), or with q_fp8 = 1 as e4m3
  *    codes with q_scale_out = max|q| / 448 per (request, head) (1 for a zero
  *    row), code = e4m3 nearest to q * 448 / max|q| — the input of

@@ -55,6 +55,7 @@ class lbp_config(ctypes.Structure):
         ("min_tiles_per_bin", ctypes.c_int32),
         ("kv_dtype", ctypes.c_int32),
         ("sm_scale", ctypes.c_float),
+        ("q_len", ctypes.c_int32),
     ]
 
 
@@ -188,11 +189,11 @@ def _check(status, what):
 
 def make_config(num_q_heads, num_kv_heads, max_batch, max_pages_per_seq, kv_dtype="bf16",
                 num_workgroups=0, min_tiles_per_bin=0, sm_scale=None, head_dim=HEAD_DIM,
-                page_size=PAGE_SIZE) -> lbp_config:
+                page_size=PAGE_SIZE, q_len=1) -> lbp_config:
     dt = {"bf16": LBP_KV_BF16, "fp8_e4m3": LBP_KV_FP8_E4M3}.get(kv_dtype, kv_dtype)
     return lbp_config(num_q_heads, num_kv_heads, head_dim, page_size, max_batch,
                       max_pages_per_seq, num_workgroups, min_tiles_per_bin, int(dt),
-                      float(sm_scale if sm_scale is not None else head_dim ** -0.5))
+                      float(sm_scale if sm_scale is not None else head_dim ** -0.5), int(q_len))
 
 
 # ---------------------------------------------------------------------------

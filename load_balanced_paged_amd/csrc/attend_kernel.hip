@@ -70,6 +70,9 @@ namespace {
 #ifndef LBP_FP8_WAVES
 #define LBP_FP8_WAVES 12
 #endif
+#ifndef LBP_BF16_SPLIT_P
+#define LBP_BF16_SPLIT_P 1
+#endif
 #ifndef LBP_FP8Q_WAVES
 #define LBP_FP8Q_WAVES 12
 #endif
@@ -130,23 +133,52 @@ struct SliceRsrc {
   rsrc_t k, v, ks, vs;
 };
 
-// BF16 query group of KV head g for request r as the MFMA B operand, in the
-// dim order of format Kv (clipped to the group's G rows: other heads read 0).
+// Query rows of the MFMA columns: column c is query token c / G, head c % G
+// of KV head g's group, at row (r * q_len + c / G) * Hq + g * G + c % G.
+// The lane's row relative to column 0's, and the span of rows the buffer
+// resource covers, depend only on the launch, so they are computed once per
+// kernel (the division stays out of the descriptor loop, where it would
+// delay the query loads behind the KV loads).  Columns past G * q_len get a
+// row past the resource's end and read zeros.  With one query token (the
+// non-causal instance) the row is the column itself, which keeps the query
+// offsets equal to the K row offsets of the same lanes.
+struct QLane {
+  int row;    // this lane's row relative to column 0's, or past `rows` (reads 0)
+  int rows;   // rows the resource spans
+};
+template <bool kMultiToken>
+__device__ inline QLane q_lane(const AttendArgs& a, int n) {
+  QLane q;
+  if constexpr (kMultiToken) {
+    q.rows = (a.q_len - 1) * a.num_q_heads + a.group;
+    q.row = n < a.ncols ? (n / a.group) * a.num_q_heads + n % a.group : q.rows;
+  } else {
+    q.rows = a.group;
+    q.row = n;
+  }
+  return q;
+}
+__device__ inline int64_t q_base_row(const AttendArgs& a, int g, int r) {
+  return int64_t(r) * a.q_len * a.num_q_heads + int64_t(g) * a.group;
+}
+
+// BF16 query columns as the MFMA B operand, in the dim order of format Kv.
 template <class Kv>
-__device__ inline void load_q_bf16(bf16x8_t* qb, const AttendArgs& a, int g, int r, int n,
-                                   int grp) {
-  const rsrc_t qr = make_rsrc(static_cast<const char*>(a.q) +
-                                  (int64_t(r) * a.num_q_heads + int64_t(g) * a.group) * kHeadDim * 2,
-                              a.group * kHeadDim * 2);
+__device__ inline void load_q_bf16(bf16x8_t* qb, const AttendArgs& a, const QLane& ql, int g,
+                                   int r, int grp) {
+  const rsrc_t qr = make_rsrc(static_cast<const char*>(a.q) + q_base_row(a, g, r) * kHeadDim * 2,
+                              ql.rows * kHeadDim * 2);
 #pragma unroll
   for (int s = 0; s < 4; ++s)
     qb[s] = __builtin_bit_cast(
-        bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(qr, Kv::q_offset(n, grp, s), 0, 0));
+        bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(
+                      qr, ql.row * kHeadDim * 2 + Kv::q_offset(0, grp, s), 0, 0));
 }
 
 struct Bf16Kv {
   static constexpr int kRowBytes = kHeadDim * 2;
   static constexpr bool kScaled = false;
+  static constexpr bool kSplitP = LBP_BF16_SPLIT_P;   // P.V with P as BF16 hi + lo
   static constexpr int kWaves = LBP_BF16_WAVES;    // waves per workgroup
   struct Buf {
     i32x4_t k[4];   // K A-operand, one per 32-dim k-step
@@ -157,8 +189,9 @@ struct Bf16Kv {
   struct Q {
     bf16x8_t v[4];
   };
-  __device__ static void load_q(Q& q, const AttendArgs& a, int g, int r, int n, int grp) {
-    load_q_bf16<Bf16Kv>(q.v, a, g, r, n, grp);
+  __device__ static void load_q(Q& q, const AttendArgs& a, const QLane& ql, int g, int r,
+                                int grp) {
+    load_q_bf16<Bf16Kv>(q.v, a, ql, g, r, grp);
   }
   __device__ static float score_scale(const Q&, float scale_log2) { return scale_log2; }
 
@@ -203,6 +236,9 @@ struct Bf16Kv {
 struct Fp8Kv {
   static constexpr int kRowBytes = kHeadDim;
   static constexpr bool kScaled = true;
+  // the FP8 tolerance leaves room for P in plain BF16, and this format needs
+  // its issue slots for the code widening
+  static constexpr bool kSplitP = false;
   // FP8 moves half the bytes per token for the same MFMA and softmax work, so
   // it needs more waves in flight per CU (three per SIMD) to stay on HBM.
   static constexpr int kWaves = LBP_FP8_WAVES;
@@ -217,8 +253,9 @@ struct Fp8Kv {
   struct Q {
     bf16x8_t v[4];
   };
-  __device__ static void load_q(Q& q, const AttendArgs& a, int g, int r, int n, int grp) {
-    load_q_bf16<Fp8Kv>(q.v, a, g, r, n, grp);
+  __device__ static void load_q(Q& q, const AttendArgs& a, const QLane& ql, int g, int r,
+                                int grp) {
+    load_q_bf16<Fp8Kv>(q.v, a, ql, g, r, grp);
   }
   __device__ static float score_scale(const Q&, float scale_log2) { return scale_log2; }
 
@@ -284,15 +321,17 @@ struct Fp8KvQ8 : Fp8Kv {
     i32x4_t c[2];   // codes of dims [32grp, 32grp + 32) of head n
     float scale;    // the head's Q scale (0 for columns past the group)
   };
-  __device__ static void load_q(Q& q, const AttendArgs& a, int g, int r, int n, int grp) {
-    const int64_t row0 = int64_t(r) * a.num_q_heads + int64_t(g) * a.group;
-    const rsrc_t qr = make_rsrc(static_cast<const char*>(a.q) + row0 * kHeadDim,
-                                a.group * kHeadDim);
-    const rsrc_t sr = make_rsrc(a.q_scale + row0, a.group * 4);
+  __device__ static void load_q(Q& q, const AttendArgs& a, const QLane& ql, int g, int r,
+                                int grp) {
+    const int64_t base = q_base_row(a, g, r);
+    const rsrc_t qr = make_rsrc(static_cast<const char*>(a.q) + base * kHeadDim,
+                                ql.rows * kHeadDim);
+    const rsrc_t sr = make_rsrc(a.q_scale + base, ql.rows * 4);
 #pragma unroll
     for (int h = 0; h < 2; ++h)
-      q.c[h] = __builtin_amdgcn_raw_buffer_load_b128(qr, n * kHeadDim + 32 * grp + 16 * h, 0, 0);
-    q.scale = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sr, 4 * n, 0, 0));
+      q.c[h] = __builtin_amdgcn_raw_buffer_load_b128(qr, ql.row * kHeadDim + 32 * grp + 16 * h,
+                                                     0, 0);
+    q.scale = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sr, 4 * ql.row, 0, 0));
   }
   __device__ static float score_scale(const Q& q, float scale_log2) { return q.scale * scale_log2; }
 
@@ -348,35 +387,65 @@ struct WaveState {
   f32x4_t acc[8];   // O^T blocks: lane (grp, n) holds dims 32grp + 8j + mb
 };
 
-template <class Kv>
+// lim: this lane's column sees tokens < lim (its causal limit in
+// multi-token verification, kCausal only).  A column with no visible token
+// so far keeps an empty state (m = -inf, l = 0, acc = 0).
+template <class Kv, bool kCausal>
 __device__ inline void consume(WaveState& st, const typename Kv::Buf& b, const typename Kv::Q& q,
-                               int tok, int e, float scale_log2, int grp) {
+                               int tok, int e, float scale_log2, int grp, int lim) {
   f32x4_t s = Kv::scores(b, q);
   f32x4_t ks = Kv::k_scales(b);
   f32x4_t vs = Kv::v_scales(b);
   float x[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j)
-    x[j] = (tok + 4 * grp + j < e) ? s[j] * ks[j] * scale_log2 : -INFINITY;
+    x[j] = (tok + 4 * grp + j < (kCausal ? min(e, lim) : e)) ? s[j] * ks[j] * scale_log2
+                                                             : -INFINITY;
   float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
   mx = wave_max_across_groups(mx);
   const float m_new = fmaxf(st.m, mx);
-  const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
+  // without a causal limit every slice has a visible token in every column,
+  // so the running max is finite after the first one
+  const float ref = kCausal ? finite_or_zero(m_new) : m_new;
+  const float alpha = __builtin_amdgcn_exp2f(st.m - ref);
   st.m = m_new;
   st.l *= alpha;
 #pragma unroll
   for (int mb = 0; mb < 8; ++mb) st.acc[mb] *= alpha;
   float p[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) p[j] = __builtin_amdgcn_exp2f(x[j] - st.m);
+  for (int j = 0; j < 4; ++j) p[j] = __builtin_amdgcn_exp2f(x[j] - ref);
   st.l += (p[0] + p[1]) + (p[2] + p[3]);
-  i32x2_t pb2 = {int(pack_bf16(p[0] * vs[0], p[1] * vs[1])),
-                 int(pack_bf16(p[2] * vs[2], p[3] * vs[3]))};
-  const i16x4_t pb = __builtin_bit_cast(i16x4_t, pb2);
+  if constexpr (Kv::kSplitP) {
+    const float pv[4] = {p[0] * vs[0], p[1] * vs[1], p[2] * vs[2], p[3] * vs[3]};
+    i32x2_t pb2 = {int(pack_bf16(pv[0], pv[1])), int(pack_bf16(pv[2], pv[3]))};
+    const i16x4_t pb = __builtin_bit_cast(i16x4_t, pb2);
+    // P as a BF16 pair hi + lo (lo = the rounding residual of hi): the P.V
+    // product then carries P to ~2^-17 instead of BF16's 2^-9, at the cost
+    // of a second MFMA per output block, of which this HBM-bound kernel has
+    // plenty to spare
+    const uint32_t h01 = uint32_t(pb2[0]), h23 = uint32_t(pb2[1]);
+    const float r0 = pv[0] - __builtin_bit_cast(float, h01 << 16);
+    const float r1 = pv[1] - __builtin_bit_cast(float, h01 & 0xFFFF0000u);
+    const float r2 = pv[2] - __builtin_bit_cast(float, h23 << 16);
+    const float r3 = pv[3] - __builtin_bit_cast(float, h23 & 0xFFFF0000u);
+    i32x2_t lo2 = {int(pack_bf16(r0, r1)), int(pack_bf16(r2, r3))};
+    const i16x4_t pl = __builtin_bit_cast(i16x4_t, lo2);
 #pragma unroll
-  for (int mb = 0; mb < 8; ++mb)
-    st.acc[mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(Kv::v_operand(b, mb), pb, st.acc[mb],
-                                                            0, 0, 0);
+    for (int mb = 0; mb < 8; ++mb) {
+      const i16x4_t vop = Kv::v_operand(b, mb);
+      st.acc[mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop, pb, st.acc[mb], 0, 0, 0);
+      st.acc[mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop, pl, st.acc[mb], 0, 0, 0);
+    }
+  } else {
+    i32x2_t pb2 = {int(pack_bf16(p[0] * vs[0], p[1] * vs[1])),
+                   int(pack_bf16(p[2] * vs[2], p[3] * vs[3]))};
+    const i16x4_t pb = __builtin_bit_cast(i16x4_t, pb2);
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb)
+      st.acc[mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(Kv::v_operand(b, mb), pb,
+                                                              st.acc[mb], 0, 0, 0);
+  }
 }
 
 // Drains one bin: every descriptor in it, in order.
@@ -387,21 +456,23 @@ __device__ inline void consume(WaveState& st, const typename Kv::Buf& b, const t
 // d + 1 and d + 1's query group, before the cross-wave merge of d, so their
 // latency overlaps the merge and the wait for the slowest wave instead of
 // following them.
-template <class Kv>
+template <class Kv, bool kCausal>
 __device__ inline void attend_bin(const AttendArgs& a, const int32_t* __restrict__ pt,
                                   const int4* __restrict__ descs,
                                   const int32_t* __restrict__ pair_count,
                                   const int32_t* __restrict__ bin_offset,
-                                  const int4* __restrict__ bin_first, float* smem, int bin) {
+                                  const int4* __restrict__ bin_first,
+                                  const int32_t* __restrict__ pair_first, float* smem, int bin) {
   constexpr int kWaves = Kv::kWaves;
   constexpr int kThreads = kWaves * 64;
   constexpr int step = kWaves * kSlice;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int n = lane & 15;         // query head within the group (MFMA column)
+  const int n = lane & 15;         // MFMA column: query token n / G, head n % G
   const int grp = lane >> 4;
   const int G = a.group;
-  const int red_stride = 32 + G * kRedRow;
+  const int C = a.ncols;           // G * q_len <= 16
+  const int red_stride = 32 + C * kRedRow;
   float* red = smem + wave * red_stride;
   // range and first descriptor are independent loads: one round trip
   const int d_begin = bin_offset[bin];
@@ -410,16 +481,26 @@ __device__ inline void attend_bin(const AttendArgs& a, const int32_t* __restrict
   asm volatile("" ::"s"(ds.x), "s"(ds.y), "s"(ds.z), "s"(ds.w));   // keep the load above the exit
   if (d_begin >= d_end) return;
 
+  const QLane ql = q_lane<kCausal>(a, n);
   typename Kv::Q qb;
   typename Kv::Buf buf[2];
-  Kv::load_q(qb, a, ds.x, ds.y, n, grp);
+  Kv::load_q(qb, a, ql, ds.x, ds.y, grp);
   Kv::issue(buf[0], slice_rsrc<Kv>(a, pt, ds.x, ds.y, ds.z + wave * kSlice, ds.w), lane);
 
   for (int d = d_begin; d < d_end; ++d) {
     const int g = ds.x, r = ds.y, t_begin = ds.z, t_end = ds.w;
-    const bool single = pair_count[g * a.batch + r] == 1;
+    const int p = g * a.batch + r;
+    const bool single = pair_count[p] == 1;
     const bool has_next = d + 1 < d_end;
     const int4 dn = descs[has_next ? d + 1 : d];
+    // causal limit of this lane's column in multi-token verification: query
+    // token j of the request sits at position L - q_len + j, L being the
+    // end of the pair's last descriptor
+    int lim = INT_MAX;
+    if constexpr (kCausal) {
+      const int L = descs[pair_first[p] + pair_count[p] - 1].w;
+      lim = L - a.q_len + 1 + n / G;
+    }
 
     WaveState st;
     st.m = -INFINITY;
@@ -435,7 +516,8 @@ __device__ inline void attend_bin(const AttendArgs& a, const int32_t* __restrict
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         Kv::issue(buf[u ^ 1], slice_rsrc<Kv>(a, pt, g, r, tok + step, t_end), lane);
-        consume<Kv>(st, buf[u], qb, tok, t_end, Kv::score_scale(qb, a.scale_log2), grp);
+        consume<Kv, kCausal>(st, buf[u], qb, tok, t_end, Kv::score_scale(qb, a.scale_log2), grp,
+                             lim);
         tok += step;
         if (tok >= t_end) {
           more = false;
@@ -444,13 +526,16 @@ __device__ inline void attend_bin(const AttendArgs& a, const int32_t* __restrict
       }
     }
     if (has_next) {
+      // the query first: as the older load it is complete whenever the
+      // slice's first K row is, so the next descriptor's loop can wait for
+      // its loads one by one
+      Kv::load_q(qb, a, ql, dn.x, dn.y, grp);
       Kv::issue(buf[0], slice_rsrc<Kv>(a, pt, dn.x, dn.y, dn.z + wave * kSlice, dn.w), lane);
-      Kv::load_q(qb, a, dn.x, dn.y, n, grp);
     }
 
     // merge the wave states of this descriptor
     st.l = wave_sum_across_groups(st.l);
-    if (n < G) {
+    if (n < C) {
       if (grp == 0) {
         red[n] = st.m;
         red[16 + n] = st.l;
@@ -465,33 +550,39 @@ __device__ inline void attend_bin(const AttendArgs& a, const int32_t* __restrict
       }
     }
     __syncthreads();
-    for (int idx = threadIdx.x; idx < G * kHeadDim; idx += kThreads) {
+    for (int idx = threadIdx.x; idx < C * kHeadDim; idx += kThreads) {
       const int q = idx >> 7, dim = idx & (kHeadDim - 1);
       float M = -INFINITY;
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) M = fmaxf(M, smem[w * red_stride + q]);
+      // a column with no visible token in this descriptor (possible only
+      // under a causal limit) gives an empty partial: o = 0, lse = -inf
+      const float Mu = kCausal ? finite_or_zero(M) : M;
       float L = 0.f, o = 0.f;
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) {
         const float* rw = smem + w * red_stride;
-        const float c = __builtin_amdgcn_exp2f(rw[q] - M);
+        const float c = __builtin_amdgcn_exp2f(rw[q] - Mu);
         L += rw[16 + q] * c;
         o += rw[32 + q * kRedRow + dim] * c;
       }
+      const bool empty = kCausal && !(L > 0.f);
+      const float on = empty ? 0.f : o / L;
       if (single) {
         // the pair's only descriptor: this is already the final output
-        const int64_t row = int64_t(r) * a.num_q_heads + int64_t(g) * G + q;
-        static_cast<__bf16*>(a.out)[row * kHeadDim + dim] = static_cast<__bf16>(o / L);
+        const int64_t row = kCausal ? query_row(r, g, q, a.q_len, G, a.num_q_heads)
+                                    : int64_t(r) * a.num_q_heads + int64_t(g) * G + q;
+        static_cast<__bf16*>(a.out)[row * kHeadDim + dim] = static_cast<__bf16>(on);
       } else {
-        float* po = a.o_part + (int64_t(d) * G + q) * kHeadDim + dim;
-        float* pl = a.lse_part + int64_t(d) * G + q;
-        const float lse = M + __builtin_amdgcn_logf(L);
+        float* po = a.o_part + (int64_t(d) * C + q) * kHeadDim + dim;
+        float* pl = a.lse_part + int64_t(d) * C + q;
+        const float lse = empty ? -INFINITY : M + __builtin_amdgcn_logf(L);
         if (a.fuse) {
           // merged inside this launch, possibly by a workgroup on another XCD
-          store_coherent(po, o / L);
+          store_coherent(po, on);
           if (dim == 0) store_coherent(pl, lse);
         } else {
-          *po = o / L;
+          *po = on;
           if (dim == 0) *pl = lse;
         }
       }
@@ -523,19 +614,20 @@ constexpr int merge_lds_floats(int threads) { return 64 + (threads / 32) * kHead
 // Merges the n partials in slots slot0, slot0 + stride, ... (in that order)
 // of pair (g, r).  dst < 0: the result is the pair's final output (BF16 to
 // `out`); otherwise it is written back as a partial (row and log-sum-exp)
-// to slot dst.  Thread t owns float4 column t % 32 of head (t / 32) % G and
-// partials i = row group (mod R), R = threads / (32 G); the R states are
+// to slot dst.  Thread t owns float4 column t % 32 of query column
+// (t / 32) % C and partials i = row group (mod R), R = threads / (32 C),
+// C = G * q_len <= 16; the R states are
 // merged through LDS in a fixed order, so the result is bitwise
 // reproducible.
 template <int kThreads>
 __device__ void merge_run(const AttendArgs& a, float* smem, int slot0, int stride, int n, int dst,
                           int g, int r) {
-  const int G = a.group;
-  const int R = kThreads / (32 * G);
+  const int C = a.ncols;       // columns: query token q / G, head q % G
+  const int R = kThreads / (32 * C);
   const int t = threadIdx.x;
   const int c4 = t & 31;
-  const int q = (t >> 5) % G;
-  const int rg = (t >> 5) / G;
+  const int q = (t >> 5) % C;
+  const int rg = (t >> 5) / C;
   float m = -INFINITY, l = 0.f;
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
   if (rg < R) {
@@ -546,7 +638,7 @@ __device__ void merge_run(const AttendArgs& a, float* smem, int slot0, int strid
       for (int u = 0; u < kMergeUnroll; ++u) {
         const int i = i0 + u * R;
         if (i < n) {
-          const int64_t e = int64_t(slot0 + i * stride) * G + q;
+          const int64_t e = int64_t(slot0 + i * stride) * C + q;
           const float* row = a.o_part + e * kHeadDim + 4 * c4;
           ls[u] = load_coherent(a.lse_part + e);
           v[u] = f32x4_t{load_coherent(row), load_coherent(row + 1), load_coherent(row + 2),
@@ -558,11 +650,11 @@ __device__ void merge_run(const AttendArgs& a, float* smem, int slot0, int strid
         if (i0 + u * R < n) merge_into(m, l, acc, ls[u], v[u]);
     }
   }
-  float* red_m = smem;         // [R * G] (R * G <= threads / 32 <= 32)
+  float* red_m = smem;         // [R * C] (R * C <= threads / 32 <= 32)
   float* red_l = smem + 32;
-  f32x4_t* red_o = reinterpret_cast<f32x4_t*>(smem + 64);   // [R * G][32]
+  f32x4_t* red_o = reinterpret_cast<f32x4_t*>(smem + 64);   // [R * C][32]
   if (rg < R) {
-    const int s = rg * G + q;
+    const int s = rg * C + q;
     if (c4 == 0) {
       red_m[s] = m;
       red_l[s] = l;
@@ -572,23 +664,25 @@ __device__ void merge_run(const AttendArgs& a, float* smem, int slot0, int strid
   __syncthreads();
   if (rg == 0) {
     float M = -INFINITY;
-    for (int k = 0; k < R; ++k) M = fmaxf(M, red_m[k * G + q]);
+    for (int k = 0; k < R; ++k) M = fmaxf(M, red_m[k * C + q]);
+    const float Mu = finite_or_zero(M);
     float L = 0.f;
     f32x4_t tot = {0.f, 0.f, 0.f, 0.f};
     for (int k = 0; k < R; ++k) {
-      const float c = __builtin_amdgcn_exp2f(red_m[k * G + q] - M);   // 0 for an empty state
-      L += red_l[k * G + q] * c;
-      tot += red_o[(k * G + q) * 32 + c4] * c;
+      const float c = __builtin_amdgcn_exp2f(red_m[k * C + q] - Mu);   // 0 for an empty state
+      L += red_l[k * C + q] * c;
+      tot += red_o[(k * C + q) * 32 + c4] * c;
     }
+    const bool empty = !(L > 0.f);   // no visible token in any merged partial
+    const f32x4_t o = empty ? f32x4_t{0.f, 0.f, 0.f, 0.f} : tot / L;
     if (dst < 0) {
-      store_bf16x4(a.out, int64_t(r) * a.num_q_heads + int64_t(g) * G + q, c4, tot / L);
+      store_bf16x4(a.out, query_row(r, g, q, a.q_len, a.group, a.num_q_heads), c4, o);
     } else {
-      const int64_t e = int64_t(dst) * G + q;
-      const f32x4_t o = tot / L;
+      const int64_t e = int64_t(dst) * C + q;
       float* row = a.o_part + e * kHeadDim + 4 * c4;
 #pragma unroll
       for (int j = 0; j < 4; ++j) store_coherent(row + j, o[j]);
-      if (c4 == 0) store_coherent(a.lse_part + e, M + __builtin_amdgcn_logf(L));
+      if (c4 == 0) store_coherent(a.lse_part + e, empty ? -INFINITY : M + __builtin_amdgcn_logf(L));
     }
   }
   __syncthreads();
@@ -662,7 +756,7 @@ __device__ void finish_split_pairs(const AttendArgs& a, const int4* __restrict__
 // on a faster CU simply drains more bins; every workgroup draws exactly one
 // ticket past the last bin, and the one holding the final ticket returns the
 // counter to zero for the next launch.
-template <class Kv>
+template <class Kv, bool kCausal>
 __global__ __launch_bounds__(Kv::kWaves * 64) void attend_kernel(
     AttendArgs a, const int32_t* __restrict__ page_table, const int4* __restrict__ descs,
     const int32_t* __restrict__ pair_count, const int32_t* __restrict__ bin_offset,
@@ -686,7 +780,8 @@ __global__ __launch_bounds__(Kv::kWaves * 64) void attend_kernel(
   };
   int bin = a.grab_counter ? next_bin() : int(blockIdx.x);
   while (bin < a.num_bins) {
-    attend_bin<Kv>(a, page_table, descs, pair_count, bin_offset, bin_first, smem, bin);
+    attend_bin<Kv, kCausal>(a, page_table, descs, pair_count, bin_offset, bin_first, pair_first,
+                            smem, bin);
     const int d_begin = bin_offset[bin], d_end = bin_offset[bin + 1];
     if (a.fuse)
       finish_split_pairs<kThreads>(a, descs, pair_count, pair_first, smem, &arrive_lds, d_begin,
@@ -701,11 +796,13 @@ __global__ __launch_bounds__(Kv::kWaves * 64) void attend_kernel(
   for (int p = blockIdx.x; p < npairs; p += gridDim.x) {
     if (pair_count[p] != 0) continue;
     const int g = p / a.batch, r = p % a.batch;
-    uint4* rows = reinterpret_cast<uint4*>(static_cast<char*>(a.out) +
-                                           (int64_t(r) * a.num_q_heads + int64_t(g) * a.group) *
-                                               kHeadDim * 2);
-    for (int i = threadIdx.x; i < a.group * kHeadDim * 2 / 16; i += kThreads)
-      rows[i] = make_uint4(0, 0, 0, 0);
+    for (int j = 0; j < a.q_len; ++j) {   // the group's rows of every query token
+      uint4* rows = reinterpret_cast<uint4*>(
+          static_cast<char*>(a.out) +
+          query_row(r, g, j * a.group, a.q_len, a.group, a.num_q_heads) * kHeadDim * 2);
+      for (int i = threadIdx.x; i < a.group * kHeadDim * 2 / 16; i += kThreads)
+        rows[i] = make_uint4(0, 0, 0, 0);
+    }
   }
 
   if (a.trace && threadIdx.x == 0) {
@@ -732,22 +829,28 @@ hipError_t launch_attend(const AttendArgs& a, AttendKind kind, int grid, hipStre
   const int32_t* pf = a.pair_first;
   const int4* bf = reinterpret_cast<const int4*>(a.bin_first);
   void* args[] = {&copy, &pt, &descs, &pc, &bo, &pf, &bf};
+  // multi-token verification (q_len > 1) runs the instances with the causal
+  // limit; plain decode keeps the loop without it
+  const bool causal = a.q_len > 1;
   int waves;
   const void* fn;
   switch (kind) {
     case kAttendFp8:
       waves = Fp8Kv::kWaves;
-      fn = reinterpret_cast<const void*>(&attend_kernel<Fp8Kv>);
+      fn = causal ? reinterpret_cast<const void*>(&attend_kernel<Fp8Kv, true>)
+                  : reinterpret_cast<const void*>(&attend_kernel<Fp8Kv, false>);
       break;
     case kAttendFp8Q8:
       waves = Fp8KvQ8::kWaves;
-      fn = reinterpret_cast<const void*>(&attend_kernel<Fp8KvQ8>);
+      fn = causal ? reinterpret_cast<const void*>(&attend_kernel<Fp8KvQ8, true>)
+                  : reinterpret_cast<const void*>(&attend_kernel<Fp8KvQ8, false>);
       break;
     default:
       waves = Bf16Kv::kWaves;
-      fn = reinterpret_cast<const void*>(&attend_kernel<Bf16Kv>);
+      fn = causal ? reinterpret_cast<const void*>(&attend_kernel<Bf16Kv, true>)
+                  : reinterpret_cast<const void*>(&attend_kernel<Bf16Kv, false>);
   }
-  size_t lds = size_t(waves) * (32 + a.group * kRedRow) * sizeof(float);
+  size_t lds = size_t(waves) * (32 + a.ncols * kRedRow) * sizeof(float);
   const size_t merge_lds = size_t(merge_lds_floats(waves * 64)) * sizeof(float);
   if (a.fuse && merge_lds > lds) lds = merge_lds;
   if (grid <= 0) return hipSuccess;

@@ -14,8 +14,9 @@
 // with none is zero-filled there too), and the plan lists them compactly:
 // (pair, first descriptor, count).  A dynamic plan splits at most W - 1 pairs
 // (one per internal bin boundary), so the grid is (min(pairs, W - 1), G)
-// regardless of batch size; workgroup (i, q) merges query head q of list
-// entry i, or exits if the plan has fewer entries.  Thread t owns dims
+// regardless of batch size; workgroup (i, q) merges column q (query token
+// q / G, head q % G) of list entry i, or exits if the plan has fewer
+// entries.  Thread t owns dims
 // [4(t%32), +4) of partials k = t/32 (mod 8) and loads each partial's
 // log-sum-exp together with its row, merging online (running max, sum and
 // rescaled accumulator), sixteen partials per thread in flight: 128 partial
@@ -47,16 +48,16 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
   const int p = e.x;             // pair = kv_head * batch + request
   const int first = e.y;
   const int cnt = e.z;           // >= 2
-  const int q = blockIdx.y;      // query head within the group
-  const int G = a.group;
+  const int q = blockIdx.y;      // column: query token q / G, head q % G of the group
+  const int C = a.ncols;
   const int g = p / a.batch, r = p % a.batch;
-  const int64_t row = int64_t(r) * a.num_q_heads + int64_t(g) * G + q;
+  const int64_t row = query_row(r, g, q, a.q_len, a.group, a.num_q_heads);
   const int t = threadIdx.x;
   const int c4 = t % kLanesPerRow;
   const int kg = t / kLanesPerRow;
-  const float* lse = a.lse_part + int64_t(first) * G + q;
-  const f32x4_t* o = reinterpret_cast<const f32x4_t*>(a.o_part + (int64_t(first) * G + q) * kHeadDim);
-  const int64_t stride4 = int64_t(G) * kLanesPerRow;   // float4s between consecutive partials
+  const float* lse = a.lse_part + int64_t(first) * C + q;
+  const f32x4_t* o = reinterpret_cast<const f32x4_t*>(a.o_part + (int64_t(first) * C + q) * kHeadDim);
+  const int64_t stride4 = int64_t(C) * kLanesPerRow;   // float4s between consecutive partials
 
   float m = -INFINITY, l = 0.f;
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
@@ -67,7 +68,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
     for (int u = 0; u < kUnroll; ++u) {
       const int k = k0 + u * kRowGroups;
       if (k < cnt) {
-        ls[u] = lse[int64_t(k) * G];
+        ls[u] = lse[int64_t(k) * C];
         v[u] = o[int64_t(k) * stride4 + c4];
       }
     }
@@ -85,15 +86,17 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
   float M = -INFINITY;
 #pragma unroll
   for (int i = 0; i < kRowGroups; ++i) M = fmaxf(M, red_m[i]);
+  const float Mu = finite_or_zero(M);
   float L = 0.f;
   f32x4_t tot = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < kRowGroups; ++i) {
-    const float c = __builtin_amdgcn_exp2f(red_m[i] - M);   // 0 for threads that saw no partial
+    const float c = __builtin_amdgcn_exp2f(red_m[i] - Mu);   // 0 for threads that saw no partial
     L += red_l[i] * c;
     tot += red_o[i][c4] * c;
   }
-  store_bf16x4(a.out, row, c4, tot / L);
+  // a query token with no visible KV position (causal verification) outputs 0
+  store_bf16x4(a.out, row, c4, L > 0.f ? tot / L : f32x4_t{0.f, 0.f, 0.f, 0.f});
 }
 
 }  // namespace
@@ -102,7 +105,7 @@ hipError_t launch_combine(const CombineArgs& a, int max_split, hipStream_t s) {
   if (max_split <= 0) return hipSuccess;
   CombineArgs copy = a;
   void* args[] = {&copy};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&combine_kernel), dim3(max_split, a.group),
+  return hipLaunchKernel(reinterpret_cast<const void*>(&combine_kernel), dim3(max_split, a.ncols),
                          dim3(kThreads), args, 0, s);
 }
 

@@ -33,6 +33,9 @@ lbp_status check_config(const lbp_config* c) {
   if (c->num_q_heads < 1 || c->num_kv_heads < 1) return LBP_ERR_INVALID_ARG;
   if (c->num_q_heads % c->num_kv_heads != 0) return LBP_ERR_INVALID_ARG;
   if (c->num_q_heads / c->num_kv_heads > kMaxGroup) return LBP_ERR_UNSUPPORTED;
+  if (c->q_len < 0) return LBP_ERR_INVALID_ARG;
+  if (int64_t(c->num_q_heads / c->num_kv_heads) * (c->q_len > 1 ? c->q_len : 1) > kMaxGroup)
+    return LBP_ERR_UNSUPPORTED;
   if (c->max_batch < 1 || c->max_pages_per_seq < 1) return LBP_ERR_INVALID_ARG;
   if (c->num_workgroups < 0 || c->min_tiles_per_bin < 0) return LBP_ERR_INVALID_ARG;
   if (c->kv_dtype != LBP_KV_BF16 && c->kv_dtype != LBP_KV_FP8_E4M3) return LBP_ERR_UNSUPPORTED;
@@ -44,6 +47,10 @@ lbp_status check_config(const lbp_config* c) {
   if (c->num_workgroups > (1 << 20)) return LBP_ERR_UNSUPPORTED;
   return LBP_OK;
 }
+
+// Query tokens per request and query columns per KV head.
+int q_len_of(const lbp_config* c) { return c->q_len > 1 ? c->q_len : 1; }
+int ncols_of(const lbp_config* c) { return c->num_q_heads / c->num_kv_heads * q_len_of(c); }
 
 lbp_status resolve_bins(const lbp_config* c, int* W) {
   if (c->num_workgroups > 0) {
@@ -156,8 +163,7 @@ lbp_plan_offsets offsets_of(const lbp_plan_info* info) {
 }
 
 lbp_status check_split(const lbp_config* cfg, const lbp_plan_info* info, size_t bytes) {
-  const int G = cfg->num_q_heads / cfg->num_kv_heads;
-  return bytes < split_bytes(info->max_desc, G) ? LBP_ERR_WORKSPACE_TOO_SMALL : LBP_OK;
+  return bytes < split_bytes(info->max_desc, ncols_of(cfg)) ? LBP_ERR_WORKSPACE_TOO_SMALL : LBP_OK;
 }
 
 }  // namespace
@@ -190,7 +196,7 @@ lbp_status lbp_query_workspace(const lbp_config* cfg, int32_t policy, int32_t pa
   st = plan_shape(cfg, policy, param, cfg->max_batch, &num_bins, &max_desc, &spp, &used);
   if (st != LBP_OK) return st;
   *plan_bytes = plan_layout(policy, num_bins, max_desc, cfg->num_kv_heads * cfg->max_batch).total;
-  *split_ws = split_bytes(max_desc, cfg->num_q_heads / cfg->num_kv_heads);
+  *split_ws = split_bytes(max_desc, ncols_of(cfg));
   return LBP_OK;
 }
 
@@ -256,7 +262,7 @@ static lbp_status attend_impl(const lbp_config* cfg, const lbp_plan_info* info,
   a.v_scale = cfg->kv_dtype == LBP_KV_FP8_E4M3 ? v_scale_dev : nullptr;
   a.o_part = static_cast<float*>(split_ws_dev);
   a.lse_part = reinterpret_cast<float*>(static_cast<char*>(split_ws_dev) +
-                                        split_lse_offset(info->max_desc, G));
+                                        split_lse_offset(info->max_desc, ncols_of(cfg)));
   a.out = out_dev;
   a.trace = trace_dev;
   a.num_bins = info->num_bins;
@@ -282,6 +288,8 @@ static lbp_status attend_impl(const lbp_config* cfg, const lbp_plan_info* info,
   a.num_q_heads = cfg->num_q_heads;
   a.num_kv_heads = cfg->num_kv_heads;
   a.group = G;
+  a.q_len = q_len_of(cfg);
+  a.ncols = ncols_of(cfg);
   a.scale_log2 = cfg->sm_scale * 1.4426950408889634f;
   const AttendKind kind = q_scale_dev ? kAttendFp8Q8
                           : cfg->kv_dtype == LBP_KV_FP8_E4M3 ? kAttendFp8 : kAttendBf16;
@@ -316,12 +324,14 @@ lbp_status lbp_combine(const lbp_config* cfg, const lbp_plan_info* info, const v
   a.split_list = reinterpret_cast<const int32_t*>(pb + off.split_list);
   a.o_part = static_cast<const float*>(split_ws_dev);
   a.lse_part = reinterpret_cast<const float*>(static_cast<const char*>(split_ws_dev) +
-                                              split_lse_offset(info->max_desc, G));
+                                              split_lse_offset(info->max_desc, ncols_of(cfg)));
   a.out = out_dev;
   a.batch = info->batch;
   a.num_q_heads = cfg->num_q_heads;
   a.num_kv_heads = cfg->num_kv_heads;
   a.group = G;
+  a.q_len = q_len_of(cfg);
+  a.ncols = ncols_of(cfg);
   const int max_split =
       max_split_pairs(info->policy, info->num_bins, cfg->num_kv_heads * info->batch);
   if (launch_combine(a, max_split, static_cast<hipStream_t>(stream)) != hipSuccess)
@@ -424,6 +434,7 @@ lbp_status lbp_prologue(const lbp_config* cfg, int32_t batch, const lbp_prologue
   a.batch = batch;
   a.num_q_heads = cfg->num_q_heads;
   a.num_kv_heads = cfg->num_kv_heads;
+  a.q_len = q_len_of(cfg);
   a.max_tokens = cfg->max_pages_per_seq * kPageTokens;
   if (launch_prologue(a, static_cast<hipStream_t>(stream)) != hipSuccess) return LBP_ERR_HIP;
   return LBP_OK;

@@ -55,12 +55,19 @@ inline lbp_plan_offsets plan_layout(int policy, int num_bins, int max_desc, int 
   return o;
 }
 
-// Split buffer: o_part[max_desc][G][128] fp32, then lse_part[max_desc][G] fp32.
-inline uint64_t split_lse_offset(int max_desc, int group) {
-  return align_up(uint64_t(max_desc) * group * kHeadDim * 4, 256);
+// Split buffer: o_part[max_desc][C][128] fp32, then lse_part[max_desc][C]
+// fp32, with C = G * q_len columns (query token c / G, head c % G).
+inline uint64_t split_lse_offset(int max_desc, int ncols) {
+  return align_up(uint64_t(max_desc) * ncols * kHeadDim * 4, 256);
 }
-inline uint64_t split_bytes(int max_desc, int group) {
-  return align_up(split_lse_offset(max_desc, group) + uint64_t(max_desc) * group * 4, 256);
+inline uint64_t split_bytes(int max_desc, int ncols) {
+  return align_up(split_lse_offset(max_desc, ncols) + uint64_t(max_desc) * ncols * 4, 256);
+}
+
+// Row of q / out ([B][q_len][Hq][128]) for column c of KV head g, request r.
+__host__ __device__ inline int64_t query_row(int r, int g, int c, int q_len, int group,
+                                             int num_q_heads) {
+  return (int64_t(r) * q_len + c / group) * num_q_heads + int64_t(g) * group + c % group;
 }
 
 struct PlanArgs {
@@ -105,6 +112,7 @@ struct AttendArgs {
   int32_t fuse;              // 1: merge split pairs in this kernel (dynamic plans)
   int32_t num_bins;
   int32_t batch, num_q_heads, num_kv_heads, group;
+  int32_t q_len, ncols;      // query tokens per request; columns = group * q_len
   float scale_log2;          // sm_scale * log2(e)
 };
 
@@ -113,8 +121,9 @@ struct CombineArgs {
   const int32_t* split_list;
   const float* o_part;
   const float* lse_part;
-  void* out;                 // [B][Hq][128] bf16
+  void* out;                 // [B][q_len][Hq][128] bf16
   int32_t batch, num_q_heads, num_kv_heads, group;
+  int32_t q_len, ncols;
 };
 
 struct PrologueArgs {
@@ -135,6 +144,7 @@ struct PrologueArgs {
   float* k_scale;
   float* v_scale;
   int32_t batch, num_q_heads, num_kv_heads;
+  int32_t q_len;             // new tokens per request
   int32_t max_tokens;        // 64 * max_pages_per_seq
 };
 

@@ -17,12 +17,17 @@ namespace lbp {
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
+// x if finite, else 0: the reference point of an exponent when every term
+// is -inf (an empty state), so that exp2(-inf - ref) = 0 instead of NaN.
+__device__ inline float finite_or_zero(float x) { return x == -INFINITY ? 0.f : x; }
+
 // Online merge of one more (lse, row) into a running (max, sum, acc) state;
-// an empty state has m = -inf, l = 0, acc = 0.
+// an empty state (and an empty partial) has m = -inf, l = 0, acc = 0.
 __device__ inline void merge_into(float& m, float& l, f32x4_t& acc, float lse, f32x4_t o) {
   const float m_new = fmaxf(m, lse);
-  const float a = __builtin_amdgcn_exp2f(m - m_new);   // 0 while the state is empty
-  const float b = __builtin_amdgcn_exp2f(lse - m_new);
+  const float ref = finite_or_zero(m_new);
+  const float a = __builtin_amdgcn_exp2f(m - ref);     // 0 while the state is empty
+  const float b = __builtin_amdgcn_exp2f(lse - ref);   // 0 for an empty partial
   acc = acc * a + o * b;
   l = l * a + b;
   m = m_new;

@@ -1,4 +1,4 @@
-// Fused attention prologue for one decode token per request.
+// Fused attention prologue for the new tokens of one decode step.
 //
 // Method (SGLang x HPC-Ops page, "A fused attention prologue"; vLLM x
 // HPC-Ops page, the HpcRopeNorm paragraph of the Attention backend
@@ -8,12 +8,13 @@
 // the new token's slot, and with an FP8 query the query leaves in e4m3 with
 // one scale per (token, head), ready for the attention kernel without
 // requantization.  RoPE rotates dim pairs (i, i + 64) by the angles of the
-// token's position, read from a caller-supplied cos/sin table.  The new
-// token of request r sits at position seq_lens[r] - 1.
+// token's position, read from a caller-supplied cos/sin table.  The q_len
+// new tokens of request r (one for plain decode, more for speculative
+// verification) sit at positions seq_lens[r] - q_len + j.
 //
 // gfx950 mapping: the step is a few KB per request and bound by memory
 // latency, not arithmetic, so there is no MFMA.  One wave handles one
-// (request, head) row of 128 dims: lane l owns dims l and l + 64, which is
+// (request, token, head) row of 128 dims: lane l owns dims l and l + 64, which is
 // exactly one RoPE pair, so the rotation needs no cross-lane exchange; the
 // RMSNorm sum of squares and the FP8 row maximum are wave reductions.  Four
 // rows per 256-thread workgroup.  FP8 rows: scale = max |x| / 448 (1 for an
@@ -65,15 +66,16 @@ __device__ inline void quantize_pair(float z0, float z1, uint8_t& c0, uint8_t& c
 __global__ __launch_bounds__(kRowsPerBlock * 64) void prologue_kernel(PrologueArgs a) {
   const int H3 = a.num_q_heads + 2 * a.num_kv_heads;
   const int row = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
-  if (row >= a.batch * H3) return;   // whole wave
+  if (row >= a.batch * a.q_len * H3) return;   // whole wave
   const int lane = threadIdx.x & 63;
-  const int r = row / H3, h = row % H3;
+  const int rt = row / H3, h = row % H3;        // rt = request * q_len + token
+  const int r = rt / a.q_len, j = rt % a.q_len;
   const int L = a.seq_lens[r];
-  if (L <= 0) return;                // no new token for this request
-  const int pos = L - 1;
+  const int pos = L - a.q_len + j;   // new token j of request r
+  if (pos < 0) return;               // before the sequence start: no token
   const int prow = min(pos, a.max_position - 1);
 
-  const uint16_t* x = static_cast<const uint16_t*>(a.qkv) + (int64_t(r) * H3 + h) * kHeadDim;
+  const uint16_t* x = static_cast<const uint16_t*>(a.qkv) + (int64_t(rt) * H3 + h) * kHeadDim;
   float z0 = bf16_to_f32(x[lane]);
   float z1 = bf16_to_f32(x[lane + 64]);
   const bool is_q = h < a.num_q_heads;
@@ -92,7 +94,7 @@ __global__ __launch_bounds__(kRowsPerBlock * 64) void prologue_kernel(PrologueAr
   }
 
   if (is_q) {
-    const int64_t qrow = int64_t(r) * a.num_q_heads + h;
+    const int64_t qrow = int64_t(rt) * a.num_q_heads + h;
     if (a.q_fp8) {
       uint8_t c0, c1;
       float scale;
@@ -133,7 +135,7 @@ __global__ __launch_bounds__(kRowsPerBlock * 64) void prologue_kernel(PrologueAr
 }  // namespace
 
 hipError_t launch_prologue(const PrologueArgs& a, hipStream_t s) {
-  const int rows = a.batch * (a.num_q_heads + 2 * a.num_kv_heads);
+  const int rows = a.batch * a.q_len * (a.num_q_heads + 2 * a.num_kv_heads);
   if (rows <= 0) return hipSuccess;
   PrologueArgs copy = a;
   void* args[] = {&copy};

@@ -48,7 +48,7 @@ class Case:
 def build_case(wcfg: WorkloadConfig, layers: int = 1, lengths: Optional[Sequence[int]] = None,
                num_workgroups: int = 0, min_tiles: int = 4, poison: bool = True,
                policy: int = lbp.LBP_POLICY_DYNAMIC, param: int = 0,
-               max_pages_per_seq: Optional[int] = None) -> Case:
+               max_pages_per_seq: Optional[int] = None, q_len: int = 1) -> Case:
     say(f"[case] {wcfg.name} B={wcfg.batch if lengths is None else len(lengths)} "
         f"Hq={wcfg.num_q_heads} Hkv={wcfg.num_kv_heads} kv={wcfg.kv_dtype} layers={layers} "
         f"W={num_workgroups} F={min_tiles} policy={policy} param={param}")
@@ -61,7 +61,7 @@ def build_case(wcfg: WorkloadConfig, layers: int = 1, lengths: Optional[Sequence
     table[:, :wl.page_table.shape[1]] = wl.page_table
     cfg = lbp.make_config(wcfg.num_q_heads, wcfg.num_kv_heads, len(wl.lengths), mp,
                           kv_dtype=wcfg.kv_dtype, num_workgroups=num_workgroups,
-                          min_tiles_per_bin=min_tiles, sm_scale=wcfg.sm_scale)
+                          min_tiles_per_bin=min_tiles, sm_scale=wcfg.sm_scale, q_len=q_len)
     pb, sb = lbp.lbp_query_workspace(cfg, policy, param)
     case = Case(wcfg, wl, cfg,
                 torch.from_numpy(np.asarray(wl.lengths, dtype=np.int32)).cuda(),
@@ -169,6 +169,53 @@ def oracle_pairs(case: Case, layer: int, pairs, q64: Optional[np.ndarray] = None
             o = np.zeros_like(o)   # a pair with no tokens outputs zeros
         res[(g, r)] = o[0]
     return res
+
+
+def oracle_verify_pairs(case: Case, layer: int, pairs, q64: np.ndarray):
+    """fp64 oracle rows [T, G, D] of multi-token verification for (kv_head,
+    request) pairs; q64 is the query [B, T, Hq, D] in fp64."""
+    Lyr = case.wl.layers[layer]
+    G = case.G
+    fp8 = case.wcfg.kv_dtype == "fp8_e4m3"
+    res = {}
+    for g, r in pairs:
+        Lr = int(case.wl.lengths[r])
+        n = max(1, (Lr + 63) // 64)
+        pages = case.page_table[r, :n].long()
+        kc = Lyr.k_cache.index_select(0, pages)[:, g:g + 1].contiguous()
+        vc = Lyr.v_cache.index_select(0, pages)[:, g:g + 1].contiguous()
+        q = q64[r:r + 1, :, g * G:(g + 1) * G]
+        table = np.arange(n, dtype=np.int32)[None]
+        if fp8:
+            ks = Lyr.k_scale.index_select(0, pages)[:, g:g + 1].contiguous().cpu().numpy()
+            vs = Lyr.v_scale.index_select(0, pages)[:, g:g + 1].contiguous().cpu().numpy()
+            o, _ = oracle.attention.paged_verify_attention(
+                q, kc.cpu().numpy(), vc.cpu().numpy(), table, [Lr], 1, case.wcfg.sm_scale,
+                kv_dtype="fp8_e4m3", k_scale=ks, v_scale=vs)
+        else:
+            o, _ = oracle.attention.paged_verify_attention(q, bits(kc), bits(vc), table, [Lr], 1,
+                                                           case.wcfg.sm_scale)
+        res[(g, r)] = o[0]
+    return res
+
+
+def compare_verify(case: Case, got: torch.Tensor, ref_rows: dict, what=""):
+    """compare() for [B, T, Hq, D] outputs: rows [r, :, g*G:(g+1)*G] per pair."""
+    G = case.G
+    gv = bf16_to_f64(got)
+    a = np.stack([gv[r, :, g * G:(g + 1) * G] for (g, r) in ref_rows])
+    b = np.stack(list(ref_rows.values()))
+    assert np.all(np.isfinite(a)), f"{what}: non-finite output"
+    diff = a - b
+    max_abs = float(np.max(np.abs(diff)))
+    rel_rms = float(np.linalg.norm(diff) / max(np.linalg.norm(b), 1e-30))
+    say(f"[parity] {what}: pairs={len(ref_rows)} max_abs={max_abs:.3e} rel_rms={rel_rms:.3e}")
+    if case.wcfg.kv_dtype == "bf16":
+        assert max_abs <= BF16_MAX_ABS, (what, max_abs)
+        assert rel_rms <= BF16_REL_RMS, (what, rel_rms)
+    else:
+        assert max_abs <= FP8_MAX_ABS, (what, max_abs)
+    return max_abs, rel_rms
 
 
 def compare(case: Case, got: torch.Tensor, ref_rows: dict, what=""):

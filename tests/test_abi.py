@@ -92,9 +92,16 @@ def query(c, policy=0, param=0):
 
 
 def test_version_and_status_strings(lib):
-    assert lbp.lbp_version() == 1
+    assert lbp.lbp_version() == 2
     for s, name in lbp._STATUS_NAMES.items():
         assert lbp.lbp_status_string(s) == name
+
+
+def test_q_len_workspace(lib):
+    _, _, sb1 = query(cfg())
+    st, _, sb2 = query(cfg(q_len=2))
+    assert st == lbp.LBP_OK and sb2 >= 2 * sb1 - 512      # twice the columns per slot
+    assert query(cfg(num_q_heads=8, num_kv_heads=8, q_len=16))[0] == lbp.LBP_OK
 
 
 def test_workspace_sizes(lib):
@@ -122,6 +129,8 @@ def test_workspace_sizes(lib):
     (dict(sm_scale=0.0), lbp.LBP_ERR_INVALID_ARG),
     (dict(sm_scale=float("nan")), lbp.LBP_ERR_INVALID_ARG),
     (dict(max_pages_per_seq=1 << 30), lbp.LBP_ERR_UNSUPPORTED),
+    (dict(q_len=3), lbp.LBP_ERR_UNSUPPORTED),                             # 8 * 3 > 16
+    (dict(q_len=-1), lbp.LBP_ERR_INVALID_ARG),
 ])
 def test_config_guards(lib, kw, status):
     assert query(cfg(**kw))[0] == status

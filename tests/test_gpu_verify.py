@@ -1,0 +1,126 @@
+"""GPU parity of multi-token decode (speculative verification, cfg.q_len > 1).
+
+Token j of request r sits at position L_r - q_len + j and attends causally to
+the KV positions up to its own; the MFMA columns hold (token, head) pairs of
+the KV head's group, G * q_len <= 16.  Every case is compared with the fp64
+oracle (oracle.attention.paged_verify_attention) at the path's tolerance,
+through lbp_attend, lbp_attend_fused and (FP8) lbp_attend_fp8q, including
+tokens with no visible position (zeros) and descriptors in which a column
+sees no token at all.
+"""
+
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import load_balanced_paged_amd as lbp
+import oracle
+from gpu_support import (all_pairs, assert_taskmap_matches, bits, build_case, compare_verify,
+                         oracle_verify_pairs, sample_pairs, say)
+from workloads import CONFIGS, quantize_query_e4m3
+
+pytestmark = pytest.mark.gpu
+
+
+def make_q(case, T, seed=0):
+    B = len(case.wl.lengths)
+    g = torch.Generator(device="cuda").manual_seed(900 + seed)
+    return torch.randn((B, T, case.wcfg.num_q_heads, 128), generator=g, device="cuda").to(
+        torch.bfloat16)
+
+
+def run(case, q, fn=lbp.lbp_attend):
+    lay = case.wl.layers[0]
+    out = torch.full_like(q, float("nan"))
+    fn(case.cfg, case.info, case.plan_ws, q, lay.k_cache, lay.v_cache, lay.k_scale, lay.v_scale,
+       case.split_ws, out)
+    torch.cuda.synchronize()
+    return out
+
+
+def q64_of(q):
+    return oracle.attention.bf16_bits_to_f64(bits(q))
+
+
+@pytest.mark.parametrize("name", ["tiny", "skewed"])
+def test_verify_two_tokens_all_rows(gpu_lib, name):
+    case = build_case(CONFIGS[name], q_len=2)
+    assert_taskmap_matches(case)
+    q = make_q(case, 2)
+    ref = oracle_verify_pairs(case, 0, all_pairs(case), q64_of(q))
+    compare_verify(case, run(case, q), ref, f"verify {name} T=2")
+    compare_verify(case, run(case, q, lbp.lbp_attend_fused), ref, f"verify {name} T=2 fused")
+
+
+def test_verify_mixed_sampled(gpu_lib):
+    case = build_case(CONFIGS["mixed"], q_len=2)
+    q = make_q(case, 2, seed=1)
+    compare_verify(case, run(case, q), oracle_verify_pairs(case, 0, sample_pairs(case, 10),
+                                                           q64_of(q)), "verify mixed T=2")
+
+
+@pytest.mark.parametrize("group,hkv,T", [(4, 2, 4), (1, 4, 16), (3, 3, 5), (16, 1, 1)])
+def test_verify_shapes_short_requests(gpu_lib, group, hkv, T):
+    """Requests shorter than T (early tokens see nothing), tile-sized bins."""
+    wcfg = dataclasses.replace(CONFIGS["tiny"], name=f"v{group}x{T}", batch=6,
+                               num_q_heads=group * hkv, num_kv_heads=hkv)
+    case = build_case(wcfg, lengths=[1, 2, 3, 65, 130, 900], num_workgroups=7, min_tiles=1,
+                      q_len=T)
+    q = make_q(case, T, seed=2)
+    ref = oracle_verify_pairs(case, 0, all_pairs(case), q64_of(q))
+    out = run(case, q)
+    compare_verify(case, out, ref, f"verify G={group} T={T}")
+    compare_verify(case, run(case, q, lbp.lbp_attend_fused), ref, f"verify G={group} T={T} fused")
+    # a token before the sequence start outputs exact zeros
+    assert torch.all(out[0, :T - 1] == 0) if T > 1 else True
+
+
+def test_verify_fully_masked_descriptor(gpu_lib):
+    """L = 65 with one-tile bins: the descriptor [64, 65) is invisible to the
+    first of two tokens, so its partial for those columns is empty."""
+    wcfg = dataclasses.replace(CONFIGS["tiny"], name="v-masked", batch=3)
+    case = build_case(wcfg, lengths=[65, 129, 64], num_workgroups=64, min_tiles=1, q_len=2)
+    tm = lbp.read_taskmap(case.plan_ws, case.info)
+    assert [64, 65] in tm["desc"][:, 2:].tolist()
+    q = make_q(case, 2, seed=3)
+    ref = oracle_verify_pairs(case, 0, all_pairs(case), q64_of(q))
+    compare_verify(case, run(case, q), ref, "verify masked descriptor")
+    compare_verify(case, run(case, q, lbp.lbp_attend_fused), ref, "verify masked descriptor fused")
+
+
+def test_verify_static_plan(gpu_lib):
+    case = build_case(CONFIGS["skewed"], policy=lbp.LBP_POLICY_STATIC_SPLITS, param=5, q_len=2)
+    q = make_q(case, 2, seed=4)
+    compare_verify(case, run(case, q), oracle_verify_pairs(case, 0, all_pairs(case), q64_of(q)),
+                   "verify static")
+
+
+def test_verify_fp8_kv_and_query(gpu_lib):
+    wcfg = dataclasses.replace(CONFIGS["fp8"], name="v-fp8", batch=5)
+    case = build_case(wcfg, lengths=[1, 70, 700, 3000, 20000], q_len=2)
+    q = make_q(case, 2, seed=5)
+    pairs = all_pairs(case)
+    compare_verify(case, run(case, q), oracle_verify_pairs(case, 0, pairs, q64_of(q)),
+                   "verify fp8 kv")
+    codes, scale = quantize_query_e4m3(q)
+    lay = case.wl.layers[0]
+    out = torch.full_like(q, float("nan"))
+    lbp.lbp_attend_fp8q(case.cfg, case.info, case.plan_ws, codes, scale, lay.k_cache,
+                        lay.v_cache, lay.k_scale, lay.v_scale, case.split_ws, out)
+    torch.cuda.synchronize()
+    q8 = oracle.e4m3.dequantize(codes.cpu().numpy(), scale.cpu().numpy())
+    compare_verify(case, out, oracle_verify_pairs(case, 0, pairs, q8), "verify fp8 q")
+
+
+def test_verify_one_token_equals_decode(gpu_lib):
+    """q_len = 1 in the [B, 1, Hq, D] layout is bit-identical to plain decode."""
+    case = build_case(CONFIGS["skewed"])
+    lay = case.wl.layers[0]
+    a = run(case, lay.q[:, None].contiguous())
+    b = torch.empty_like(lay.q)
+    lbp.lbp_attend(case.cfg, case.info, case.plan_ws, lay.q, lay.k_cache, lay.v_cache, None, None,
+                   case.split_ws, b)
+    torch.cuda.synchronize()
+    assert torch.equal(a[:, 0].view(torch.int16), b.view(torch.int16))
