@@ -62,6 +62,8 @@ def parse_args():
                     help="skip the lbp_attend_fused timing (profiler runs: keeps every launch of "
                          "the attention kernel a plain one)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-verify", action="store_true",
+                    help="skip the multi-token verification timings (q_len 2 and 4)")
     ap.add_argument("--no-table3", action="store_true",
                     help="skip the six FP8-KV length mixes of the vLLM x HPC-Ops page, Table 3")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -111,16 +113,45 @@ class Bench:
             self.plans[key] = (info, plan_ws, split_ws)
         return self.plans[key]
 
-    def step_fn(self, policy=0, param=0, fused=False, fp8q=False):
+    def verify_setup(self, q_len):
+        """Config, dynamic plan, queries and outputs for multi-token
+        verification: q_len new tokens per request (the lengths already count
+        them), queries [batch, q_len, Hq, 128] drawn like the decode ones."""
+        if not hasattr(self, "verify"):
+            self.verify = {}
+        if q_len not in self.verify:
+            lbp, w = self.lbp, self.wcfg
+            cfg = lbp.make_config(w.num_q_heads, w.num_kv_heads, w.batch,
+                                  self.wl.page_table.shape[1], kv_dtype=w.kv_dtype,
+                                  num_workgroups=0, min_tiles_per_bin=4, sm_scale=w.sm_scale,
+                                  q_len=q_len)
+            pb, sb = lbp.lbp_query_workspace(cfg)
+            plan_ws = torch.empty(pb, dtype=torch.uint8, device="cuda")
+            split_ws = torch.empty(sb, dtype=torch.uint8, device="cuda")
+            info = lbp.lbp_plan(cfg, self.seq, self.table, plan_ws)
+            g = torch.Generator(device="cuda")
+            g.manual_seed(w.seed + 7919 * q_len)
+            qs = [torch.randn((w.batch, q_len, w.num_q_heads, 128), generator=g, device="cuda")
+                  .to(torch.bfloat16) for _ in range(self.layers)]
+            outs = [torch.empty_like(q) for q in qs]
+            self.verify[q_len] = (cfg, (info, plan_ws, split_ws), qs, outs)
+        return self.verify[q_len]
+
+    def step_fn(self, policy=0, param=0, fused=False, fp8q=False, q_len=1):
         """A closure launching one attend (lbp_attend, lbp_attend_fused, or
         lbp_attend_fp8q with the layer's query in e4m3) on layer i with
-        pre-marshalled arguments."""
+        pre-marshalled arguments; q_len > 1 runs multi-token verification
+        (lbp_attend, dynamic plan)."""
         import ctypes
         lbp = self.lbp
         lib = lbp.load()
-        info, plan_ws, split_ws = self.plan(policy, param)
+        cfg, outs, vq = self.cfg, self.outs, None
+        if q_len > 1:
+            cfg, (info, plan_ws, split_ws), vq, outs = self.verify_setup(q_len)
+        else:
+            info, plan_ws, split_ws = self.plan(policy, param)
         stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-        cfgp, infop = ctypes.byref(self.cfg), ctypes.byref(info)
+        cfgp, infop = ctypes.byref(cfg), ctypes.byref(info)
         P = ctypes.c_void_p
         sbytes = split_ws.numel()
         args = []
@@ -131,10 +162,10 @@ class Bench:
             ks = P(L.k_scale.data_ptr()) if L.k_scale is not None else None
             vs = P(L.v_scale.data_ptr()) if L.v_scale is not None else None
             q = (P(self.q8[i][0].data_ptr()), P(self.q8[i][1].data_ptr())) if fp8q else \
-                (P(L.q.data_ptr()),)
+                (P((vq[i] if vq is not None else L.q).data_ptr()),)
             args.append((cfgp, infop, P(plan_ws.data_ptr())) + q +
                         (P(L.k_cache.data_ptr()), P(L.v_cache.data_ptr()), ks, vs,
-                         P(split_ws.data_ptr()), sbytes, P(self.outs[i].data_ptr()), stream))
+                         P(split_ws.data_ptr()), sbytes, P(outs[i].data_ptr()), stream))
 
         fn = lib.lbp_attend_fp8q if fp8q else lib.lbp_attend_fused if fused else lib.lbp_attend
 
@@ -156,8 +187,9 @@ class Bench:
                 i += 1
             torch.cuda.synchronize()
 
-    def time_steps(self, steps, warmup, policy=0, param=0, eager=False, fused=False, fp8q=False):
-        run, _ = self.step_fn(policy, param, fused, fp8q)
+    def time_steps(self, steps, warmup, policy=0, param=0, eager=False, fused=False, fp8q=False,
+                   q_len=1):
+        run, _ = self.step_fn(policy, param, fused, fp8q, q_len)
         for i in range(warmup):
             run(i)
         torch.cuda.synchronize()
@@ -169,7 +201,7 @@ class Bench:
                 s = torch.cuda.Stream()
                 s.wait_stream(torch.cuda.current_stream())
                 with torch.cuda.stream(s):
-                    run_g, _ = self.step_fn(policy, param, fused, fp8q)   # capture stream
+                    run_g, _ = self.step_fn(policy, param, fused, fp8q, q_len)   # capture stream
                     with torch.cuda.graph(graph, stream=s):
                         for i in range(steps):
                             run_g(i)
@@ -288,6 +320,7 @@ class Bench:
 
     def free(self):
         self.plans.clear()
+        self.verify = {}
         self.outs = None
         self.wl = None
         torch.cuda.empty_cache()
@@ -397,6 +430,16 @@ def bench_one(name, lbp, args, headline):
                                "min": round(k_min, 2), "max": round(k_max, 2)}
     res["plan_us"] = round(b.time_plan(), 2)
     res["prologue"] = b.time_prologue(min(args.steps, 100))
+    if not args.no_verify:
+        # multi-token verification: the same KV, q_len query tokens per request
+        res["verify"] = {}
+        for T in (2, 4):
+            if b.wcfg.num_q_heads // b.wcfg.num_kv_heads * T > 16:
+                continue
+            vms, _ = b.time_steps(args.steps, args.warmup, eager=args.eager, q_len=T)
+            vgbs = b.wl.kv_bytes / (vms * 1e-3) / 1e9
+            res["verify"][f"q_len={T}"] = {"us_per_step": round(vms * 1e3, 2),
+                                           "kv_gbs": round(vgbs, 1)}
     res["amortized_us_per_layer"] = round((res["plan_us"] + b.layers * us) / b.layers, 2)
     if not args.no_static:
         W = info.num_bins
@@ -547,7 +590,7 @@ def main():
         "amortized_us_per_layer": head["amortized_us_per_layer"],
         "attend_kernel_us": head["attend_kernel_us"],
     }
-    for k in ("fused_us_per_step", "fp8q_us_per_step", "prologue"):
+    for k in ("fused_us_per_step", "fp8q_us_per_step", "prologue", "verify"):
         if k in head:
             out[k] = head[k]
     if "static_splits" in head:
