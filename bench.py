@@ -63,7 +63,7 @@ def parse_args():
                          "the attention kernel a plain one)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-verify", action="store_true",
-                    help="skip the multi-token verification timings (q_len 2 and 4)")
+                    help="skip the multi-token verification timings (q_len 2, 4, 6)")
     ap.add_argument("--no-table3", action="store_true",
                     help="skip the six FP8-KV length mixes of the vLLM x HPC-Ops page, Table 3")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -433,8 +433,8 @@ def bench_one(name, lbp, args, headline):
     if not args.no_verify:
         # multi-token verification: the same KV, q_len query tokens per request
         res["verify"] = {}
-        for T in (2, 4):
-            if b.wcfg.num_q_heads // b.wcfg.num_kv_heads * T > 16:
+        for T in (2, 4, 6):
+            if b.wcfg.num_q_heads // b.wcfg.num_kv_heads * T > 64:
                 continue
             vms, _ = b.time_steps(args.steps, args.warmup, eager=args.eager, q_len=T)
             vgbs = b.wl.kv_bytes / (vms * 1e-3) / 1e9

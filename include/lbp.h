@@ -52,12 +52,13 @@ extern "C" {
 #define LBP_HEAD_DIM 128
 #define LBP_PAGE_SIZE 64
 #define LBP_MAX_GROUP 16
+#define LBP_MAX_QUERY_COLUMNS 64 /* (Hq / H_kv) * q_len */
 #define LBP_PLAN_MAGIC 0x4C425031u /* "LBP1" */
 
 typedef enum lbp_status {
   LBP_OK = 0,
   LBP_ERR_INVALID_ARG = 1,         /* NULL pointer, non-positive size, ... */
-  LBP_ERR_UNSUPPORTED = 2,         /* head_dim != 128, page != 64, group * q_len > 16 */
+  LBP_ERR_UNSUPPORTED = 2,         /* head_dim != 128, page != 64, group * q_len > 64 */
   LBP_ERR_WORKSPACE_TOO_SMALL = 3, /* a caller workspace is below the query */
   LBP_ERR_MISMATCH = 4,            /* plan info does not match the config */
   LBP_ERR_HIP = 5                  /* the HIP runtime refused a launch/query */
@@ -93,7 +94,7 @@ typedef struct lbp_config {
                                 speculative verification, where token j of request r
                                 sits at position L_r - q_len + j and attends causally
                                 to KV positions <= its own; requires
-                                (Hq / H_kv) * q_len <= 16 */
+                                (Hq / H_kv) * q_len <= LBP_MAX_QUERY_COLUMNS */
 } lbp_config;
 
 /* Host-side record of a built plan, filled by lbp_plan / lbp_plan_static and

@@ -133,25 +133,28 @@ struct SliceRsrc {
   rsrc_t k, v, ks, vs;
 };
 
-// Query rows of the MFMA columns: column c is query token c / G, head c % G
+// Query rows of the query columns: column c is query token c / G, head c % G
 // of KV head g's group, at row (r * q_len + c / G) * Hq + g * G + c % G.
-// The lane's row relative to column 0's, and the span of rows the buffer
-// resource covers, depend only on the launch, so they are computed once per
-// kernel (the division stays out of the descriptor loop, where it would
-// delay the query loads behind the KV loads).  Columns past G * q_len get a
-// row past the resource's end and read zeros.  With one query token (the
-// non-causal instance) the row is the column itself, which keeps the query
-// offsets equal to the K row offsets of the same lanes.
+// MFMA lane column n of a wave in column block b holds column
+// c = b * block_cols + n.  The lane's row relative to column 0's, and the
+// span of rows the buffer resource covers, depend only on the launch and the
+// wave, so they are computed once per kernel (the division stays out of the
+// descriptor loop, where it would delay the query loads behind the KV
+// loads).  Lanes past the block's columns get a row past the resource's end
+// and read zeros.  With one query token (the non-causal instance, a single
+// block) the row is the column itself, which keeps the query offsets equal to
+// the K row offsets of the same lanes.
 struct QLane {
   int row;    // this lane's row relative to column 0's, or past `rows` (reads 0)
   int rows;   // rows the resource spans
 };
 template <bool kMultiToken>
-__device__ inline QLane q_lane(const AttendArgs& a, int n) {
+__device__ inline QLane q_lane(const AttendArgs& a, int n, int col0, int block_valid) {
   QLane q;
   if constexpr (kMultiToken) {
+    const int c = col0 + n;
     q.rows = (a.q_len - 1) * a.num_q_heads + a.group;
-    q.row = n < a.ncols ? (n / a.group) * a.num_q_heads + n % a.group : q.rows;
+    q.row = n < block_valid ? (c / a.group) * a.num_q_heads + c % a.group : q.rows;
   } else {
     q.rows = a.group;
     q.row = n;
@@ -465,14 +468,27 @@ __device__ inline void attend_bin(const AttendArgs& a, const int32_t* __restrict
                                   const int32_t* __restrict__ pair_first, float* smem, int bin) {
   constexpr int kWaves = Kv::kWaves;
   constexpr int kThreads = kWaves * 64;
-  constexpr int step = kWaves * kSlice;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int n = lane & 15;         // MFMA column: query token n / G, head n % G
+  const int n = lane & 15;         // MFMA column of this lane within its block
   const int grp = lane >> 4;
   const int G = a.group;
-  const int C = a.ncols;           // G * q_len <= 16
-  const int red_stride = 32 + C * kRedRow;
+  const int C = a.ncols;           // G * q_len
+  // Column blocks (multi-token verification with more than 16 columns): the
+  // waves split into nblk equal groups, group b computes columns
+  // [b * cpb, b * cpb + cpb) over every slice of the descriptor, so each
+  // group reads the same KV slices (the repeats come from the CU's caches)
+  // and keeps the register footprint of one 16-column tile.  Plain decode
+  // has one block of all the waves.
+  const int nblk = kCausal ? a.col_blocks : 1;
+  const int wpb = kCausal ? kWaves / nblk : kWaves;    // waves per block
+  const int blk = kCausal ? wave / wpb : 0;
+  const int wslot = kCausal ? wave - blk * wpb : wave;  // the wave's place in its block
+  const int cpb = kCausal ? a.block_cols : C;          // columns per block, <= 16
+  const int col0 = blk * cpb;
+  const int nvalid = kCausal ? min(cpb, C - col0) : C; // this block's columns
+  const int step = wpb * kSlice;
+  const int red_stride = 32 + cpb * kRedRow;
   float* red = smem + wave * red_stride;
   // range and first descriptor are independent loads: one round trip
   const int d_begin = bin_offset[bin];
@@ -481,11 +497,11 @@ __device__ inline void attend_bin(const AttendArgs& a, const int32_t* __restrict
   asm volatile("" ::"s"(ds.x), "s"(ds.y), "s"(ds.z), "s"(ds.w));   // keep the load above the exit
   if (d_begin >= d_end) return;
 
-  const QLane ql = q_lane<kCausal>(a, n);
+  const QLane ql = q_lane<kCausal>(a, n, col0, nvalid);
   typename Kv::Q qb;
   typename Kv::Buf buf[2];
   Kv::load_q(qb, a, ql, ds.x, ds.y, grp);
-  Kv::issue(buf[0], slice_rsrc<Kv>(a, pt, ds.x, ds.y, ds.z + wave * kSlice, ds.w), lane);
+  Kv::issue(buf[0], slice_rsrc<Kv>(a, pt, ds.x, ds.y, ds.z + wslot * kSlice, ds.w), lane);
 
   for (int d = d_begin; d < d_end; ++d) {
     const int g = ds.x, r = ds.y, t_begin = ds.z, t_end = ds.w;
@@ -499,7 +515,7 @@ __device__ inline void attend_bin(const AttendArgs& a, const int32_t* __restrict
     int lim = INT_MAX;
     if constexpr (kCausal) {
       const int L = descs[pair_first[p] + pair_count[p] - 1].w;
-      lim = L - a.q_len + 1 + n / G;
+      lim = L - a.q_len + 1 + (col0 + n) / G;
     }
 
     WaveState st;
@@ -510,7 +526,7 @@ __device__ inline void attend_bin(const AttendArgs& a, const int32_t* __restrict
 
     // buf[0] already holds (or is loading) this wave's first slice of d; a
     // slice past t_end loads nothing
-    int tok = t_begin + wave * kSlice;
+    int tok = t_begin + wslot * kSlice;
     bool more = tok < t_end;
     while (more) {
 #pragma unroll
@@ -530,12 +546,12 @@ __device__ inline void attend_bin(const AttendArgs& a, const int32_t* __restrict
       // slice's first K row is, so the next descriptor's loop can wait for
       // its loads one by one
       Kv::load_q(qb, a, ql, dn.x, dn.y, grp);
-      Kv::issue(buf[0], slice_rsrc<Kv>(a, pt, dn.x, dn.y, dn.z + wave * kSlice, dn.w), lane);
+      Kv::issue(buf[0], slice_rsrc<Kv>(a, pt, dn.x, dn.y, dn.z + wslot * kSlice, dn.w), lane);
     }
 
     // merge the wave states of this descriptor
     st.l = wave_sum_across_groups(st.l);
-    if (n < C) {
+    if (n < nvalid) {
       if (grp == 0) {
         red[n] = st.m;
         red[16 + n] = st.l;
@@ -552,19 +568,23 @@ __device__ inline void attend_bin(const AttendArgs& a, const int32_t* __restrict
     __syncthreads();
     for (int idx = threadIdx.x; idx < C * kHeadDim; idx += kThreads) {
       const int q = idx >> 7, dim = idx & (kHeadDim - 1);
+      // the waves of q's column block hold it, as their column qc
+      const int qb = kCausal ? q / cpb : 0;
+      const int qc = q - qb * cpb;
+      const float* rb = smem + qb * wpb * red_stride;
       float M = -INFINITY;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, smem[w * red_stride + q]);
+      for (int w = 0; w < wpb; ++w) M = fmaxf(M, rb[w * red_stride + qc]);
       // a column with no visible token in this descriptor (possible only
       // under a causal limit) gives an empty partial: o = 0, lse = -inf
       const float Mu = kCausal ? finite_or_zero(M) : M;
       float L = 0.f, o = 0.f;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float* rw = smem + w * red_stride;
-        const float c = __builtin_amdgcn_exp2f(rw[q] - Mu);
-        L += rw[16 + q] * c;
-        o += rw[32 + q * kRedRow + dim] * c;
+      for (int w = 0; w < wpb; ++w) {
+        const float* rw = rb + w * red_stride;
+        const float c = __builtin_amdgcn_exp2f(rw[qc] - Mu);
+        L += rw[16 + qc] * c;
+        o += rw[32 + qc * kRedRow + dim] * c;
       }
       const bool empty = kCausal && !(L > 0.f);
       const float on = empty ? 0.f : o / L;
@@ -611,23 +631,23 @@ __device__ inline int merge_group_size(int cnt) {
 // LDS floats the merge needs: per (row group, head) a max, a sum and a row.
 constexpr int merge_lds_floats(int threads) { return 64 + (threads / 32) * kHeadDim; }
 
-// Merges the n partials in slots slot0, slot0 + stride, ... (in that order)
-// of pair (g, r).  dst < 0: the result is the pair's final output (BF16 to
-// `out`); otherwise it is written back as a partial (row and log-sum-exp)
-// to slot dst.  Thread t owns float4 column t % 32 of query column
-// (t / 32) % C and partials i = row group (mod R), R = threads / (32 C),
-// C = G * q_len <= 16; the R states are
-// merged through LDS in a fixed order, so the result is bitwise
-// reproducible.
+// Merges, for chunk columns q0 .. q0 + Cc - 1, the n partials in slots
+// slot0, slot0 + stride, ... (in that order) of pair (g, r).  dst < 0: the
+// result is the pair's final output (BF16 to `out`); otherwise it is written
+// back as a partial (row and log-sum-exp) to slot dst.  Thread t owns float4
+// column t % 32 of column q0 + (t / 32) % Cc and partials i = row group
+// (mod R), R = threads / (32 Cc); the R states are merged through LDS in a
+// fixed order, so the result is bitwise reproducible.
 template <int kThreads>
-__device__ void merge_run(const AttendArgs& a, float* smem, int slot0, int stride, int n, int dst,
-                          int g, int r) {
+__device__ void merge_columns(const AttendArgs& a, float* smem, int slot0, int stride, int n,
+                              int dst, int g, int r, int q0, int Cc) {
   const int C = a.ncols;       // columns: query token q / G, head q % G
-  const int R = kThreads / (32 * C);
+  const int R = kThreads / (32 * Cc);
   const int t = threadIdx.x;
   const int c4 = t & 31;
-  const int q = (t >> 5) % C;
-  const int rg = (t >> 5) / C;
+  const int qc = (t >> 5) % Cc;
+  const int q = q0 + qc;
+  const int rg = (t >> 5) / Cc;
   float m = -INFINITY, l = 0.f;
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
   if (rg < R) {
@@ -650,11 +670,11 @@ __device__ void merge_run(const AttendArgs& a, float* smem, int slot0, int strid
         if (i0 + u * R < n) merge_into(m, l, acc, ls[u], v[u]);
     }
   }
-  float* red_m = smem;         // [R * C] (R * C <= threads / 32 <= 32)
+  float* red_m = smem;         // [R * Cc] (R * Cc <= threads / 32 <= 32)
   float* red_l = smem + 32;
-  f32x4_t* red_o = reinterpret_cast<f32x4_t*>(smem + 64);   // [R * C][32]
+  f32x4_t* red_o = reinterpret_cast<f32x4_t*>(smem + 64);   // [R * Cc][32]
   if (rg < R) {
-    const int s = rg * C + q;
+    const int s = rg * Cc + qc;
     if (c4 == 0) {
       red_m[s] = m;
       red_l[s] = l;
@@ -664,14 +684,14 @@ __device__ void merge_run(const AttendArgs& a, float* smem, int slot0, int strid
   __syncthreads();
   if (rg == 0) {
     float M = -INFINITY;
-    for (int k = 0; k < R; ++k) M = fmaxf(M, red_m[k * C + q]);
+    for (int k = 0; k < R; ++k) M = fmaxf(M, red_m[k * Cc + qc]);
     const float Mu = finite_or_zero(M);
     float L = 0.f;
     f32x4_t tot = {0.f, 0.f, 0.f, 0.f};
     for (int k = 0; k < R; ++k) {
-      const float c = __builtin_amdgcn_exp2f(red_m[k * C + q] - Mu);   // 0 for an empty state
-      L += red_l[k * C + q] * c;
-      tot += red_o[(k * C + q) * 32 + c4] * c;
+      const float c = __builtin_amdgcn_exp2f(red_m[k * Cc + qc] - Mu);   // 0 for an empty state
+      L += red_l[k * Cc + qc] * c;
+      tot += red_o[(k * Cc + qc) * 32 + c4] * c;
     }
     const bool empty = !(L > 0.f);   // no visible token in any merged partial
     const f32x4_t o = empty ? f32x4_t{0.f, 0.f, 0.f, 0.f} : tot / L;
@@ -686,6 +706,18 @@ __device__ void merge_run(const AttendArgs& a, float* smem, int slot0, int strid
     }
   }
   __syncthreads();
+}
+
+// Merges the n partials in slots slot0, slot0 + stride, ... of pair (g, r)
+// for every query column, in chunks of at most threads / 32 columns (see
+// merge_columns for dst).
+template <int kThreads>
+__device__ void merge_run(const AttendArgs& a, float* smem, int slot0, int stride, int n, int dst,
+                          int g, int r) {
+  constexpr int kSlots = kThreads / 32;
+  const int C = a.ncols;
+  for (int q0 = 0; q0 < C; q0 += kSlots)
+    merge_columns<kThreads>(a, smem, slot0, stride, n, dst, g, r, q0, min(kSlots, C - q0));
 }
 
 // Waits until every device-coherent store of the workgroup has completed
@@ -850,7 +882,14 @@ hipError_t launch_attend(const AttendArgs& a, AttendKind kind, int grid, hipStre
       fn = causal ? reinterpret_cast<const void*>(&attend_kernel<Bf16Kv, true>)
                   : reinterpret_cast<const void*>(&attend_kernel<Bf16Kv, false>);
   }
-  size_t lds = size_t(waves) * (32 + a.ncols * kRedRow) * sizeof(float);
+  // columns in blocks of at most 16 over an equal share of the waves each:
+  // the fewest blocks that divide the waves
+  int blocks = (a.ncols + 15) / 16;
+  if (!causal && blocks > 1) return hipErrorInvalidValue;
+  while (waves % blocks != 0) ++blocks;
+  copy.col_blocks = blocks;
+  copy.block_cols = (a.ncols + blocks - 1) / blocks;
+  size_t lds = size_t(waves) * (32 + copy.block_cols * kRedRow) * sizeof(float);
   const size_t merge_lds = size_t(merge_lds_floats(waves * 64)) * sizeof(float);
   if (a.fuse && merge_lds > lds) lds = merge_lds;
   if (grid <= 0) return hipSuccess;

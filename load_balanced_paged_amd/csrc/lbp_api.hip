@@ -34,7 +34,8 @@ lbp_status check_config(const lbp_config* c) {
   if (c->num_q_heads % c->num_kv_heads != 0) return LBP_ERR_INVALID_ARG;
   if (c->num_q_heads / c->num_kv_heads > kMaxGroup) return LBP_ERR_UNSUPPORTED;
   if (c->q_len < 0) return LBP_ERR_INVALID_ARG;
-  if (int64_t(c->num_q_heads / c->num_kv_heads) * (c->q_len > 1 ? c->q_len : 1) > kMaxGroup)
+  if (int64_t(c->num_q_heads / c->num_kv_heads) * (c->q_len > 1 ? c->q_len : 1) >
+      LBP_MAX_QUERY_COLUMNS)
     return LBP_ERR_UNSUPPORTED;
   if (c->max_batch < 1 || c->max_pages_per_seq < 1) return LBP_ERR_INVALID_ARG;
   if (c->num_workgroups < 0 || c->min_tiles_per_bin < 0) return LBP_ERR_INVALID_ARG;

@@ -101,7 +101,9 @@ def test_q_len_workspace(lib):
     _, _, sb1 = query(cfg())
     st, _, sb2 = query(cfg(q_len=2))
     assert st == lbp.LBP_OK and sb2 >= 2 * sb1 - 512      # twice the columns per slot
-    assert query(cfg(num_q_heads=8, num_kv_heads=8, q_len=16))[0] == lbp.LBP_OK
+    assert query(cfg(num_q_heads=8, num_kv_heads=8, q_len=64))[0] == lbp.LBP_OK
+    st, _, sb6 = query(cfg(q_len=6))                        # 48 columns: three blocks
+    assert st == lbp.LBP_OK and sb6 >= 6 * sb1 - 512
 
 
 def test_workspace_sizes(lib):
@@ -129,7 +131,8 @@ def test_workspace_sizes(lib):
     (dict(sm_scale=0.0), lbp.LBP_ERR_INVALID_ARG),
     (dict(sm_scale=float("nan")), lbp.LBP_ERR_INVALID_ARG),
     (dict(max_pages_per_seq=1 << 30), lbp.LBP_ERR_UNSUPPORTED),
-    (dict(q_len=3), lbp.LBP_ERR_UNSUPPORTED),                             # 8 * 3 > 16
+    (dict(q_len=9), lbp.LBP_ERR_UNSUPPORTED),                             # 8 * 9 > 64
+    (dict(num_q_heads=16, num_kv_heads=1, q_len=5), lbp.LBP_ERR_UNSUPPORTED),  # 80 > 64
     (dict(q_len=-1), lbp.LBP_ERR_INVALID_ARG),
 ])
 def test_config_guards(lib, kw, status):

@@ -2,7 +2,8 @@
 
 Token j of request r sits at position L_r - q_len + j and attends causally to
 the KV positions up to its own; the MFMA columns hold (token, head) pairs of
-the KV head's group, G * q_len <= 16.  Every case is compared with the fp64
+the KV head's group, G * q_len <= 64, in column blocks of at most 16 once
+there are more than 16.  Every case is compared with the fp64
 oracle (oracle.attention.paged_verify_attention) at the path's tolerance,
 through lbp_attend, lbp_attend_fused and (FP8) lbp_attend_fp8q, including
 tokens with no visible position (zeros) and descriptors in which a column
@@ -77,6 +78,32 @@ def test_verify_shapes_short_requests(gpu_lib, group, hkv, T):
     assert torch.all(out[0, :T - 1] == 0) if T > 1 else True
 
 
+@pytest.mark.parametrize("group,hkv,T", [(8, 2, 6), (8, 1, 8), (4, 2, 5), (16, 1, 4), (3, 3, 7)])
+def test_verify_column_blocks(gpu_lib, group, hkv, T):
+    """More than 16 query columns (up to 64): the workgroup's waves split
+    into column blocks that each walk every KV slice of a descriptor."""
+    wcfg = dataclasses.replace(CONFIGS["tiny"], name=f"vb{group}x{T}", batch=6,
+                               num_q_heads=group * hkv, num_kv_heads=hkv)
+    case = build_case(wcfg, lengths=[1, 5, 64, 200, 777, 2100], num_workgroups=9, min_tiles=1,
+                      q_len=T)
+    q = make_q(case, T, seed=6)
+    ref = oracle_verify_pairs(case, 0, all_pairs(case), q64_of(q))
+    out = run(case, q)
+    compare_verify(case, out, ref, f"verify blocks G={group} T={T}")
+    compare_verify(case, run(case, q, lbp.lbp_attend_fused), ref,
+                   f"verify blocks G={group} T={T} fused")
+    assert torch.all(out[0, :T - 1] == 0)
+
+
+def test_verify_six_rows_mixed_sampled(gpu_lib):
+    """Six verification rows per request at the 8-query-head group (48
+    columns), on the mixed-length workload."""
+    case = build_case(CONFIGS["mixed"], q_len=6)
+    q = make_q(case, 6, seed=7)
+    compare_verify(case, run(case, q), oracle_verify_pairs(case, 0, sample_pairs(case, 6),
+                                                           q64_of(q)), "verify mixed T=6")
+
+
 def test_verify_fully_masked_descriptor(gpu_lib):
     """L = 65 with one-tile bins: the descriptor [64, 65) is invisible to the
     first of two tokens, so its partial for those columns is empty."""
@@ -112,6 +139,26 @@ def test_verify_fp8_kv_and_query(gpu_lib):
     torch.cuda.synchronize()
     q8 = oracle.e4m3.dequantize(codes.cpu().numpy(), scale.cpu().numpy())
     compare_verify(case, out, oracle_verify_pairs(case, 0, pairs, q8), "verify fp8 q")
+
+
+def test_verify_fp8_column_blocks(gpu_lib):
+    """FP8 KV and FP8 query with 48 columns (three blocks of the 12 waves)."""
+    wcfg = dataclasses.replace(CONFIGS["fp8"], name="vb-fp8", batch=4)
+    case = build_case(wcfg, lengths=[3, 300, 4000, 9000], num_workgroups=20, q_len=6)
+    q = make_q(case, 6, seed=8)
+    pairs = all_pairs(case)
+    compare_verify(case, run(case, q), oracle_verify_pairs(case, 0, pairs, q64_of(q)),
+                   "verify blocks fp8 kv")
+    compare_verify(case, run(case, q, lbp.lbp_attend_fused),
+                   oracle_verify_pairs(case, 0, pairs, q64_of(q)), "verify blocks fp8 kv fused")
+    codes, scale = quantize_query_e4m3(q)
+    lay = case.wl.layers[0]
+    out = torch.full_like(q, float("nan"))
+    lbp.lbp_attend_fp8q(case.cfg, case.info, case.plan_ws, codes, scale, lay.k_cache,
+                        lay.v_cache, lay.k_scale, lay.v_scale, case.split_ws, out)
+    torch.cuda.synchronize()
+    q8 = oracle.e4m3.dequantize(codes.cpu().numpy(), scale.cpu().numpy())
+    compare_verify(case, out, oracle_verify_pairs(case, 0, pairs, q8), "verify blocks fp8 q")
 
 
 def test_verify_one_token_equals_decode(gpu_lib):
