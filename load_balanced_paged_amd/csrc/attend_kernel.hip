@@ -114,6 +114,15 @@ __device__ inline float load_coherent(const float* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Keeps the memory operations on either side in program order (an empty
+// asm statement that clobbers memory): where one code path would otherwise
+// issue a slice's loads in another order than the loop that waits for them,
+// the wait counts at the join fall back to the most conservative.
+template <bool kOrdered>
+__device__ inline void keep_order() {
+  if constexpr (kOrdered) asm volatile("" ::: "memory");
+}
+
 __device__ inline float wave_max_across_groups(float x) {
   x = fmaxf(x, __shfl_xor(x, 16, 64));
   x = fmaxf(x, __shfl_xor(x, 32, 64));
@@ -198,14 +207,19 @@ struct Bf16Kv {
   }
   __device__ static float score_scale(const Q&, float scale_log2) { return scale_log2; }
 
+  template <bool kOrdered = false>
   __device__ static void issue(Buf& b, const SliceRsrc& rs, int lane) {
     const int m = lane & 15, grp = lane >> 4;
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
+    for (int s = 0; s < 4; ++s) {
       b.k[s] = __builtin_amdgcn_raw_buffer_load_b128(rs.k, m * kRowBytes + 64 * s + 16 * grp, 0, kLoadAux);
+      keep_order<kOrdered>();
+    }
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i) {
       b.v[i] = __builtin_amdgcn_raw_buffer_load_b128(rs.v, (4 * grp + i) * kRowBytes + 16 * m, 0, kLoadAux);
+      keep_order<kOrdered>();
+    }
   }
 
   __device__ static f32x4_t scores(const Buf& b, const Q& q) {
@@ -262,15 +276,21 @@ struct Fp8Kv {
   }
   __device__ static float score_scale(const Q&, float scale_log2) { return scale_log2; }
 
+  template <bool kOrdered = false>
   __device__ static void issue(Buf& b, const SliceRsrc& rs, int lane) {
     const int m = lane & 15, grp = lane >> 4;
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int h = 0; h < 2; ++h) {
       b.k[h] = __builtin_amdgcn_raw_buffer_load_b128(rs.k, m * kRowBytes + 32 * grp + 16 * h, 0, kLoadAux);
+      keep_order<kOrdered>();
+    }
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i) {
       b.v[i] = __builtin_amdgcn_raw_buffer_load_b64(rs.v, (4 * grp + i) * kRowBytes + 8 * m, 0, kLoadAux);
+      keep_order<kOrdered>();
+    }
     b.ks = __builtin_amdgcn_raw_buffer_load_b128(rs.ks, 16 * grp, 0, 0);
+    keep_order<kOrdered>();
     b.vs = __builtin_amdgcn_raw_buffer_load_b128(rs.vs, 16 * grp, 0, 0);
   }
 
@@ -451,6 +471,38 @@ __device__ inline void consume(WaveState& st, const typename Kv::Buf& b, const t
   }
 }
 
+// Waves of the staged instance (column blocks, more than 16 query columns)
+// for every KV format: its LDS ring of 2 x waves slices must fit the CU.
+constexpr int kStagedWaves = 8;
+
+template <class Kv, bool kStaged>
+constexpr int waves_of() {
+  return kStaged ? kStagedWaves : Kv::kWaves;
+}
+
+// A slice's register image in LDS: vector v of lane l at [v][l], so each
+// 16-byte write or read of a wave covers 1 KB of consecutive LDS.
+template <class Kv>
+struct BufImage {
+  static constexpr int kVecs = sizeof(typename Kv::Buf) / 16;
+  static_assert(kVecs * 16 == sizeof(typename Kv::Buf), "Buf must be whole 16-byte vectors");
+  static constexpr int kBytes = kVecs * 64 * 16;   // one slice, one wave
+  struct Raw {
+    i32x4_t v[kVecs];
+  };
+  __device__ static void store(i32x4_t* dst, const typename Kv::Buf& b, int lane) {
+    const Raw r = __builtin_bit_cast(Raw, b);
+#pragma unroll
+    for (int v = 0; v < kVecs; ++v) dst[v * 64 + lane] = r.v[v];
+  }
+  __device__ static typename Kv::Buf load(const i32x4_t* src, int lane) {
+    Raw r;
+#pragma unroll
+    for (int v = 0; v < kVecs; ++v) r.v[v] = src[v * 64 + lane];
+    return __builtin_bit_cast(typename Kv::Buf, r);
+  }
+};
+
 // Drains one bin: every descriptor in it, in order.
 //
 // Slice i of a descriptor goes to wave i % kWaves; each wave keeps two
@@ -459,35 +511,43 @@ __device__ inline void consume(WaveState& st, const typename Kv::Buf& b, const t
 // d + 1 and d + 1's query group, before the cross-wave merge of d, so their
 // latency overlaps the merge and the wait for the slowest wave instead of
 // following them.
-template <class Kv, bool kCausal>
+//
+// Staged form (kStaged: multi-token verification with more than 16 query
+// columns): the columns split into nblk blocks of at most 16, one per group
+// of waves.  The descriptor is walked in rounds of one slice per wave:
+// every wave loads a different slice (two rounds in flight, as above),
+// copies it into a two-stage LDS ring once it has arrived, and after one
+// barrier per round computes, for its block's columns, its share of the
+// round's slices from LDS.  Every KV byte is then fetched once per
+// workgroup with the full set of loads in flight, while each wave keeps the
+// register state of a single 16-column tile.
+template <class Kv, bool kCausal, bool kStaged>
 __device__ inline void attend_bin(const AttendArgs& a, const int32_t* __restrict__ pt,
                                   const int4* __restrict__ descs,
                                   const int32_t* __restrict__ pair_count,
                                   const int32_t* __restrict__ bin_offset,
                                   const int4* __restrict__ bin_first,
                                   const int32_t* __restrict__ pair_first, float* smem, int bin) {
-  constexpr int kWaves = Kv::kWaves;
+  constexpr int kWaves = waves_of<Kv, kStaged>();
   constexpr int kThreads = kWaves * 64;
+  static_assert(kCausal || !kStaged, "the staged form serves verification only");
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15;         // MFMA column of this lane within its block
   const int grp = lane >> 4;
   const int G = a.group;
   const int C = a.ncols;           // G * q_len
-  // Column blocks (multi-token verification with more than 16 columns): the
-  // waves split into nblk equal groups, group b computes columns
-  // [b * cpb, b * cpb + cpb) over every slice of the descriptor, so each
-  // group reads the same KV slices (the repeats come from the CU's caches)
-  // and keeps the register footprint of one 16-column tile.  Plain decode
-  // has one block of all the waves.
-  const int nblk = kCausal ? a.col_blocks : 1;
-  const int wpb = kCausal ? kWaves / nblk : kWaves;    // waves per block
-  const int blk = kCausal ? wave / wpb : 0;
-  const int wslot = kCausal ? wave - blk * wpb : wave;  // the wave's place in its block
-  const int cpb = kCausal ? a.block_cols : C;          // columns per block, <= 16
+  // column blocks (staged form only): the waves split into nblk equal
+  // groups, group b computes columns [b * cpb, b * cpb + cpb); otherwise one
+  // block of all the waves and all C <= 16 columns
+  const int nblk = kStaged ? a.col_blocks : 1;
+  const int wpb = kStaged ? kWaves / nblk : kWaves;    // waves per block
+  const int blk = kStaged ? wave / wpb : 0;
+  const int wslot = kStaged ? wave - blk * wpb : wave;  // the wave's place in its block
+  const int cpb = kStaged ? a.block_cols : C;          // columns per block, <= 16
   const int col0 = blk * cpb;
-  const int nvalid = kCausal ? min(cpb, C - col0) : C; // this block's columns
-  const int step = wpb * kSlice;
+  const int nvalid = kStaged ? min(cpb, C - col0) : C; // this block's columns
+  constexpr int step = kWaves * kSlice;                // tokens per round / per wave stride
   const int red_stride = 32 + cpb * kRedRow;
   float* red = smem + wave * red_stride;
   // range and first descriptor are independent loads: one round trip
@@ -501,7 +561,8 @@ __device__ inline void attend_bin(const AttendArgs& a, const int32_t* __restrict
   typename Kv::Q qb;
   typename Kv::Buf buf[2];
   Kv::load_q(qb, a, ql, ds.x, ds.y, grp);
-  Kv::issue(buf[0], slice_rsrc<Kv>(a, pt, ds.x, ds.y, ds.z + wslot * kSlice, ds.w), lane);
+  Kv::template issue<kStaged>(buf[0], slice_rsrc<Kv>(a, pt, ds.x, ds.y, ds.z + wave * kSlice, ds.w),
+                              lane);
 
   for (int d = d_begin; d < d_end; ++d) {
     const int g = ds.x, r = ds.y, t_begin = ds.z, t_end = ds.w;
@@ -526,28 +587,71 @@ __device__ inline void attend_bin(const AttendArgs& a, const int32_t* __restrict
 
     // buf[0] already holds (or is loading) this wave's first slice of d; a
     // slice past t_end loads nothing
-    int tok = t_begin + wslot * kSlice;
-    bool more = tok < t_end;
-    while (more) {
+    if constexpr (kStaged) {
+      constexpr int kImg = BufImage<Kv>::kBytes;
+      i32x4_t* ring = reinterpret_cast<i32x4_t*>(smem);   // [2 stages][kWaves slices][image]
+      int base = t_begin;          // round: tokens [base, base + step), slice w at base + 16 w
+      Kv::template issue<true>(buf[1], slice_rsrc<Kv>(a, pt, g, r, base + step + wave * kSlice, t_end),
+                               lane);
+      // one round from ring stage u (buf[u] holds this wave's slice of it)
+      auto round = [&](const int u) {
+        i32x4_t* stage = ring + u * (kWaves * kImg / 16);
+        BufImage<Kv>::store(stage + wave * (kImg / 16), buf[u], lane);
+        Kv::template issue<true>(
+            buf[u], slice_rsrc<Kv>(a, pt, g, r, base + 2 * step + wave * kSlice, t_end), lane);
+        // the round's slices are in LDS; every wave is past the round that
+        // last used this stage
+        __syncthreads();
+        for (int j = wslot; j < kWaves; j += wpb) {
+          const int tok = base + j * kSlice;
+          if (tok >= t_end) break;
+          const typename Kv::Buf b = BufImage<Kv>::load(stage + j * (kImg / 16), lane);
+          consume<Kv, kCausal>(st, b, qb, tok, t_end, Kv::score_scale(qb, a.scale_log2), grp,
+                               lim);
+        }
+        base += step;
+      };
+      // rounds go in pairs (a second round past t_end loads and computes
+      // nothing): with a single exit, every path to the loop top has buf[0]
+      // as the older of the two loads in flight, so the waits stay exact
+      do {
+        round(0);
+        round(1);
+      } while (base < t_end);
+      // the merge below reuses the ring's LDS
+      __syncthreads();
+    } else {
+      int tok = t_begin + wave * kSlice;
+      bool more = tok < t_end;
+      while (more) {
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        Kv::issue(buf[u ^ 1], slice_rsrc<Kv>(a, pt, g, r, tok + step, t_end), lane);
-        consume<Kv, kCausal>(st, buf[u], qb, tok, t_end, Kv::score_scale(qb, a.scale_log2), grp,
-                             lim);
-        tok += step;
-        if (tok >= t_end) {
-          more = false;
-          break;
+        for (int u = 0; u < 2; ++u) {
+          Kv::issue(buf[u ^ 1], slice_rsrc<Kv>(a, pt, g, r, tok + step, t_end), lane);
+          consume<Kv, kCausal>(st, buf[u], qb, tok, t_end, Kv::score_scale(qb, a.scale_log2),
+                               grp, lim);
+          tok += step;
+          if (tok >= t_end) {
+            more = false;
+            break;
+          }
         }
       }
     }
-    if (has_next) {
-      // the query first: as the older load it is complete whenever the
-      // slice's first K row is, so the next descriptor's loop can wait for
-      // its loads one by one
+    // the next descriptor's query and first slice, the query first: as the
+    // older load it is complete whenever the slice's first K row is, so the
+    // next descriptor's loop can wait for its loads one by one.  The staged
+    // form issues them after the merge's stores instead, and always (past
+    // the bin's last descriptor, an empty token range that moves no data),
+    // so that its round loop is entered with exactly the loads outstanding
+    // that it loops with and the compiler's wait counts stay exact.
+    auto prefetch_next = [&]() {
+      const int first = has_next ? dn.z : dn.w;
       Kv::load_q(qb, a, ql, dn.x, dn.y, grp);
-      Kv::issue(buf[0], slice_rsrc<Kv>(a, pt, dn.x, dn.y, dn.z + wslot * kSlice, dn.w), lane);
-    }
+      Kv::template issue<kStaged>(buf[0],
+                                  slice_rsrc<Kv>(a, pt, dn.x, dn.y, first + wave * kSlice, dn.w),
+                                  lane);
+    };
+    if (!kStaged && has_next) prefetch_next();
 
     // merge the wave states of this descriptor
     st.l = wave_sum_across_groups(st.l);
@@ -569,7 +673,7 @@ __device__ inline void attend_bin(const AttendArgs& a, const int32_t* __restrict
     for (int idx = threadIdx.x; idx < C * kHeadDim; idx += kThreads) {
       const int q = idx >> 7, dim = idx & (kHeadDim - 1);
       // the waves of q's column block hold it, as their column qc
-      const int qb = kCausal ? q / cpb : 0;
+      const int qb = kStaged ? q / cpb : 0;
       const int qc = q - qb * cpb;
       const float* rb = smem + qb * wpb * red_stride;
       float M = -INFINITY;
@@ -608,6 +712,7 @@ __device__ inline void attend_bin(const AttendArgs& a, const int32_t* __restrict
       }
     }
     __syncthreads();
+    if (kStaged) prefetch_next();
     ds = dn;
   }
 }
@@ -788,12 +893,12 @@ __device__ void finish_split_pairs(const AttendArgs& a, const int4* __restrict__
 // on a faster CU simply drains more bins; every workgroup draws exactly one
 // ticket past the last bin, and the one holding the final ticket returns the
 // counter to zero for the next launch.
-template <class Kv, bool kCausal>
-__global__ __launch_bounds__(Kv::kWaves * 64) void attend_kernel(
+template <class Kv, bool kCausal, bool kStaged>
+__global__ __launch_bounds__((waves_of<Kv, kStaged>() * 64)) void attend_kernel(
     AttendArgs a, const int32_t* __restrict__ page_table, const int4* __restrict__ descs,
     const int32_t* __restrict__ pair_count, const int32_t* __restrict__ bin_offset,
     const int32_t* __restrict__ pair_first, const int4* __restrict__ bin_first) {
-  constexpr int kThreads = Kv::kWaves * 64;
+  constexpr int kThreads = waves_of<Kv, kStaged>() * 64;
   extern __shared__ __attribute__((aligned(16))) float smem[];   // f32x4 rows are stored in it
   __shared__ int ticket_lds;
   __shared__ int arrive_lds;
@@ -812,8 +917,8 @@ __global__ __launch_bounds__(Kv::kWaves * 64) void attend_kernel(
   };
   int bin = a.grab_counter ? next_bin() : int(blockIdx.x);
   while (bin < a.num_bins) {
-    attend_bin<Kv, kCausal>(a, page_table, descs, pair_count, bin_offset, bin_first, pair_first,
-                            smem, bin);
+    attend_bin<Kv, kCausal, kStaged>(a, page_table, descs, pair_count, bin_offset, bin_first,
+                                     pair_first, smem, bin);
     const int d_begin = bin_offset[bin], d_end = bin_offset[bin + 1];
     if (a.fuse)
       finish_split_pairs<kThreads>(a, descs, pair_count, pair_first, smem, &arrive_lds, d_begin,
@@ -862,34 +967,51 @@ hipError_t launch_attend(const AttendArgs& a, AttendKind kind, int grid, hipStre
   const int4* bf = reinterpret_cast<const int4*>(a.bin_first);
   void* args[] = {&copy, &pt, &descs, &pc, &bo, &pf, &bf};
   // multi-token verification (q_len > 1) runs the instances with the causal
-  // limit; plain decode keeps the loop without it
+  // limit, the staged one past 16 query columns; plain decode keeps the loop
+  // without either
   const bool causal = a.q_len > 1;
+  const bool staged = causal && a.ncols > 16;
+  if (!causal && a.ncols > 16) return hipErrorInvalidValue;
   int waves;
   const void* fn;
   switch (kind) {
     case kAttendFp8:
-      waves = Fp8Kv::kWaves;
-      fn = causal ? reinterpret_cast<const void*>(&attend_kernel<Fp8Kv, true>)
-                  : reinterpret_cast<const void*>(&attend_kernel<Fp8Kv, false>);
+      waves = staged ? waves_of<Fp8Kv, true>() : Fp8Kv::kWaves;
+      fn = staged   ? reinterpret_cast<const void*>(&attend_kernel<Fp8Kv, true, true>)
+           : causal ? reinterpret_cast<const void*>(&attend_kernel<Fp8Kv, true, false>)
+                    : reinterpret_cast<const void*>(&attend_kernel<Fp8Kv, false, false>);
       break;
     case kAttendFp8Q8:
-      waves = Fp8KvQ8::kWaves;
-      fn = causal ? reinterpret_cast<const void*>(&attend_kernel<Fp8KvQ8, true>)
-                  : reinterpret_cast<const void*>(&attend_kernel<Fp8KvQ8, false>);
+      waves = staged ? waves_of<Fp8KvQ8, true>() : Fp8KvQ8::kWaves;
+      fn = staged   ? reinterpret_cast<const void*>(&attend_kernel<Fp8KvQ8, true, true>)
+           : causal ? reinterpret_cast<const void*>(&attend_kernel<Fp8KvQ8, true, false>)
+                    : reinterpret_cast<const void*>(&attend_kernel<Fp8KvQ8, false, false>);
       break;
     default:
-      waves = Bf16Kv::kWaves;
-      fn = causal ? reinterpret_cast<const void*>(&attend_kernel<Bf16Kv, true>)
-                  : reinterpret_cast<const void*>(&attend_kernel<Bf16Kv, false>);
+      waves = staged ? waves_of<Bf16Kv, true>() : Bf16Kv::kWaves;
+      fn = staged   ? reinterpret_cast<const void*>(&attend_kernel<Bf16Kv, true, true>)
+           : causal ? reinterpret_cast<const void*>(&attend_kernel<Bf16Kv, true, false>)
+                    : reinterpret_cast<const void*>(&attend_kernel<Bf16Kv, false, false>);
   }
-  // columns in blocks of at most 16 over an equal share of the waves each:
-  // the fewest blocks that divide the waves
-  int blocks = (a.ncols + 15) / 16;
-  if (!causal && blocks > 1) return hipErrorInvalidValue;
-  while (waves % blocks != 0) ++blocks;
+  // staged: columns in blocks of at most 16 over an equal share of the
+  // waves each, the fewest blocks that divide the waves
+  int blocks = 1;
+  if (staged) {
+    blocks = (a.ncols + 15) / 16;
+    while (waves % blocks != 0) ++blocks;
+  }
   copy.col_blocks = blocks;
   copy.block_cols = (a.ncols + blocks - 1) / blocks;
   size_t lds = size_t(waves) * (32 + copy.block_cols * kRedRow) * sizeof(float);
+  if (staged) {
+    size_t ring;
+    switch (kind) {
+      case kAttendFp8: ring = 2 * size_t(waves) * BufImage<Fp8Kv>::kBytes; break;
+      case kAttendFp8Q8: ring = 2 * size_t(waves) * BufImage<Fp8KvQ8>::kBytes; break;
+      default: ring = 2 * size_t(waves) * BufImage<Bf16Kv>::kBytes;
+    }
+    if (ring > lds) lds = ring;
+  }
   const size_t merge_lds = size_t(merge_lds_floats(waves * 64)) * sizeof(float);
   if (a.fuse && merge_lds > lds) lds = merge_lds;
   if (grid <= 0) return hipSuccess;
