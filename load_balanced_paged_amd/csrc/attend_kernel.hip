@@ -123,15 +123,55 @@ __device__ inline void keep_order() {
   if constexpr (kOrdered) asm volatile("" ::: "memory");
 }
 
-__device__ inline float wave_max_across_groups(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16, 64));
-  x = fmaxf(x, __shfl_xor(x, 32, 64));
-  return x;
+// The four lane groups (lanes n, n + 16, n + 32, n + 48) hold one MFMA
+// column.  Their reductions use gfx950's lane swaps instead of a trip
+// through the LDS crossbar: swapping a value with a copy of itself across
+// the wave's halves (then across neighbouring 16-lane rows) leaves lane l's
+// partner l ^ 32 (then l ^ 16) in the pair, in the same order on both
+// partners, so all four lanes of a column end with the same result.  Each
+// swap is one asm statement (copy, the required wait states, swap) with both
+// results as outputs: through the builtin the compiler has merged the two
+// results of a swap into one register.
+__device__ inline void partners32(float x, float& lo, float& hi) {
+  float a = x, b;
+  asm("v_mov_b32 %1, %0\n\ts_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1"
+      : "+v"(a), "=&v"(b));
+  lo = a;   // the value of lane l & 31
+  hi = b;   // the value of lane (l & 31) + 32
 }
+__device__ inline void partners16(float x, float& lo, float& hi) {
+  float a = x, b;
+  asm("v_mov_b32 %1, %0\n\ts_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1"
+      : "+v"(a), "=&v"(b));
+  lo = a;   // the value of lane l & ~16
+  hi = b;   // the value of lane l | 16
+}
+// kSwap: the lane swaps above, else cross-lane shuffles through the LDS
+// crossbar (measured faster for the FP8 decode formats, whose loop has no
+// registers to spare at three waves per SIMD).
+template <bool kSwap>
+__device__ inline float wave_max_across_groups(float x) {
+  if constexpr (kSwap) {
+    float a, b;
+    partners32(x, a, b);
+    partners16(fmaxf(a, b), a, b);
+    return fmaxf(a, b);
+  } else {
+    x = fmaxf(x, __shfl_xor(x, 16, 64));
+    return fmaxf(x, __shfl_xor(x, 32, 64));
+  }
+}
+template <bool kSwap>
 __device__ inline float wave_sum_across_groups(float x) {
-  x += __shfl_xor(x, 16, 64);
-  x += __shfl_xor(x, 32, 64);
-  return x;
+  if constexpr (kSwap) {
+    float a, b;
+    partners32(x, a, b);
+    partners16(a + b, a, b);
+    return a + b;
+  } else {
+    x += __shfl_xor(x, 16, 64);
+    return x + __shfl_xor(x, 32, 64);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -192,6 +232,7 @@ struct Bf16Kv {
   static constexpr bool kScaled = false;
   static constexpr bool kSplitP = LBP_BF16_SPLIT_P;   // P.V with P as BF16 hi + lo
   static constexpr int kWaves = LBP_BF16_WAVES;    // waves per workgroup
+  static constexpr bool kLaneSwap = true;          // column reductions by lane swaps
   struct Buf {
     i32x4_t k[4];   // K A-operand, one per 32-dim k-step
     i32x4_t v[4];   // V rows 4*grp+i, dims [8c, 8c+8)
@@ -222,7 +263,9 @@ struct Bf16Kv {
     }
   }
 
-  __device__ static f32x4_t scores(const Buf& b, const Q& q) {
+  // (B: any slice type holding the K operand as member k)
+  template <class B>
+  __device__ static f32x4_t scores(const B& b, const Q& q) {
     f32x4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int k = 0; k < 4; ++k)
@@ -256,6 +299,7 @@ struct Fp8Kv {
   // the FP8 tolerance leaves room for P in plain BF16, and this format needs
   // its issue slots for the code widening
   static constexpr bool kSplitP = false;
+  static constexpr bool kLaneSwap = false;
   // FP8 moves half the bytes per token for the same MFMA and softmax work, so
   // it needs more waves in flight per CU (three per SIMD) to stay on HBM.
   static constexpr int kWaves = LBP_FP8_WAVES;
@@ -301,7 +345,8 @@ struct Fp8Kv {
                               __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(int(codes), 1.0f, kHiWord));
   }
 
-  __device__ static f32x4_t scores(const Buf& b, const Q& q) {
+  template <class B>
+  __device__ static f32x4_t scores(const B& b, const Q& q) {
     f32x4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -364,13 +409,62 @@ struct Fp8KvQ8 : Fp8Kv {
     typedef long i64x2_t __attribute__((ext_vector_type(2)));
     return __builtin_bit_cast(i64x2_t, c[k >> 1])[k & 1];
   }
-  __device__ static f32x4_t scores(const Buf& b, const Q& q) {
+  template <class B>
+  __device__ static f32x4_t scores(const B& b, const Q& q) {
     f32x4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int k = 0; k < 4; ++k)
       s = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(codes8(b.k, k), codes8(q.c, k), s, 0, 0, 0);
     return s;
   }
+};
+
+// A slice as the staged instance keeps it in LDS: the K operand as loaded,
+// the eight P.V A operands already built (for FP8: already widened), and the
+// FP8 scales.  The wave that loads a slice builds this once; every column
+// block then reads it ready for the MFMAs.  128 bytes per lane in every
+// format.
+template <class Kv, bool kScaled = Kv::kScaled>
+struct StagedSlice {
+  decltype(Kv::Buf::k) k;
+  i16x4_t v[8];
+};
+template <class Kv>
+struct StagedSlice<Kv, true> {
+  decltype(Kv::Buf::k) k;
+  i16x4_t v[8];
+  i32x4_t ks, vs;
+};
+
+template <class Kv>
+struct Staged {
+  using Buf = StagedSlice<Kv>;
+  using Q = typename Kv::Q;
+  static constexpr bool kSplitP = Kv::kSplitP;
+  static constexpr bool kLaneSwap = true;
+  static constexpr bool kScaled = Kv::kScaled;
+  __device__ static Buf build(const typename Kv::Buf& b) {
+    Buf t;
+#pragma unroll
+    for (int i = 0; i < int(sizeof(t.k) / sizeof(t.k[0])); ++i) t.k[i] = b.k[i];
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) t.v[mb] = Kv::v_operand(b, mb);
+    if constexpr (kScaled) {
+      t.ks = b.ks;
+      t.vs = b.vs;
+    }
+    return t;
+  }
+  __device__ static f32x4_t scores(const Buf& b, const Q& q) { return Kv::scores(b, q); }
+  __device__ static f32x4_t k_scales(const Buf& b) {
+    if constexpr (kScaled) return __builtin_bit_cast(f32x4_t, b.ks);
+    else return f32x4_t{1.f, 1.f, 1.f, 1.f};
+  }
+  __device__ static f32x4_t v_scales(const Buf& b) {
+    if constexpr (kScaled) return __builtin_bit_cast(f32x4_t, b.vs);
+    else return f32x4_t{1.f, 1.f, 1.f, 1.f};
+  }
+  __device__ static i16x4_t v_operand(const Buf& b, int mb) { return b.v[mb]; }
 };
 
 // ---------------------------------------------------------------------------
@@ -412,8 +506,11 @@ struct WaveState {
 
 // lim: this lane's column sees tokens < lim (its causal limit in
 // multi-token verification, kCausal only).  A column with no visible token
-// so far keeps an empty state (m = -inf, l = 0, acc = 0).
-template <class Kv, bool kCausal>
+// so far keeps an empty state (m = -inf, l = 0, acc = 0).  Kv: the slice
+// format (a KV format, or its staged form).  kLazy: skip the rescale of the
+// running state when no lane's maximum grew; its factor would be exactly 1,
+// so the result is the same bit for bit.
+template <class Kv, bool kCausal, bool kLazy = false>
 __device__ inline void consume(WaveState& st, const typename Kv::Buf& b, const typename Kv::Q& q,
                                int tok, int e, float scale_log2, int grp, int lim) {
   f32x4_t s = Kv::scores(b, q);
@@ -425,16 +522,21 @@ __device__ inline void consume(WaveState& st, const typename Kv::Buf& b, const t
     x[j] = (tok + 4 * grp + j < (kCausal ? min(e, lim) : e)) ? s[j] * ks[j] * scale_log2
                                                              : -INFINITY;
   float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-  mx = wave_max_across_groups(mx);
+  mx = wave_max_across_groups<Kv::kLaneSwap>(mx);
   const float m_new = fmaxf(st.m, mx);
   // without a causal limit every slice has a visible token in every column,
   // so the running max is finite after the first one
   const float ref = kCausal ? finite_or_zero(m_new) : m_new;
-  const float alpha = __builtin_amdgcn_exp2f(st.m - ref);
-  st.m = m_new;
-  st.l *= alpha;
+  if (!kLazy || __ballot(m_new > st.m) != 0) {
+    // (an opaque statement keeps the skip a branch instead of a select
+    // folded into the multiplies, which would do the work anyway)
+    if constexpr (kLazy) asm volatile("");
+    const float alpha = __builtin_amdgcn_exp2f(st.m - ref);
+    st.l *= alpha;
 #pragma unroll
-  for (int mb = 0; mb < 8; ++mb) st.acc[mb] *= alpha;
+    for (int mb = 0; mb < 8; ++mb) st.acc[mb] *= alpha;
+  }
+  st.m = m_new;
   float p[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) p[j] = __builtin_amdgcn_exp2f(x[j] - ref);
@@ -480,8 +582,9 @@ constexpr int waves_of() {
   return kStaged ? kStagedWaves : Kv::kWaves;
 }
 
-// A slice's register image in LDS: vector v of lane l at [v][l], so each
-// 16-byte write or read of a wave covers 1 KB of consecutive LDS.
+// A slice's register image in LDS (Kv: a slice format with member type
+// Buf): vector v of lane l at [v][l], so each 16-byte write or read of a
+// wave covers 1 KB of consecutive LDS.
 template <class Kv>
 struct BufImage {
   static constexpr int kVecs = sizeof(typename Kv::Buf) / 16;
@@ -588,7 +691,8 @@ __device__ inline void attend_bin(const AttendArgs& a, const int32_t* __restrict
     // buf[0] already holds (or is loading) this wave's first slice of d; a
     // slice past t_end loads nothing
     if constexpr (kStaged) {
-      constexpr int kImg = BufImage<Kv>::kBytes;
+      using S = Staged<Kv>;
+      constexpr int kImg = BufImage<S>::kBytes;
       i32x4_t* ring = reinterpret_cast<i32x4_t*>(smem);   // [2 stages][kWaves slices][image]
       int base = t_begin;          // round: tokens [base, base + step), slice w at base + 16 w
       Kv::template issue<true>(buf[1], slice_rsrc<Kv>(a, pt, g, r, base + step + wave * kSlice, t_end),
@@ -596,7 +700,7 @@ __device__ inline void attend_bin(const AttendArgs& a, const int32_t* __restrict
       // one round from ring stage u (buf[u] holds this wave's slice of it)
       auto round = [&](const int u) {
         i32x4_t* stage = ring + u * (kWaves * kImg / 16);
-        BufImage<Kv>::store(stage + wave * (kImg / 16), buf[u], lane);
+        BufImage<S>::store(stage + wave * (kImg / 16), S::build(buf[u]), lane);
         Kv::template issue<true>(
             buf[u], slice_rsrc<Kv>(a, pt, g, r, base + 2 * step + wave * kSlice, t_end), lane);
         // the round's slices are in LDS; every wave is past the round that
@@ -605,9 +709,9 @@ __device__ inline void attend_bin(const AttendArgs& a, const int32_t* __restrict
         for (int j = wslot; j < kWaves; j += wpb) {
           const int tok = base + j * kSlice;
           if (tok >= t_end) break;
-          const typename Kv::Buf b = BufImage<Kv>::load(stage + j * (kImg / 16), lane);
-          consume<Kv, kCausal>(st, b, qb, tok, t_end, Kv::score_scale(qb, a.scale_log2), grp,
-                               lim);
+          const typename S::Buf b = BufImage<S>::load(stage + j * (kImg / 16), lane);
+          consume<S, kCausal, true>(st, b, qb, tok, t_end, Kv::score_scale(qb, a.scale_log2),
+                                    grp, lim);
         }
         base += step;
       };
@@ -654,7 +758,7 @@ __device__ inline void attend_bin(const AttendArgs& a, const int32_t* __restrict
     if (!kStaged && has_next) prefetch_next();
 
     // merge the wave states of this descriptor
-    st.l = wave_sum_across_groups(st.l);
+    st.l = wave_sum_across_groups<kStaged || Kv::kLaneSwap>(st.l);
     if (n < nvalid) {
       if (grp == 0) {
         red[n] = st.m;
@@ -1006,9 +1110,9 @@ hipError_t launch_attend(const AttendArgs& a, AttendKind kind, int grid, hipStre
   if (staged) {
     size_t ring;
     switch (kind) {
-      case kAttendFp8: ring = 2 * size_t(waves) * BufImage<Fp8Kv>::kBytes; break;
-      case kAttendFp8Q8: ring = 2 * size_t(waves) * BufImage<Fp8KvQ8>::kBytes; break;
-      default: ring = 2 * size_t(waves) * BufImage<Bf16Kv>::kBytes;
+      case kAttendFp8: ring = 2 * size_t(waves) * BufImage<Staged<Fp8Kv>>::kBytes; break;
+      case kAttendFp8Q8: ring = 2 * size_t(waves) * BufImage<Staged<Fp8KvQ8>>::kBytes; break;
+      default: ring = 2 * size_t(waves) * BufImage<Staged<Bf16Kv>>::kBytes;
     }
     if (ring > lds) lds = ring;
   }
