@@ -17,7 +17,8 @@ import torch
 
 import load_balanced_paged_amd as lbp
 import oracle
-from gpu_support import all_pairs, build_case, compare, oracle_pairs, say
+from gpu_support import (all_pairs, bits, build_case, compare, compare_verify, oracle_pairs,
+                         oracle_verify_pairs, say)
 from workloads import CONFIGS, make_prologue_inputs, rope_cos_sin_table
 
 pytestmark = pytest.mark.gpu
@@ -62,10 +63,15 @@ def check_fp8(codes: np.ndarray, scale: np.ndarray, exact: np.ndarray, what: str
     say(f"[prologue] {what}: {exact.size} codes, {int(bad.sum())} at a midpoint")
 
 
-def run_case(wcfg, lengths=None, q_fp8=None, seed=0, max_position=None, override=None):
+def run_case(wcfg, lengths=None, q_fp8=None, seed=0, max_position=None, override=None,
+             q_len=1, qkv_scale=1.0):
     """override: {request: length} applied to the device lengths after the plan
-    (e.g. a length past the page table's capacity, which the plan would clamp)."""
-    case = build_case(wcfg, lengths=lengths, poison=False)
+    (e.g. a length past the page table's capacity, which the plan would clamp).
+    q_len: new tokens per request (token j of request r at position
+    L_r - q_len + j); outputs keep the [B, q_len, ...] layout for q_len > 1.
+    qkv_scale: a power of two applied to the projection (exact in BF16)."""
+    T = q_len
+    case = build_case(wcfg, lengths=lengths, poison=False, q_len=T)
     B = len(case.wl.lengths)
     L = np.asarray(case.wl.lengths).copy()
     for r, v in (override or {}).items():
@@ -74,15 +80,19 @@ def run_case(wcfg, lengths=None, q_fp8=None, seed=0, max_position=None, override
     Hq, Hkv = wcfg.num_q_heads, wcfg.num_kv_heads
     fp8_kv = wcfg.kv_dtype == "fp8_e4m3"
     q_fp8 = fp8_kv if q_fp8 is None else q_fp8
-    qkv, qw, kw = make_prologue_inputs(B, Hq, Hkv, seed, device="cuda")
+    qkv, qw, kw = make_prologue_inputs(B * T, Hq, Hkv, seed, device="cuda")
+    qkv = qkv * qkv_scale
+    qkv = qkv.view(B, T, -1) if T > 1 else qkv
     maxpos = max_position or int(max(L.max(), 1))
     cs = rope_cos_sin_table(maxpos, device="cuda")
     lay = case.wl.layers[0]
     k0, v0 = lay.k_cache.clone(), lay.v_cache.clone()
     ks0 = lay.k_scale.clone() if fp8_kv else None
     vs0 = lay.v_scale.clone() if fp8_kv else None
-    q_out = torch.empty((B, Hq, 128), dtype=torch.uint8 if q_fp8 else torch.bfloat16, device="cuda")
-    q_scale = torch.empty((B, Hq), dtype=torch.float32, device="cuda") if q_fp8 else None
+    lead = (B, T) if T > 1 else (B,)
+    q_out = torch.empty(lead + (Hq, 128), dtype=torch.uint8 if q_fp8 else torch.bfloat16,
+                        device="cuda")
+    q_scale = torch.empty(lead + (Hq,), dtype=torch.float32, device="cuda") if q_fp8 else None
     lbp.lbp_prologue(case.cfg, qkv, case.seq_lens, case.page_table, qw, kw, cs, q_out,
                      lay.k_cache, lay.v_cache, lay.k_scale, lay.v_scale, q_scale, EPS)
     torch.cuda.synchronize()
@@ -99,21 +109,25 @@ def run_case(wcfg, lengths=None, q_fp8=None, seed=0, max_position=None, override
     cap = 64 * case.cfg.max_pages_per_seq
     table = case.page_table.cpu().numpy()
     changed = np.zeros(lay.k_cache.shape[:3], dtype=bool)
-    rows_k, rows_v, gk, gv, sk, sv = [], [], [], [], [], []
+    pos = ref["pos"].reshape(B, T)
+    rk = ref["k"].reshape(B, T, Hkv, 128)
+    rv = ref["v"].reshape(B, T, Hkv, 128)
+    rows_k, rows_v, gk = [], [], []
     for r in range(B):
-        p = int(ref["pos"][r])
-        if p < 0 or p >= cap:
-            continue
-        page = int(table[r, p // 64])
-        changed[page, :, p % 64] = True
-        rows_k.append(ref["k"][r])
-        rows_v.append(ref["v"][r])
-        gk.append((page, p % 64))
+        for j in range(T):
+            p = int(pos[r, j])
+            if p < 0 or p >= cap:
+                continue
+            page = int(table[r, p // 64])
+            changed[page, :, p % 64] = True
+            rows_k.append(rk[r, j])
+            rows_v.append(rv[r, j])
+            gk.append((page, p % 64))
     kc, vc = lay.k_cache.cpu(), lay.v_cache.cpu()
     conv = (lambda t: t.numpy()) if fp8_kv else (lambda t: t.double().numpy())
-    got_k = np.stack([conv(kc[pg, :, sl]) for pg, sl in gk]) if gk else None
-    got_v = np.stack([conv(vc[pg, :, sl]) for pg, sl in gk]) if gk else None
     if gk:
+        got_k = np.stack([conv(kc[pg, :, sl]) for pg, sl in gk])
+        got_v = np.stack([conv(vc[pg, :, sl]) for pg, sl in gk])
         ek, ev = np.stack(rows_k), np.stack(rows_v)
         if fp8_kv:
             ksc = np.stack([lay.k_scale[pg, :, sl].cpu().numpy() for pg, sl in gk])
@@ -176,3 +190,32 @@ def test_prologue_then_attention(gpu_lib):
     torch.cuda.synchronize()
     q64 = oracle.e4m3.dequantize(q_out.cpu().numpy(), q_scale.cpu().numpy())
     compare(case, out, oracle_pairs(case, 0, all_pairs(case), q64), "prologue + attention")
+
+
+@pytest.mark.parametrize("T,fp8", [(3, False), (6, True)])
+def test_prologue_multi_token(gpu_lib, T, fp8):
+    """q_len new tokens per request (speculative verification): every token's
+    query, K and V, including requests shorter than q_len (tokens before the
+    sequence start write nothing) and tokens that straddle a page boundary."""
+    base = CONFIGS["fp8"] if fp8 else CONFIGS["tiny"]
+    wcfg = dataclasses.replace(base, name=f"pro-t{T}", batch=6)
+    run_case(wcfg, lengths=[1, 2, 65, 66, 700, 3000], seed=6 + T, q_len=T)
+
+
+def test_prologue_then_verify(gpu_lib):
+    """Prologue for four new tokens, then verification attention over the cache
+    it wrote, against the oracle on that cache and query.  The projection is
+    halved so that V has the unit spread of the attention workloads, whose
+    absolute tolerance this comparison uses."""
+    wcfg = dataclasses.replace(CONFIGS["tiny"], name="pro-verify", batch=5)
+    T = 4
+    case, q_out, _ = run_case(wcfg, lengths=[2, 64, 67, 700, 3000], seed=11, q_len=T,
+                              qkv_scale=0.5)
+    lay = case.wl.layers[0]
+    out = torch.full_like(q_out, float("nan"))
+    lbp.lbp_attend(case.cfg, case.info, case.plan_ws, q_out, lay.k_cache, lay.v_cache, None,
+                   None, case.split_ws, out)
+    torch.cuda.synchronize()
+    q64 = oracle.attention.bf16_bits_to_f64(bits(q_out))
+    compare_verify(case, out, oracle_verify_pairs(case, 0, all_pairs(case), q64),
+                   "prologue + verification")

@@ -161,6 +161,71 @@ def test_verify_fp8_column_blocks(gpu_lib):
     compare_verify(case, out, oracle_verify_pairs(case, 0, pairs, q8), "verify blocks fp8 q")
 
 
+@pytest.mark.parametrize("T", [2, 6])
+def test_verify_ticket_mode(gpu_lib, T):
+    """More bins than CUs: workgroups take bins from the ticket counter, in
+    the causal (T = 2) and staged (T = 6) instances, both merge forms."""
+    wcfg = dataclasses.replace(CONFIGS["tiny"], name=f"v-ticket{T}", batch=4)
+    case = build_case(wcfg, lengths=[3000, 50, 700, 9000], num_workgroups=1024, min_tiles=1,
+                      q_len=T)
+    q = make_q(case, T, seed=9)
+    ref = oracle_verify_pairs(case, 0, all_pairs(case), q64_of(q))
+    compare_verify(case, run(case, q), ref, f"verify ticket T={T}")
+    compare_verify(case, run(case, q, lbp.lbp_attend_fused), ref, f"verify ticket T={T} fused")
+
+
+def test_verify_zero_length_requests(gpu_lib):
+    """A request with no tokens outputs zero rows for every query token."""
+    wcfg = dataclasses.replace(CONFIGS["tiny"], name="v-zero", batch=4)
+    case = build_case(wcfg, lengths=[0, 5, 0, 300], num_workgroups=3, min_tiles=1, q_len=4)
+    q = make_q(case, 4, seed=10)
+    out = run(case, q)
+    assert torch.all(out[0] == 0) and torch.all(out[2] == 0)
+    compare_verify(case, out, oracle_verify_pairs(case, 0, all_pairs(case), q64_of(q)),
+                   "verify zero lengths")
+
+
+def test_verify_fused_two_levels_blocks(gpu_lib):
+    """A pair of more than 256 partials at 48 columns: the in-kernel merge runs
+    both levels in column chunks."""
+    wcfg = dataclasses.replace(CONFIGS["tiny"], name="v-two-level", batch=2)
+    case = build_case(wcfg, lengths=[20000, 100], num_workgroups=1024, min_tiles=1, q_len=6)
+    tm = lbp.read_taskmap(case.plan_ws, case.info)
+    assert tm["pair_count"].max() > 256
+    q = make_q(case, 6, seed=11)
+    ref = oracle_verify_pairs(case, 0, all_pairs(case), q64_of(q))
+    compare_verify(case, run(case, q, lbp.lbp_attend_fused), ref, "verify two-level fused")
+    compare_verify(case, run(case, q), ref, "verify two-level two launches")
+
+
+def test_verify_graph_replay_matches_eager(gpu_lib):
+    """Plan and staged fused verification captured in a HIP graph: every
+    replay equals eager, bit for bit."""
+    T = 6
+    wcfg = dataclasses.replace(CONFIGS["tiny"], name="v-graph", batch=4)
+    case = build_case(wcfg, lengths=[3000, 50, 700, 9000], num_workgroups=64, min_tiles=1,
+                      q_len=T)
+    q = make_q(case, T, seed=12)
+    eager = run(case, q, lbp.lbp_attend_fused).clone()
+    out = torch.zeros_like(eager)
+    lay = case.wl.layers[0]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            lbp.lbp_plan(case.cfg, case.seq_lens, case.page_table, case.plan_ws, stream=s)
+            lbp.lbp_attend_fused(case.cfg, case.info, case.plan_ws, q, lay.k_cache, lay.v_cache,
+                                 None, None, case.split_ws, out, stream=s)
+    torch.cuda.current_stream().wait_stream(s)
+    for rep in range(4):
+        out.zero_()
+        run(case, q)                       # unrelated eager work between replays
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), rep
+
+
 def test_verify_one_token_equals_decode(gpu_lib):
     """q_len = 1 in the [B, 1, Hq, D] layout is bit-identical to plain decode."""
     case = build_case(CONFIGS["skewed"])
