@@ -327,6 +327,38 @@ class Bench:
 
 
 # ---------------------------------------------------------------------------
+# read-stream reference
+# ---------------------------------------------------------------------------
+
+def read_stream_reference(lbp, gib=4, reps=5):
+    """This GPU's attainable HBM read rate for streaming traffic: the library's
+    read-stream kernel over a `gib` GiB buffer, best over a few grid sizes
+    (HIP events around `reps` launches each)."""
+    n = gib << 30
+    buf = torch.empty(n, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    sink = torch.empty(1 << 16, dtype=torch.int32, device="cuda")
+    best, best_blocks = 0.0, 0
+    for blocks in (2048, 4096, 8192, 16384):
+        lbp.lbp_read_stream(buf, sink, blocks)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            lbp.lbp_read_stream(buf, sink, blocks)
+        e1.record()
+        torch.cuda.synchronize()
+        gbs = reps * n / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        if gbs > best:
+            best, best_blocks = gbs, blocks
+    del buf, sink
+    torch.cuda.empty_cache()
+    log(f"read stream: {best:.0f} GB/s ({gib} GiB, {best_blocks} workgroups)")
+    return {"gbs": round(best, 1), "bytes": n, "workgroups": best_blocks,
+            "kernel": "read_stream_kernel", "pct_of_hbm_peak": round(100 * best / HBM_PEAK_GBS, 1)}
+
+
+# ---------------------------------------------------------------------------
 # CPU oracle baseline
 # ---------------------------------------------------------------------------
 
@@ -406,7 +438,7 @@ def traffic_record(kv_dtype):
     return entry.get("hbm_bytes_per_launch")
 
 
-def bench_one(name, lbp, args, headline):
+def bench_one(name, lbp, args, headline, stream_gbs=None):
     b = Bench(name, lbp)
     res = {"workload": name}
     info, _, _ = b.plan()
@@ -417,6 +449,7 @@ def bench_one(name, lbp, args, headline):
     gbs = b.wl.kv_bytes / (us * 1e-6) / 1e9
     res.update(us_per_step=round(us, 2), kv_gbs=round(gbs, 1),
                pct_of_hbm_peak=round(100 * gbs / HBM_PEAK_GBS, 1), timing=mode,
+               pct_of_read_stream=round(100 * gbs / stream_gbs, 1) if stream_gbs else None,
                kv_bytes_per_layer=b.wl.kv_bytes, total_tokens=b.wl.total_tokens,
                workgroups=info.num_bins, layers=b.layers)
     if not args.no_fused:
@@ -464,7 +497,9 @@ def bench_one(name, lbp, args, headline):
                        "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                        "traffic": traffic, "kernel": ATTEND_KERNEL[b.wcfg.kv_dtype],
                        "algorithmic_bytes_per_launch": b.wl.kv_bytes,
-                       "avg_kernel_us": round(k_mean, 2)}
+                       "avg_kernel_us": round(k_mean, 2),
+                       "read_stream_gbs": stream_gbs,
+                       "frac_of_read_stream": round(achieved / stream_gbs, 4) if stream_gbs else None}
     log(f"{name}: {us:.1f} us/step ({mode}), {gbs:.0f} GB/s KV, kernel {k_mean:.1f} us "
         f"({achieved:.0f} GB/s), plan {res['plan_us']:.1f} us")
     b.free()
@@ -553,7 +588,9 @@ def main():
         log(f"copy calibration: {n} bytes read + {n} bytes written")
         del src, dst
 
-    results = [bench_one(n, lbp, args, headline=(i == 0)) for i, n in enumerate(names)]
+    stream = read_stream_reference(lbp)
+    results = [bench_one(n, lbp, args, headline=(i == 0), stream_gbs=stream["gbs"])
+               for i, n in enumerate(names)]
     head = results[0]
     wcfg = __import__("workloads").CONFIGS[names[0]]
     out = {
@@ -567,6 +604,8 @@ def main():
         "ms_per_step": round(head["us_per_step"] / 1e3, 5),
         "us_per_step": head["us_per_step"],
         "pct_of_hbm_peak": head["pct_of_hbm_peak"],
+        "pct_of_read_stream": head["pct_of_read_stream"],
+        "read_stream": stream,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -332,6 +332,17 @@ lbp_status lbp_combine(const lbp_config* cfg, const lbp_plan_info* info,
                        const void* plan_ws_dev, const void* split_ws_dev,
                        size_t split_ws_bytes, void* out_dev, void* stream);
 
+/* Measurement reference, not part of the attention method: reads `bytes`
+ * of device memory at buf_dev once (non-temporal 16-byte loads, workgroup b
+ * reading the b-th of `blocks` contiguous chunks) and writes one XOR
+ * digest per workgroup to sink_dev[blocks] (int32, caller-owned), so that
+ * a timed launch gives this GPU's attainable HBM read rate for streaming
+ * traffic like the KV reads of lbp_attend.  buf_dev must be 16-byte aligned
+ * and bytes a multiple of 16 (else LBP_ERR_INVALID_ARG); blocks >= 1.
+ * Asynchronous on `stream`; LBP_ERR_HIP if the launch is refused. */
+lbp_status lbp_read_stream(const void* buf_dev, size_t bytes, int32_t* sink_dev, int32_t blocks,
+                           void* stream);
+
 #ifdef __cplusplus
 }
 #endif

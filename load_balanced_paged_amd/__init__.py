@@ -39,7 +39,7 @@ EXPORTED_SYMBOLS = (
     "lbp_status_string", "lbp_version", "lbp_query_workspace", "lbp_plan", "lbp_plan_static",
     "lbp_plan_layout", "lbp_attend", "lbp_attend_fused", "lbp_attend_partials",
     "lbp_attend_traced", "lbp_attend_fp8q", "lbp_prologue",
-    "lbp_combine",
+    "lbp_combine", "lbp_read_stream",
 )
 
 
@@ -143,6 +143,7 @@ def load(path: str = LIB_PATH):
         "lbp_attend_fp8q": (I32, [cfgp, infop, P, P, P, P, P, P, P, P, SZ, P, P]),
         "lbp_prologue": (I32, [cfgp, I32, ctypes.POINTER(lbp_prologue_args), P]),
         "lbp_combine": (I32, [cfgp, infop, P, P, SZ, P, P]),
+        "lbp_read_stream": (I32, [P, SZ, P, I32, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -353,6 +354,17 @@ def lbp_combine(cfg, info, plan_ws, split_ws, out, stream=None):
                               _ptr(split_ws, "split_ws"),
                               split_ws.numel() * split_ws.element_size(),
                               _ptr(out, "out", torch.bfloat16), _stream(stream)), "lbp_combine")
+
+
+def lbp_read_stream(buf, sink, blocks, stream=None):
+    """Measurement reference (not the method): read every byte of `buf` once
+    with `blocks` workgroups; sink is an int32 tensor of at least `blocks`."""
+    import torch
+    if sink.numel() < blocks:
+        raise ValueError("sink needs one int32 per workgroup")
+    _check(load().lbp_read_stream(_ptr(buf, "buf"), buf.numel() * buf.element_size(),
+                                  _ptr(sink, "sink", torch.int32), int(blocks), _stream(stream)),
+           "lbp_read_stream")
 
 
 # ---------------------------------------------------------------------------

@@ -441,4 +441,14 @@ lbp_status lbp_prologue(const lbp_config* cfg, int32_t batch, const lbp_prologue
   return LBP_OK;
 }
 
+lbp_status lbp_read_stream(const void* buf_dev, size_t bytes, int32_t* sink_dev, int32_t blocks,
+                           void* stream) {
+  if (!buf_dev || !sink_dev || blocks < 1 || bytes % 16 != 0) return LBP_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(buf_dev) % 16 != 0) return LBP_ERR_INVALID_ARG;
+  if (launch_read_stream(buf_dev, int64_t(bytes / 16), sink_dev, blocks,
+                         static_cast<hipStream_t>(stream)) != hipSuccess)
+    return LBP_ERR_HIP;
+  return LBP_OK;
+}
+
 }  // extern "C"

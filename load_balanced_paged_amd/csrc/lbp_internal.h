@@ -158,5 +158,7 @@ enum AttendKind { kAttendBf16 = 0, kAttendFp8 = 1, kAttendFp8Q8 = 2 };
 hipError_t launch_attend(const AttendArgs& a, AttendKind kind, int grid, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, int max_split, hipStream_t s);
 hipError_t launch_prologue(const PrologueArgs& a, hipStream_t s);
+hipError_t launch_read_stream(const void* src, int64_t n16, int32_t* sink, int blocks,
+                              hipStream_t s);
 
 }  // namespace lbp

@@ -298,3 +298,14 @@ def test_prologue_guards(lib):
     assert st(prologue_args(v_scale=None), config=c8) == lbp.LBP_ERR_INVALID_ARG
     assert st(prologue_args(), config=cfg(head_dim=64)) == lbp.LBP_ERR_UNSUPPORTED
     assert lib.lbp_prologue(ctypes.byref(c), 4, None, None) == lbp.LBP_ERR_INVALID_ARG
+
+
+def test_read_stream_guards(lib):
+    """The read-stream reference rejects bad arguments before any launch."""
+    P = ctypes.c_void_p
+    aligned, odd = P(1 << 20), P((1 << 20) + 4)
+    assert lib.lbp_read_stream(None, 1024, FAKE, 8, None) == lbp.LBP_ERR_INVALID_ARG
+    assert lib.lbp_read_stream(aligned, 1024, None, 8, None) == lbp.LBP_ERR_INVALID_ARG
+    assert lib.lbp_read_stream(aligned, 1024, FAKE, 0, None) == lbp.LBP_ERR_INVALID_ARG
+    assert lib.lbp_read_stream(aligned, 1000, FAKE, 8, None) == lbp.LBP_ERR_INVALID_ARG
+    assert lib.lbp_read_stream(odd, 1024, FAKE, 8, None) == lbp.LBP_ERR_INVALID_ARG
