@@ -36,7 +36,6 @@ import torch  # noqa: E402
 
 METRIC = "µs per decode-attention step + achieved KV HBM GB/s (% of peak), mixed-length"
 HBM_PEAK_GBS = 8000.0
-HEADLINE = "mixed"
 LAYERS = {"mixed": 8, "uniform": 4, "skewed": 16, "fp8": 1, "tiny": 1}
 ATTEND_KERNEL = {"bf16": "attend_kernel<Bf16Kv>", "fp8_e4m3": "attend_kernel<Fp8Kv>"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attend_traffic.json")
@@ -424,15 +423,16 @@ def cpu_baseline(b: Bench, seconds: float):
 
 # ---------------------------------------------------------------------------
 
-def traffic_record(kv_dtype):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
-    taken on the current attention kernel source; else None."""
+def traffic_record(workload):
+    """HBM bytes per launch from committed rocprofv3 counter runs on this
+    workload, if they were taken on the current attention kernel source;
+    else None."""
     try:
         rec = json.load(open(TRAFFIC_FILE))
     except Exception:
         return None
     src_hash = hashlib.sha256(open(ATTEND_SRC, "rb").read()).hexdigest()[:16]
-    entry = rec.get(HEADLINE if kv_dtype == "bf16" else "fp8")
+    entry = rec.get(workload)
     if not entry or entry.get("attend_src_sha") != src_hash:
         return None
     return entry.get("hbm_bytes_per_launch")
@@ -491,7 +491,7 @@ def bench_one(name, lbp, args, headline, stream_gbs=None):
     if headline and not args.no_cpu_baseline:
         log(f"{name}: CPU oracle baseline ({args.cpu_seconds:.0f}s budget)")
         res["cpu_baseline"] = cpu_baseline(b, args.cpu_seconds)
-    traffic = traffic_record(b.wcfg.kv_dtype)
+    traffic = traffic_record(name)
     achieved = b.wl.kv_bytes / (k_mean * 1e-6) / 1e9
     res["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                        "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
