@@ -58,6 +58,13 @@
 //    are widened to bf16 exactly in registers; the K scale multiplies the
 //    score of its token, the V scale is folded into the probability before
 //    the bf16 P.V product (sum_t p_t (c_t s_t) = sum_t (p_t s_t) c_t).
+//  * Multi-token verification (q_len > 1 query tokens per request, each
+//    attending causally up to its own position): the G * q_len query rows of
+//    a KV head are the MFMA columns.  Up to 16 columns run the loop above
+//    with a per-column causal limit; past 16, a staged instance splits the
+//    columns into blocks over groups of waves and shares each KV slice
+//    through an LDS ring, so that every KV byte is still fetched once per
+//    workgroup (see attend_bin).
 #include "lse_merge.h"
 
 namespace lbp {
