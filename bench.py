@@ -300,6 +300,27 @@ class Bench:
         return {"us": round(us, 2), "bytes": nbytes, "gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
                 "query": "e4m3 + scale" if fp8 else "bf16"}
 
+    def finish_spread(self, policy=0, param=0):
+        """Finishing times of the attention kernel's workgroups in one traced
+        launch (lbp_attend_traced, layer 0): with equal bins they should end
+        together.  Times in µs from the earliest workgroup start; only
+        workgroups that drained at least one descriptor count."""
+        lbp = self.lbp
+        info, plan_ws, split_ws = self.plan(policy, param)
+        L = self.wl.layers[0]
+        trace = torch.zeros(4 * info.num_bins, dtype=torch.int64, device="cuda")
+        for _ in range(2):             # the second launch is the one read
+            lbp.lbp_attend_traced(self.cfg, info, plan_ws, L.q, L.k_cache, L.v_cache, L.k_scale,
+                                  L.v_scale, split_ws, self.outs[0], trace)
+        torch.cuda.synchronize()
+        t = trace.view(-1, 4).cpu().numpy()
+        t = t[t[:, 3] > 0]
+        end = (t[:, 1] - t[:, 0].min()) / 100.0   # 100 MHz real-time counter
+        med, mx = float(np.median(end)), float(end.max())
+        return {"workgroups": int(len(t)), "end_us_min": round(float(end.min()), 1),
+                "end_us_median": round(med, 1), "end_us_max": round(mx, 1),
+                "tail_frac": round((mx - med) / mx, 4)}
+
     def time_plan(self, reps=20):
         lbp = self.lbp
         info, plan_ws, _ = self.plan()
@@ -483,6 +504,9 @@ def bench_one(name, lbp, args, headline, stream_gbs=None):
                                   eager=args.eager)
             static[S] = sms * 1e3
         best = min(static, key=static.get)
+        res["finish_spread"] = {"dynamic": b.finish_spread(),
+                                "static_grid_matched": b.finish_spread(
+                                    lbp.LBP_POLICY_STATIC_SPLITS, s0)}
         res["static_splits"] = {"S_grid_matched": s0, "us_grid_matched": round(static[s0], 2),
                                 "best_S": best, "us_best": round(static[best], 2),
                                 "dynamic_speedup_vs_grid_matched": round(static[s0] / us, 3),
@@ -634,6 +658,7 @@ def main():
             out[k] = head[k]
     if "static_splits" in head:
         out["static_splits"] = head["static_splits"]
+        out["finish_spread"] = head["finish_spread"]
     if "cpu_baseline" in head:
         out["cpu_baseline"] = head["cpu_baseline"]
     if len(results) > 1:
