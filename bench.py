@@ -322,13 +322,23 @@ class Bench:
                 "tail_frac": round((mx - med) / mx, 4)}
 
     def time_plan(self, reps=20):
+        """µs per lbp_plan: `reps` plans captured in a HIP graph, as a decode
+        step would launch it (eager launches here would time the host)."""
         lbp = self.lbp
         info, plan_ws, _ = self.plan()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                for _ in range(reps):
+                    lbp.lbp_plan(self.cfg, self.seq, self.table, plan_ws, stream=s)
+        torch.cuda.current_stream().wait_stream(s)
+        g.replay()
         torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        for _ in range(reps):
-            lbp.lbp_plan(self.cfg, self.seq, self.table, plan_ws)
+        g.replay()
         e1.record()
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) * 1e3 / reps

@@ -102,6 +102,19 @@ def test_large_pair_count_bitexact(gpu_lib):
     check(got, oracle.assign.assign_dynamic(L, 8, 512, 4))
 
 
+def test_pair_count_past_lds_bitexact(gpu_lib):
+    """More than 8192 pairs: the assign kernel keeps its per-pair arrays in
+    the plan workspace instead of LDS (dynamic and static plans)."""
+    import oracle
+    rng = np.random.default_rng(6)
+    L = rng.integers(0, 3000, size=1100).astype(np.int32)
+    assert 8 * len(L) > 8192
+    got, info, _ = plan_only(None, L, 8, 512, 4)
+    check(got, oracle.assign.assign_dynamic(L, 8, 512, 4))
+    got, info, _ = plan_only(None, L, 8, 0, 4, lbp.LBP_POLICY_STATIC_SPLITS, 3)
+    check(got, oracle.assign.assign_static_splits(L, 8, 3))
+
+
 @pytest.mark.parametrize("S", [1, 2, 3, 8, 64])
 def test_static_splits_bitexact(gpu_lib, S):
     import oracle
