@@ -130,6 +130,19 @@ __device__ inline void keep_order() {
   if constexpr (kOrdered) asm volatile("" ::: "memory");
 }
 
+// Ties a register block to the memory operations issued before it (an empty
+// asm statement that clobbers memory and claims to rewrite the block): math
+// that reads the block cannot be scheduled above those loads.  The decode
+// loop passes the query through it right after issuing the next slice, so
+// that slice's loads go out before the current slice's scores instead of
+// after them, and two slices stay in flight.
+__device__ inline void after_loads(i32x4_t& x) { asm volatile("" : "+v"(x)::"memory"); }
+__device__ inline void after_loads(bf16x8_t& x) {
+  i32x4_t y = __builtin_bit_cast(i32x4_t, x);
+  after_loads(y);
+  x = __builtin_bit_cast(bf16x8_t, y);
+}
+
 // The four lane groups (lanes n, n + 16, n + 32, n + 48) hold one MFMA
 // column.  Their reductions use gfx950's lane swaps instead of a trip
 // through the LDS crossbar: swapping a value with a copy of itself across
@@ -254,6 +267,10 @@ struct Bf16Kv {
     load_q_bf16<Bf16Kv>(q.v, a, ql, g, r, grp);
   }
   __device__ static float score_scale(const Q&, float scale_log2) { return scale_log2; }
+  __device__ static void after_loads(Q& q) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) lbp::after_loads(q.v[k]);
+  }
 
   template <bool kOrdered = false>
   __device__ static void issue(Buf& b, const SliceRsrc& rs, int lane) {
@@ -326,6 +343,10 @@ struct Fp8Kv {
     load_q_bf16<Fp8Kv>(q.v, a, ql, g, r, grp);
   }
   __device__ static float score_scale(const Q&, float scale_log2) { return scale_log2; }
+  __device__ static void after_loads(Q& q) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) lbp::after_loads(q.v[k]);
+  }
 
   template <bool kOrdered = false>
   __device__ static void issue(Buf& b, const SliceRsrc& rs, int lane) {
@@ -409,6 +430,10 @@ struct Fp8KvQ8 : Fp8Kv {
     q.scale = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sr, 4 * ql.row, 0, 0));
   }
   __device__ static float score_scale(const Q& q, float scale_log2) { return q.scale * scale_log2; }
+  __device__ static void after_loads(Q& q) {
+    lbp::after_loads(q.c[0]);
+    lbp::after_loads(q.c[1]);
+  }
 
   // 8 codes (one k-step of 32 dims split over the four lane groups) as an
   // fp8 MFMA operand.
@@ -477,6 +502,12 @@ struct Staged {
 // ---------------------------------------------------------------------------
 // the kernel
 // ---------------------------------------------------------------------------
+
+// Number of slices a wave takes from [t, e) when its slices start at t and
+// advance by `stride` tokens.
+__device__ inline int wave_slices(int t, int e, int stride) {
+  return t < e ? (e - t + stride - 1) / stride : 0;
+}
 
 // The read-only tables (page table, descriptors, pair counts, bin offsets)
 // reach the kernel as separate `const __restrict__` parameters: proven
@@ -732,20 +763,36 @@ __device__ inline void attend_bin(const AttendArgs& a, const int32_t* __restrict
       // the merge below reuses the ring's LDS
       __syncthreads();
     } else {
+      // The wave's n slices of the descriptor, the first in buf[0]: each one
+      // that has a successor issues the successor's loads and then
+      // computes, with both in flight; the last one issues nothing (the next
+      // descriptor's loads follow the loop; a load past the end, though it
+      // moves no data, costs as much issue and queue time as a real one).
+      // Whole trips of two steps, then for even n one more step and a copy
+      // of the last slice from buf[1] to buf[0] (which waits for it), so a
+      // single code path computes every last slice: with one such path per
+      // parity the compiler kept two copies of the wave state.  The loop has
+      // one exit and every path to a step has the same loads outstanding, so
+      // the compiler's wait counts stay exact.
       int tok = t_begin + wave * kSlice;
-      bool more = tok < t_end;
-      while (more) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          Kv::issue(buf[u ^ 1], slice_rsrc<Kv>(a, pt, g, r, tok + step, t_end), lane);
-          consume<Kv, kCausal>(st, buf[u], qb, tok, t_end, Kv::score_scale(qb, a.scale_log2),
-                               grp, lim);
-          tok += step;
-          if (tok >= t_end) {
-            more = false;
-            break;
-          }
+      const int ns = wave_slices(tok, t_end, step);
+      const float sc = Kv::score_scale(qb, a.scale_log2);
+      auto step_on = [&](const typename Kv::Buf& cur, typename Kv::Buf& nxt) {
+        Kv::issue(nxt, slice_rsrc<Kv>(a, pt, g, r, tok + step, t_end), lane);
+        Kv::after_loads(qb);
+        consume<Kv, kCausal>(st, cur, qb, tok, t_end, sc, grp, lim);
+        tok += step;
+      };
+      if (ns > 0) {
+        for (int i = (ns - 1) >> 1; i > 0; --i) {
+          step_on(buf[0], buf[1]);
+          step_on(buf[1], buf[0]);
         }
+        if ((ns & 1) == 0) {
+          step_on(buf[0], buf[1]);
+          buf[0] = buf[1];
+        }
+        consume<Kv, kCausal>(st, buf[0], qb, tok, t_end, sc, grp, lim);
       }
     }
     // the next descriptor's query and first slice, the query first: as the
