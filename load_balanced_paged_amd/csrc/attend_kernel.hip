@@ -27,13 +27,13 @@
 //    in-register 16-bit pack is needed - no LDS transpose.
 //  * Every KV load is a buffer load whose resource covers only the slice's
 //    valid rows: rows past the descriptor's end read as zero and cost no
-//    memory traffic, which both masks the unused slots of a request's last
-//    page (they may hold NaN) and lets the prefetch of nonexistent slices be
-//    issued unconditionally, keeping the wait counts static.
-//  * Two slices are in flight per wave (one computing, one loading) with 8
-//    waves per workgroup for BF16; FP8 moves half the bytes per token for
-//    the same math, so it runs 12 waves (three per SIMD) to keep enough
-//    loads in flight.
+//    memory traffic, which masks the unused slots of a request's last page
+//    (they may hold NaN).
+//  * Two slices are in flight per wave (one computing, one loading): a
+//    slice's successor is issued before the slice's math, and a wave's last
+//    slice of a descriptor issues nothing.  BF16 runs 8 waves per
+//    workgroup, FP8 6: with both slices really in flight, more FP8 waves
+//    only added merge work per descriptor and register pressure.
 //  * A pair served by a single descriptor is finished in place: its
 //    normalised output goes straight to `out` in BF16, and a pair without
 //    tokens gets zero rows here too.  Only pairs split over several bins use
@@ -75,13 +75,13 @@ namespace {
 #define LBP_BF16_WAVES 8
 #endif
 #ifndef LBP_FP8_WAVES
-#define LBP_FP8_WAVES 12
+#define LBP_FP8_WAVES 6
 #endif
 #ifndef LBP_BF16_SPLIT_P
 #define LBP_BF16_SPLIT_P 1
 #endif
 #ifndef LBP_FP8Q_WAVES
-#define LBP_FP8Q_WAVES 12
+#define LBP_FP8Q_WAVES 8
 #endif
 #ifndef LBP_KV_LOAD_AUX
 #define LBP_KV_LOAD_AUX 2
@@ -324,8 +324,9 @@ struct Fp8Kv {
   // its issue slots for the code widening
   static constexpr bool kSplitP = false;
   static constexpr bool kLaneSwap = false;
-  // FP8 moves half the bytes per token for the same MFMA and softmax work, so
-  // it needs more waves in flight per CU (three per SIMD) to stay on HBM.
+  // waves per workgroup: FP8 moves half the bytes per token, but 6 waves with
+  // two slices each keep enough loads in flight, and fewer waves make each
+  // descriptor's merge cheaper
   static constexpr int kWaves = LBP_FP8_WAVES;
   struct Buf {
     i32x4_t k[2];   // 32 codes: dims [32grp, 32grp + 32) of token m
@@ -413,6 +414,8 @@ struct Fp8Kv {
 // probabilities take the FP8 KV path above.
 struct Fp8KvQ8 : Fp8Kv {
   static constexpr int kWaves = LBP_FP8Q_WAVES;
+  // no code widening on the score side leaves VALU slots for lane swaps
+  static constexpr bool kLaneSwap = true;
   struct Q {
     i32x4_t c[2];   // codes of dims [32grp, 32grp + 32) of head n
     float scale;    // the head's Q scale (0 for columns past the group)

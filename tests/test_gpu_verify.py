@@ -142,7 +142,8 @@ def test_verify_fp8_kv_and_query(gpu_lib):
 
 
 def test_verify_fp8_column_blocks(gpu_lib):
-    """FP8 KV and FP8 query with 48 columns (three blocks of the 12 waves)."""
+    """FP8 KV and FP8 query with 48 columns (four blocks of 12 columns over
+    the staged instance's 8 waves)."""
     wcfg = dataclasses.replace(CONFIGS["fp8"], name="vb-fp8", batch=4)
     case = build_case(wcfg, lengths=[3, 300, 4000, 9000], num_workgroups=20, q_len=6)
     q = make_q(case, 6, seed=8)
