@@ -17,24 +17,28 @@
 // regardless of batch size; workgroup (i, q) merges column q (query token
 // q / G, head q % G) of list entry i, or exits if the plan has fewer
 // entries.  Thread t owns dims
-// [4(t%32), +4) of partials k = t/32 (mod 8) and loads each partial's
-// log-sum-exp together with its row, merging online (running max, sum and
-// rescaled accumulator), sixteen partials per thread in flight: 128 partial
-// rows per round trip, so the critical path is the launch plus two dependent
-// memory round trips (the list entry, then the rows) for up to 128 splits.
-// The eight per-thread states are merged in LDS in a fixed order (bitwise
-// deterministic).
+// [4(t%32), +4) of partials k = t/32 (mod R), R = threads / 32, and loads
+// each partial's log-sum-exp together with its row, merging online (running
+// max, sum and rescaled accumulator), sixteen partials per thread in flight:
+// 16 R partial rows per round trip, so the critical path is the launch plus
+// two dependent memory round trips (the list entry, then the rows) for up to
+// 16 R splits.  The R per-thread states are merged in LDS in a fixed order
+// (bitwise deterministic).  Workgroups have 256 threads (128 rows per round
+// trip); a grid of at most one workgroup per CU, which few split pairs with
+// many partials each give, uses 512 (256 rows): the wider workgroups cost
+// dispatch time only when there are many of them.
 #include "lse_merge.h"
 
 namespace lbp {
 namespace {
 
-constexpr int kThreads = 256;
 constexpr int kLanesPerRow = kHeadDim / 4;              // 32 float4 per 128-dim row
-constexpr int kRowGroups = kThreads / kLanesPerRow;     // 8 partial rows per sweep
 constexpr int kUnroll = 16;
+constexpr int kWideGrid = 256;   // workgroups up to which the 512-thread form runs
 
+template <int kThreads>
 __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
+  constexpr int kRowGroups = kThreads / kLanesPerRow;     // partial rows per sweep
   __shared__ float red_m[kRowGroups];
   __shared__ float red_l[kRowGroups];
   __shared__ f32x4_t red_o[kRowGroups][kLanesPerRow];
@@ -105,8 +109,10 @@ hipError_t launch_combine(const CombineArgs& a, int max_split, hipStream_t s) {
   if (max_split <= 0) return hipSuccess;
   CombineArgs copy = a;
   void* args[] = {&copy};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&combine_kernel), dim3(max_split, a.ncols),
-                         dim3(kThreads), args, 0, s);
+  const bool wide = int64_t(max_split) * a.ncols <= kWideGrid;
+  const void* fn = wide ? reinterpret_cast<const void*>(&combine_kernel<512>)
+                        : reinterpret_cast<const void*>(&combine_kernel<256>);
+  return hipLaunchKernel(fn, dim3(max_split, a.ncols), dim3(wide ? 512 : 256), args, 0, s);
 }
 
 }  // namespace lbp

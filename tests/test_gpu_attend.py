@@ -93,6 +93,24 @@ def test_attend_bin_shapes(gpu_lib, W, F):
     compare(case, out, oracle_pairs(case, 0, all_pairs(case)), f"tiny W={W} F={F}")
 
 
+@pytest.mark.parametrize("batch,W,wide", [(1, 600, True), (40, 400, False)])
+def test_combine_rounds_both_widths(gpu_lib, batch, W, wide):
+    """A pair split into more partials than one round of the combine's loads
+    takes: 600 partials through the 512-thread form (a grid of at most 256
+    workgroups, 256 rows per round) and 300 through the 256-thread form
+    (128 rows per round)."""
+    n_long = 600 if batch == 1 else 300
+    wcfg = dataclasses.replace(CONFIGS["skewed"], name=f"rounds{batch}", batch=batch)
+    case = build_case(wcfg, lengths=[64 * n_long] + [64] * (batch - 1), num_workgroups=W,
+                      min_tiles=1)
+    assert_taskmap_matches(case)
+    tm = lbp.read_taskmap(case.plan_ws, case.info)
+    assert int(tm["pair_count"].max()) == n_long
+    assert (min(batch, W - 1) * wcfg.num_q_heads <= 256) == wide
+    out = run_attend(case)
+    compare(case, out, oracle_pairs(case, 0, all_pairs(case)), f"combine rounds B={batch}")
+
+
 @pytest.mark.parametrize("policy,param", [(lbp.LBP_POLICY_STATIC_SPLITS, 1),
                                           (lbp.LBP_POLICY_STATIC_SPLITS, 7),
                                           (lbp.LBP_POLICY_STATIC_CHUNK, 2)])
