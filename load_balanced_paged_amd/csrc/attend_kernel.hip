@@ -167,8 +167,8 @@ __device__ inline void partners16(float x, float& lo, float& hi) {
   hi = b;   // the value of lane l | 16
 }
 // kSwap: the lane swaps above, else cross-lane shuffles through the LDS
-// crossbar (measured faster for the FP8 decode formats, whose loop has no
-// registers to spare at three waves per SIMD).
+// crossbar (measured faster for FP8 KV with a BF16 query, whose loop spends
+// its VALU slots on widening the codes).
 template <bool kSwap>
 __device__ inline float wave_max_across_groups(float x) {
   if constexpr (kSwap) {
@@ -614,13 +614,20 @@ __device__ inline void consume(WaveState& st, const typename Kv::Buf& b, const t
   }
 }
 
-// Waves of the staged instance (column blocks, more than 16 query columns)
-// for every KV format: its LDS ring of 2 x waves slices must fit the CU.
+// Waves of the staged instances (column blocks, more than 16 query columns),
+// for every KV format; their LDS ring of 2 x waves slices must fit the CU.
+// The column blocks divide the waves evenly.  8 waves give full blocks for
+// 17-32 columns (two) and 49-64 (four); 33-48 columns over 8 waves would be
+// four blocks of at most 12, leaving a quarter of every MFMA tile idle, so
+// those run 6 waves (three blocks of at most 16).
 constexpr int kStagedWaves = 8;
+constexpr int kStagedWaves33To48 = 6;
 
-template <class Kv, bool kStaged>
+// kStagedW: 0 for the decode and causal instances (the format's own wave
+// count), else the staged instance's wave count.
+template <class Kv, int kStagedW>
 constexpr int waves_of() {
-  return kStaged ? kStagedWaves : Kv::kWaves;
+  return kStagedW > 0 ? kStagedW : Kv::kWaves;
 }
 
 // A slice's register image in LDS (Kv: a slice format with member type
@@ -665,14 +672,15 @@ struct BufImage {
 // round's slices from LDS.  Every KV byte is then fetched once per
 // workgroup with the full set of loads in flight, while each wave keeps the
 // register state of a single 16-column tile.
-template <class Kv, bool kCausal, bool kStaged>
+template <class Kv, bool kCausal, int kStagedW>
 __device__ inline void attend_bin(const AttendArgs& a, const int32_t* __restrict__ pt,
                                   const int4* __restrict__ descs,
                                   const int32_t* __restrict__ pair_count,
                                   const int32_t* __restrict__ bin_offset,
                                   const int4* __restrict__ bin_first,
                                   const int32_t* __restrict__ pair_first, float* smem, int bin) {
-  constexpr int kWaves = waves_of<Kv, kStaged>();
+  constexpr bool kStaged = kStagedW > 0;
+  constexpr int kWaves = waves_of<Kv, kStagedW>();
   constexpr int kThreads = kWaves * 64;
   static_assert(kCausal || !kStaged, "the staged form serves verification only");
   const int lane = threadIdx.x & 63;
@@ -1054,12 +1062,12 @@ __device__ void finish_split_pairs(const AttendArgs& a, const int4* __restrict__
 // on a faster CU simply drains more bins; every workgroup draws exactly one
 // ticket past the last bin, and the one holding the final ticket returns the
 // counter to zero for the next launch.
-template <class Kv, bool kCausal, bool kStaged>
-__global__ __launch_bounds__((waves_of<Kv, kStaged>() * 64)) void attend_kernel(
+template <class Kv, bool kCausal, int kStagedW>
+__global__ __launch_bounds__((waves_of<Kv, kStagedW>() * 64)) void attend_kernel(
     AttendArgs a, const int32_t* __restrict__ page_table, const int4* __restrict__ descs,
     const int32_t* __restrict__ pair_count, const int32_t* __restrict__ bin_offset,
     const int32_t* __restrict__ pair_first, const int4* __restrict__ bin_first) {
-  constexpr int kThreads = waves_of<Kv, kStaged>() * 64;
+  constexpr int kThreads = waves_of<Kv, kStagedW>() * 64;
   extern __shared__ __attribute__((aligned(16))) float smem[];   // f32x4 rows are stored in it
   __shared__ int ticket_lds;
   __shared__ int arrive_lds;
@@ -1078,8 +1086,8 @@ __global__ __launch_bounds__((waves_of<Kv, kStaged>() * 64)) void attend_kernel(
   };
   int bin = a.grab_counter ? next_bin() : int(blockIdx.x);
   while (bin < a.num_bins) {
-    attend_bin<Kv, kCausal, kStaged>(a, page_table, descs, pair_count, bin_offset, bin_first,
-                                     pair_first, smem, bin);
+    attend_bin<Kv, kCausal, kStagedW>(a, page_table, descs, pair_count, bin_offset, bin_first,
+                                      pair_first, smem, bin);
     const int d_begin = bin_offset[bin], d_end = bin_offset[bin + 1];
     if (a.fuse)
       finish_split_pairs<kThreads>(a, descs, pair_count, pair_first, smem, &arrive_lds, d_begin,
@@ -1118,6 +1126,24 @@ __global__ __launch_bounds__((waves_of<Kv, kStaged>() * 64)) void attend_kernel(
 
 }  // namespace
 
+// The instance for a KV format: decode, causal (q_len > 1, at most 16
+// columns) or staged with staged_w waves; its wave count and, when staged,
+// the bytes of its LDS ring.
+template <class Kv>
+void pick_instance(bool causal, int staged_w, const void** fn, int* waves, size_t* ring) {
+  *ring = 0;
+  if (staged_w == kStagedWaves) {
+    *fn = reinterpret_cast<const void*>(&attend_kernel<Kv, true, kStagedWaves>);
+  } else if (staged_w == kStagedWaves33To48) {
+    *fn = reinterpret_cast<const void*>(&attend_kernel<Kv, true, kStagedWaves33To48>);
+  } else {
+    *fn = causal ? reinterpret_cast<const void*>(&attend_kernel<Kv, true, 0>)
+                 : reinterpret_cast<const void*>(&attend_kernel<Kv, false, 0>);
+  }
+  *waves = staged_w > 0 ? staged_w : Kv::kWaves;
+  if (staged_w > 0) *ring = 2 * size_t(staged_w) * BufImage<Staged<Kv>>::kBytes;
+}
+
 hipError_t launch_attend(const AttendArgs& a, AttendKind kind, int grid, hipStream_t s) {
   AttendArgs copy = a;
   const int32_t* pt = a.page_table;
@@ -1133,26 +1159,21 @@ hipError_t launch_attend(const AttendArgs& a, AttendKind kind, int grid, hipStre
   const bool causal = a.q_len > 1;
   const bool staged = causal && a.ncols > 16;
   if (!causal && a.ncols > 16) return hipErrorInvalidValue;
+  const int staged_w = !staged                            ? 0
+                       : a.ncols > 32 && a.ncols <= 48 ? kStagedWaves33To48
+                                                       : kStagedWaves;
   int waves;
   const void* fn;
+  size_t ring;   // the staged instance's LDS ring
   switch (kind) {
     case kAttendFp8:
-      waves = staged ? waves_of<Fp8Kv, true>() : Fp8Kv::kWaves;
-      fn = staged   ? reinterpret_cast<const void*>(&attend_kernel<Fp8Kv, true, true>)
-           : causal ? reinterpret_cast<const void*>(&attend_kernel<Fp8Kv, true, false>)
-                    : reinterpret_cast<const void*>(&attend_kernel<Fp8Kv, false, false>);
+      pick_instance<Fp8Kv>(causal, staged_w, &fn, &waves, &ring);
       break;
     case kAttendFp8Q8:
-      waves = staged ? waves_of<Fp8KvQ8, true>() : Fp8KvQ8::kWaves;
-      fn = staged   ? reinterpret_cast<const void*>(&attend_kernel<Fp8KvQ8, true, true>)
-           : causal ? reinterpret_cast<const void*>(&attend_kernel<Fp8KvQ8, true, false>)
-                    : reinterpret_cast<const void*>(&attend_kernel<Fp8KvQ8, false, false>);
+      pick_instance<Fp8KvQ8>(causal, staged_w, &fn, &waves, &ring);
       break;
     default:
-      waves = staged ? waves_of<Bf16Kv, true>() : Bf16Kv::kWaves;
-      fn = staged   ? reinterpret_cast<const void*>(&attend_kernel<Bf16Kv, true, true>)
-           : causal ? reinterpret_cast<const void*>(&attend_kernel<Bf16Kv, true, false>)
-                    : reinterpret_cast<const void*>(&attend_kernel<Bf16Kv, false, false>);
+      pick_instance<Bf16Kv>(causal, staged_w, &fn, &waves, &ring);
   }
   // staged: columns in blocks of at most 16 over an equal share of the
   // waves each, the fewest blocks that divide the waves
@@ -1164,15 +1185,7 @@ hipError_t launch_attend(const AttendArgs& a, AttendKind kind, int grid, hipStre
   copy.col_blocks = blocks;
   copy.block_cols = (a.ncols + blocks - 1) / blocks;
   size_t lds = size_t(waves) * (32 + copy.block_cols * kRedRow) * sizeof(float);
-  if (staged) {
-    size_t ring;
-    switch (kind) {
-      case kAttendFp8: ring = 2 * size_t(waves) * BufImage<Staged<Fp8Kv>>::kBytes; break;
-      case kAttendFp8Q8: ring = 2 * size_t(waves) * BufImage<Staged<Fp8KvQ8>>::kBytes; break;
-      default: ring = 2 * size_t(waves) * BufImage<Staged<Bf16Kv>>::kBytes;
-    }
-    if (ring > lds) lds = ring;
-  }
+  if (staged && ring > lds) lds = ring;
   const size_t merge_lds = size_t(merge_lds_floats(waves * 64)) * sizeof(float);
   if (a.fuse && merge_lds > lds) lds = merge_lds;
   if (grid <= 0) return hipSuccess;
