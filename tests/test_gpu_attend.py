@@ -14,7 +14,7 @@ import load_balanced_paged_amd as lbp
 import oracle
 from gpu_support import (all_pairs, assert_taskmap_matches, bf16_to_f64, bits, build_case,
                          compare, oracle_pairs, run_attend, sample_pairs, say)
-from workloads import CONFIGS
+from workloads import CONFIGS, quantize_query_e4m3
 
 pytestmark = pytest.mark.gpu
 
@@ -82,6 +82,42 @@ def test_attend_zero_length_requests(gpu_lib):
     out = run_attend(case)
     assert torch.all(out[0] == 0) and torch.all(out[2] == 0)
     compare(case, out, oracle_pairs(case, 0, all_pairs(case)), "zero-length")
+
+
+@pytest.mark.parametrize("kv,q_len,entry", [("bf16", 1, "attend"), ("bf16", 1, "fused"),
+                                             ("bf16", 3, "attend"), ("bf16", 6, "fused"),
+                                             ("fp8_e4m3", 1, "attend"), ("fp8_e4m3", 1, "fp8q")])
+def test_all_requests_empty(gpu_lib, kv, q_len, entry):
+    """Every length zero (T = 0: no tile, no descriptor, every bin empty):
+    every output row is exactly zero, and nothing is read from a KV cache
+    (and scales) holding only NaN."""
+    base = CONFIGS["tiny"] if kv == "bf16" else CONFIGS["fp8"]
+    wcfg = dataclasses.replace(base, name=f"empty-{kv}", batch=3)
+    case = build_case(wcfg, lengths=[0, 0, 0], max_pages_per_seq=1, q_len=q_len, poison=False)
+    assert_taskmap_matches(case)
+    lay = case.wl.layers[0]
+    H, D = wcfg.num_kv_heads, 128
+    if kv == "bf16":
+        kc = torch.full((1, H, 64, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+        vc, ks, vs = kc.clone(), None, None
+    else:
+        kc = torch.full((1, H, 64, D), 0x7F, dtype=torch.uint8, device="cuda")   # e4m3 NaN
+        vc = kc.clone()
+        ks = torch.full((1, H, 64), float("nan"), dtype=torch.float32, device="cuda")
+        vs = ks.clone()
+    q = torch.randn((3, q_len, wcfg.num_q_heads, D), device="cuda").to(torch.bfloat16)
+    if q_len == 1:
+        q = q[:, 0].contiguous()
+    out = torch.full_like(q, float("nan"))
+    if entry == "fp8q":
+        codes, scale = quantize_query_e4m3(q)
+        lbp.lbp_attend_fp8q(case.cfg, case.info, case.plan_ws, codes, scale, kc, vc, ks, vs,
+                            case.split_ws, out)
+    else:
+        fn = lbp.lbp_attend if entry == "attend" else lbp.lbp_attend_fused
+        fn(case.cfg, case.info, case.plan_ws, q, kc, vc, ks, vs, case.split_ws, out)
+    torch.cuda.synchronize()
+    assert torch.equal(out, torch.zeros_like(out)), f"{kv} q_len={q_len} {entry}"
 
 
 @pytest.mark.parametrize("W,F", [(1, 1), (5, 1), (64, 1), (256, 4), (1024, 1)])
