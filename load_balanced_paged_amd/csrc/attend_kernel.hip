@@ -61,10 +61,11 @@
 //  * Multi-token verification (q_len > 1 query tokens per request, each
 //    attending causally up to its own position): the G * q_len query rows of
 //    a KV head are the MFMA columns.  Up to 16 columns run the loop above
-//    with a per-column causal limit; past 16, a staged instance splits the
-//    columns into blocks over groups of waves and shares each KV slice
-//    through an LDS ring, so that every KV byte is still fetched once per
-//    workgroup (see attend_bin).
+//    with a per-column causal limit, up to 32 the same loop with two
+//    16-column tiles per wave (each slice's K and V serve both); past 32, a
+//    staged instance splits the columns into blocks over groups of waves and
+//    shares each KV slice through an LDS ring, so that every KV byte is
+//    still fetched once per workgroup (see attend_bin).
 #include "lse_merge.h"
 
 namespace lbp {
@@ -614,12 +615,12 @@ __device__ inline void consume(WaveState& st, const typename Kv::Buf& b, const t
   }
 }
 
-// Waves of the staged instances (column blocks, more than 16 query columns),
+// Waves of the staged instances (column blocks, more than 32 query columns),
 // for every KV format; their LDS ring of 2 x waves slices must fit the CU.
-// The column blocks divide the waves evenly.  8 waves give full blocks for
-// 17-32 columns (two) and 49-64 (four); 33-48 columns over 8 waves would be
-// four blocks of at most 12, leaving a quarter of every MFMA tile idle, so
-// those run 6 waves (three blocks of at most 16).
+// The column blocks divide the waves evenly: 8 waves give four full blocks
+// for 49-64 columns; 33-48 columns over 8 waves would be four blocks of at
+// most 12, leaving a quarter of every MFMA tile idle, so those run 6 waves
+// (three blocks of at most 16).
 constexpr int kStagedWaves = 8;
 constexpr int kStagedWaves33To48 = 6;
 
@@ -663,7 +664,12 @@ struct BufImage {
 // latency overlaps the merge and the wait for the slowest wave instead of
 // following them.
 //
-// Staged form (kStaged: multi-token verification with more than 16 query
+// kNB: 16-column MFMA tiles per wave in the decode/causal form (1, or 2 for
+// 17-32 query columns: every wave keeps a wave state per tile and computes
+// both from each slice it loads, which at up to 32 columns stays cheaper
+// than staging slices through LDS).
+//
+// Staged form (kStaged: multi-token verification with more than 32 query
 // columns): the columns split into nblk blocks of at most 16, one per group
 // of waves.  The descriptor is walked in rounds of one slice per wave:
 // every wave loads a different slice (two rounds in flight, as above),
@@ -672,7 +678,7 @@ struct BufImage {
 // round's slices from LDS.  Every KV byte is then fetched once per
 // workgroup with the full set of loads in flight, while each wave keeps the
 // register state of a single 16-column tile.
-template <class Kv, bool kCausal, int kStagedW>
+template <class Kv, bool kCausal, int kStagedW, int kNB>
 __device__ inline void attend_bin(const AttendArgs& a, const int32_t* __restrict__ pt,
                                   const int4* __restrict__ descs,
                                   const int32_t* __restrict__ pair_count,
@@ -683,24 +689,30 @@ __device__ inline void attend_bin(const AttendArgs& a, const int32_t* __restrict
   constexpr int kWaves = waves_of<Kv, kStagedW>();
   constexpr int kThreads = kWaves * 64;
   static_assert(kCausal || !kStaged, "the staged form serves verification only");
+  static_assert(kNB == 1 || (kNB == 2 && kCausal && !kStaged),
+                "two column tiles per wave: causal form only");
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15;         // MFMA column of this lane within its block
   const int grp = lane >> 4;
   const int G = a.group;
   const int C = a.ncols;           // G * q_len
-  // column blocks (staged form only): the waves split into nblk equal
-  // groups, group b computes columns [b * cpb, b * cpb + cpb); otherwise one
-  // block of all the waves and all C <= 16 columns
+  // column blocks, staged form: the waves split into nblk equal groups,
+  // group b computes columns [b * cpb, b * cpb + cpb); otherwise every wave
+  // computes all C <= 16 kNB columns, as kNB 16-column MFMA tiles
   const int nblk = kStaged ? a.col_blocks : 1;
   const int wpb = kStaged ? kWaves / nblk : kWaves;    // waves per block
   const int blk = kStaged ? wave / wpb : 0;
   const int wslot = kStaged ? wave - blk * wpb : wave;  // the wave's place in its block
-  const int cpb = kStaged ? a.block_cols : C;          // columns per block, <= 16
+  const int cpb = kStaged ? a.block_cols : C;          // columns per block, <= 16 staged
   const int col0 = blk * cpb;
   const int nvalid = kStaged ? min(cpb, C - col0) : C; // this block's columns
   constexpr int step = kWaves * kSlice;                // tokens per round / per wave stride
-  const int red_stride = 32 + cpb * kRedRow;
+  // per wave in LDS for the merge: m and l of 16 kNB columns, then the rows
+  constexpr int kRedHead = 32 * kNB;
+  const int red_stride = kRedHead + cpb * kRedRow;
+  // tile t's columns: [col0 + 16 t, + tile_cols(t))
+  auto tile_cols = [&](int t) { return kNB == 1 ? nvalid : min(16, C - 16 * t); };
   float* red = smem + wave * red_stride;
   // range and first descriptor are independent loads: one round trip
   const int d_begin = bin_offset[bin];
@@ -709,10 +721,21 @@ __device__ inline void attend_bin(const AttendArgs& a, const int32_t* __restrict
   asm volatile("" ::"s"(ds.x), "s"(ds.y), "s"(ds.z), "s"(ds.w));   // keep the load above the exit
   if (d_begin >= d_end) return;
 
-  const QLane ql = q_lane<kCausal>(a, n, col0, nvalid);
-  typename Kv::Q qb;
+  QLane ql[kNB];
+  typename Kv::Q qb[kNB];
   typename Kv::Buf buf[2];
-  Kv::load_q(qb, a, ql, ds.x, ds.y, grp);
+  if constexpr (kNB == 1) {
+    // (spelled out: the loop form below, though equivalent, made the
+    // compiler schedule the decode instance differently, and slower)
+    ql[0] = q_lane<kCausal>(a, n, col0, nvalid);
+    Kv::load_q(qb[0], a, ql[0], ds.x, ds.y, grp);
+  } else {
+#pragma unroll
+    for (int t = 0; t < kNB; ++t) {
+      ql[t] = q_lane<kCausal>(a, n, col0 + 16 * t, tile_cols(t));
+      Kv::load_q(qb[t], a, ql[t], ds.x, ds.y, grp);
+    }
+  }
   Kv::template issue<kStaged>(buf[0], slice_rsrc<Kv>(a, pt, ds.x, ds.y, ds.z + wave * kSlice, ds.w),
                               lane);
 
@@ -725,17 +748,20 @@ __device__ inline void attend_bin(const AttendArgs& a, const int32_t* __restrict
     // causal limit of this lane's column in multi-token verification: query
     // token j of the request sits at position L - q_len + j, L being the
     // end of the pair's last descriptor
-    int lim = INT_MAX;
-    if constexpr (kCausal) {
-      const int L = descs[pair_first[p] + pair_count[p] - 1].w;
-      lim = L - a.q_len + 1 + (col0 + n) / G;
-    }
-
-    WaveState st;
-    st.m = -INFINITY;
-    st.l = 0.f;
+    int lim[kNB];
+    WaveState st[kNB];
 #pragma unroll
-    for (int mb = 0; mb < 8; ++mb) st.acc[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < kNB; ++t) {
+      lim[t] = INT_MAX;
+      if constexpr (kCausal) {
+        const int L = descs[pair_first[p] + pair_count[p] - 1].w;
+        lim[t] = L - a.q_len + 1 + (col0 + 16 * t + n) / G;
+      }
+      st[t].m = -INFINITY;
+      st[t].l = 0.f;
+#pragma unroll
+      for (int mb = 0; mb < 8; ++mb) st[t].acc[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
 
     // buf[0] already holds (or is loading) this wave's first slice of d; a
     // slice past t_end loads nothing
@@ -759,8 +785,8 @@ __device__ inline void attend_bin(const AttendArgs& a, const int32_t* __restrict
           const int tok = base + j * kSlice;
           if (tok >= t_end) break;
           const typename S::Buf b = BufImage<S>::load(stage + j * (kImg / 16), lane);
-          consume<S, kCausal, true>(st, b, qb, tok, t_end, Kv::score_scale(qb, a.scale_log2),
-                                    grp, lim);
+          consume<S, kCausal, true>(st[0], b, qb[0], tok, t_end,
+                                    Kv::score_scale(qb[0], a.scale_log2), grp, lim[0]);
         }
         base += step;
       };
@@ -787,11 +813,19 @@ __device__ inline void attend_bin(const AttendArgs& a, const int32_t* __restrict
       // the compiler's wait counts stay exact.
       int tok = t_begin + wave * kSlice;
       const int ns = wave_slices(tok, t_end, step);
-      const float sc = Kv::score_scale(qb, a.scale_log2);
+      // (one tile spelled out, as in the query setup above)
+      const float sc0 = Kv::score_scale(qb[0], a.scale_log2);
+      const float sc1 = kNB > 1 ? Kv::score_scale(qb[kNB - 1], a.scale_log2) : sc0;
+      auto compute = [&](const typename Kv::Buf& cur) {
+        consume<Kv, kCausal>(st[0], cur, qb[0], tok, t_end, sc0, grp, lim[0]);
+        if constexpr (kNB > 1)
+          consume<Kv, kCausal>(st[1], cur, qb[1], tok, t_end, sc1, grp, lim[1]);
+      };
       auto step_on = [&](const typename Kv::Buf& cur, typename Kv::Buf& nxt) {
         Kv::issue(nxt, slice_rsrc<Kv>(a, pt, g, r, tok + step, t_end), lane);
-        Kv::after_loads(qb);
-        consume<Kv, kCausal>(st, cur, qb, tok, t_end, sc, grp, lim);
+        Kv::after_loads(qb[0]);
+        if constexpr (kNB > 1) Kv::after_loads(qb[1]);
+        compute(cur);
         tok += step;
       };
       if (ns > 0) {
@@ -803,7 +837,7 @@ __device__ inline void attend_bin(const AttendArgs& a, const int32_t* __restrict
           step_on(buf[0], buf[1]);
           buf[0] = buf[1];
         }
-        consume<Kv, kCausal>(st, buf[0], qb, tok, t_end, sc, grp, lim);
+        compute(buf[0]);
       }
     }
     // the next descriptor's query and first slice, the query first: as the
@@ -815,7 +849,8 @@ __device__ inline void attend_bin(const AttendArgs& a, const int32_t* __restrict
     // that it loops with and the compiler's wait counts stay exact.
     auto prefetch_next = [&]() {
       const int first = has_next ? dn.z : dn.w;
-      Kv::load_q(qb, a, ql, dn.x, dn.y, grp);
+#pragma unroll
+      for (int t = 0; t < kNB; ++t) Kv::load_q(qb[t], a, ql[t], dn.x, dn.y, grp);
       Kv::template issue<kStaged>(buf[0],
                                   slice_rsrc<Kv>(a, pt, dn.x, dn.y, first + wave * kSlice, dn.w),
                                   lane);
@@ -823,28 +858,33 @@ __device__ inline void attend_bin(const AttendArgs& a, const int32_t* __restrict
     if (!kStaged && has_next) prefetch_next();
 
     // merge the wave states of this descriptor
-    st.l = wave_sum_across_groups<kStaged || Kv::kLaneSwap>(st.l);
-    if (n < nvalid) {
-      if (grp == 0) {
-        red[n] = st.m;
-        red[16 + n] = st.l;
-      }
-      float* orow = red + 32 + n * kRedRow + 32 * grp;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        *reinterpret_cast<f32x4_t*>(orow + 8 * j) =
-            f32x4_t{st.acc[0][j], st.acc[1][j], st.acc[2][j], st.acc[3][j]};
-        *reinterpret_cast<f32x4_t*>(orow + 8 * j + 4) =
-            f32x4_t{st.acc[4][j], st.acc[5][j], st.acc[6][j], st.acc[7][j]};
+    for (int t = 0; t < kNB; ++t) {
+      const WaveState& w = st[t];
+      const float l = wave_sum_across_groups<kStaged || Kv::kLaneSwap>(w.l);
+      if (n < tile_cols(t)) {
+        const int c = 16 * t + n;   // the column within this wave's columns
+        if (grp == 0) {
+          red[c] = w.m;
+          red[16 * kNB + c] = l;
+        }
+        float* orow = red + kRedHead + c * kRedRow + 32 * grp;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          *reinterpret_cast<f32x4_t*>(orow + 8 * j) =
+              f32x4_t{w.acc[0][j], w.acc[1][j], w.acc[2][j], w.acc[3][j]};
+          *reinterpret_cast<f32x4_t*>(orow + 8 * j + 4) =
+              f32x4_t{w.acc[4][j], w.acc[5][j], w.acc[6][j], w.acc[7][j]};
+        }
       }
     }
     __syncthreads();
     for (int idx = threadIdx.x; idx < C * kHeadDim; idx += kThreads) {
       const int q = idx >> 7, dim = idx & (kHeadDim - 1);
       // the waves of q's column block hold it, as their column qc
-      const int qb = kStaged ? q / cpb : 0;
-      const int qc = q - qb * cpb;
-      const float* rb = smem + qb * wpb * red_stride;
+      const int qblk = kStaged ? q / cpb : 0;
+      const int qc = q - qblk * cpb;
+      const float* rb = smem + qblk * wpb * red_stride;
       float M = -INFINITY;
 #pragma unroll
       for (int w = 0; w < wpb; ++w) M = fmaxf(M, rb[w * red_stride + qc]);
@@ -856,8 +896,8 @@ __device__ inline void attend_bin(const AttendArgs& a, const int32_t* __restrict
       for (int w = 0; w < wpb; ++w) {
         const float* rw = rb + w * red_stride;
         const float c = __builtin_amdgcn_exp2f(rw[qc] - Mu);
-        L += rw[16 + qc] * c;
-        o += rw[32 + qc * kRedRow + dim] * c;
+        L += rw[16 * kNB + qc] * c;
+        o += rw[kRedHead + qc * kRedRow + dim] * c;
       }
       const bool empty = kCausal && !(L > 0.f);
       const float on = empty ? 0.f : o / L;
@@ -1062,7 +1102,7 @@ __device__ void finish_split_pairs(const AttendArgs& a, const int4* __restrict__
 // on a faster CU simply drains more bins; every workgroup draws exactly one
 // ticket past the last bin, and the one holding the final ticket returns the
 // counter to zero for the next launch.
-template <class Kv, bool kCausal, int kStagedW>
+template <class Kv, bool kCausal, int kStagedW, int kNB>
 __global__ __launch_bounds__((waves_of<Kv, kStagedW>() * 64)) void attend_kernel(
     AttendArgs a, const int32_t* __restrict__ page_table, const int4* __restrict__ descs,
     const int32_t* __restrict__ pair_count, const int32_t* __restrict__ bin_offset,
@@ -1086,8 +1126,8 @@ __global__ __launch_bounds__((waves_of<Kv, kStagedW>() * 64)) void attend_kernel
   };
   int bin = a.grab_counter ? next_bin() : int(blockIdx.x);
   while (bin < a.num_bins) {
-    attend_bin<Kv, kCausal, kStagedW>(a, page_table, descs, pair_count, bin_offset, bin_first,
-                                      pair_first, smem, bin);
+    attend_bin<Kv, kCausal, kStagedW, kNB>(a, page_table, descs, pair_count, bin_offset,
+                                           bin_first, pair_first, smem, bin);
     const int d_begin = bin_offset[bin], d_end = bin_offset[bin + 1];
     if (a.fuse)
       finish_split_pairs<kThreads>(a, descs, pair_count, pair_first, smem, &arrive_lds, d_begin,
@@ -1126,19 +1166,23 @@ __global__ __launch_bounds__((waves_of<Kv, kStagedW>() * 64)) void attend_kernel
 
 }  // namespace
 
-// The instance for a KV format: decode, causal (q_len > 1, at most 16
-// columns) or staged with staged_w waves; its wave count and, when staged,
-// the bytes of its LDS ring.
+// The instance for a KV format: decode, causal with one or two MFMA column
+// tiles per wave (q_len > 1, at most 16 or 32 columns) or staged with
+// staged_w waves; its wave count and, when staged, the bytes of its LDS
+// ring.
 template <class Kv>
-void pick_instance(bool causal, int staged_w, const void** fn, int* waves, size_t* ring) {
+void pick_instance(bool causal, int tiles, int staged_w, const void** fn, int* waves,
+                   size_t* ring) {
   *ring = 0;
   if (staged_w == kStagedWaves) {
-    *fn = reinterpret_cast<const void*>(&attend_kernel<Kv, true, kStagedWaves>);
+    *fn = reinterpret_cast<const void*>(&attend_kernel<Kv, true, kStagedWaves, 1>);
   } else if (staged_w == kStagedWaves33To48) {
-    *fn = reinterpret_cast<const void*>(&attend_kernel<Kv, true, kStagedWaves33To48>);
+    *fn = reinterpret_cast<const void*>(&attend_kernel<Kv, true, kStagedWaves33To48, 1>);
+  } else if (tiles == 2) {
+    *fn = reinterpret_cast<const void*>(&attend_kernel<Kv, true, 0, 2>);
   } else {
-    *fn = causal ? reinterpret_cast<const void*>(&attend_kernel<Kv, true, 0>)
-                 : reinterpret_cast<const void*>(&attend_kernel<Kv, false, 0>);
+    *fn = causal ? reinterpret_cast<const void*>(&attend_kernel<Kv, true, 0, 1>)
+                 : reinterpret_cast<const void*>(&attend_kernel<Kv, false, 0, 1>);
   }
   *waves = staged_w > 0 ? staged_w : Kv::kWaves;
   if (staged_w > 0) *ring = 2 * size_t(staged_w) * BufImage<Staged<Kv>>::kBytes;
@@ -1154,26 +1198,26 @@ hipError_t launch_attend(const AttendArgs& a, AttendKind kind, int grid, hipStre
   const int4* bf = reinterpret_cast<const int4*>(a.bin_first);
   void* args[] = {&copy, &pt, &descs, &pc, &bo, &pf, &bf};
   // multi-token verification (q_len > 1) runs the instances with the causal
-  // limit, the staged one past 16 query columns; plain decode keeps the loop
+  // limit: one MFMA column tile per wave up to 16 query columns, two up to
+  // 32, and the staged instance past that; plain decode keeps the loop
   // without either
   const bool causal = a.q_len > 1;
-  const bool staged = causal && a.ncols > 16;
+  const int tiles = causal && a.ncols > 16 && a.ncols <= 32 ? 2 : 1;
+  const bool staged = causal && a.ncols > 32;
   if (!causal && a.ncols > 16) return hipErrorInvalidValue;
-  const int staged_w = !staged                            ? 0
-                       : a.ncols > 32 && a.ncols <= 48 ? kStagedWaves33To48
-                                                       : kStagedWaves;
+  const int staged_w = !staged ? 0 : a.ncols <= 48 ? kStagedWaves33To48 : kStagedWaves;
   int waves;
   const void* fn;
   size_t ring;   // the staged instance's LDS ring
   switch (kind) {
     case kAttendFp8:
-      pick_instance<Fp8Kv>(causal, staged_w, &fn, &waves, &ring);
+      pick_instance<Fp8Kv>(causal, tiles, staged_w, &fn, &waves, &ring);
       break;
     case kAttendFp8Q8:
-      pick_instance<Fp8KvQ8>(causal, staged_w, &fn, &waves, &ring);
+      pick_instance<Fp8KvQ8>(causal, tiles, staged_w, &fn, &waves, &ring);
       break;
     default:
-      pick_instance<Bf16Kv>(causal, staged_w, &fn, &waves, &ring);
+      pick_instance<Bf16Kv>(causal, tiles, staged_w, &fn, &waves, &ring);
   }
   // staged: columns in blocks of at most 16 over an equal share of the
   // waves each, the fewest blocks that divide the waves
@@ -1184,7 +1228,7 @@ hipError_t launch_attend(const AttendArgs& a, AttendKind kind, int grid, hipStre
   }
   copy.col_blocks = blocks;
   copy.block_cols = (a.ncols + blocks - 1) / blocks;
-  size_t lds = size_t(waves) * (32 + copy.block_cols * kRedRow) * sizeof(float);
+  size_t lds = size_t(waves) * (32 * tiles + copy.block_cols * kRedRow) * sizeof(float);
   if (staged && ring > lds) lds = ring;
   const size_t merge_lds = size_t(merge_lds_floats(waves * 64)) * sizeof(float);
   if (a.fuse && merge_lds > lds) lds = merge_lds;
