@@ -124,10 +124,13 @@ def test_verify_static_plan(gpu_lib):
                    "verify static")
 
 
-def test_verify_fp8_kv_and_query(gpu_lib):
+@pytest.mark.parametrize("T", [2, 3, 4])
+def test_verify_fp8_kv_and_query(gpu_lib, T):
+    """FP8 KV with a BF16 and with an FP8 query: 16 columns (one MFMA column
+    tile per wave), 24 and 32 (two tiles per wave)."""
     wcfg = dataclasses.replace(CONFIGS["fp8"], name="v-fp8", batch=5)
-    case = build_case(wcfg, lengths=[1, 70, 700, 3000, 20000], q_len=2)
-    q = make_q(case, 2, seed=5)
+    case = build_case(wcfg, lengths=[1, 70, 700, 3000, 20000], q_len=T)
+    q = make_q(case, T, seed=5)
     pairs = all_pairs(case)
     compare_verify(case, run(case, q), oracle_verify_pairs(case, 0, pairs, q64_of(q)),
                    "verify fp8 kv")
@@ -142,8 +145,8 @@ def test_verify_fp8_kv_and_query(gpu_lib):
 
 
 def test_verify_fp8_column_blocks(gpu_lib):
-    """FP8 KV and FP8 query with 48 columns (four blocks of 12 columns over
-    the staged instance's 8 waves)."""
+    """FP8 KV and FP8 query with 48 columns (the staged instance: three
+    blocks of 16 columns over 6 waves)."""
     wcfg = dataclasses.replace(CONFIGS["fp8"], name="vb-fp8", batch=4)
     case = build_case(wcfg, lengths=[3, 300, 4000, 9000], num_workgroups=20, q_len=6)
     q = make_q(case, 6, seed=8)
