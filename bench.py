@@ -360,27 +360,31 @@ class Bench:
 # read-stream reference
 # ---------------------------------------------------------------------------
 
-def read_stream_reference(lbp, gib=4, reps=5):
+def read_stream_reference(lbp, gib=4, reps=5, rounds=3, warm_seconds=0.2):
     """This GPU's attainable HBM read rate for streaming traffic: the library's
     read-stream kernel over a `gib` GiB buffer, best over a few grid sizes
-    (HIP events around `reps` launches each)."""
+    and `rounds` batches of `reps` launches each (HIP events around each
+    batch), after `warm_seconds` of streaming to bring the clocks up."""
     n = gib << 30
     buf = torch.empty(n, dtype=torch.uint8, device="cuda")
     buf.fill_(1)
     sink = torch.empty(1 << 16, dtype=torch.int32, device="cuda")
+    t0 = time.time()
+    while time.time() - t0 < warm_seconds:
+        lbp.lbp_read_stream(buf, sink, 8192)
+        torch.cuda.synchronize()
     best, best_blocks = 0.0, 0
     for blocks in (2048, 4096, 8192, 16384):
-        lbp.lbp_read_stream(buf, sink, blocks)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
-            lbp.lbp_read_stream(buf, sink, blocks)
-        e1.record()
-        torch.cuda.synchronize()
-        gbs = reps * n / (e0.elapsed_time(e1) * 1e-3) / 1e9
-        if gbs > best:
-            best, best_blocks = gbs, blocks
+        for _ in range(rounds):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                lbp.lbp_read_stream(buf, sink, blocks)
+            e1.record()
+            torch.cuda.synchronize()
+            gbs = reps * n / (e0.elapsed_time(e1) * 1e-3) / 1e9
+            if gbs > best:
+                best, best_blocks = gbs, blocks
     del buf, sink
     torch.cuda.empty_cache()
     log(f"read stream: {best:.0f} GB/s ({gib} GiB, {best_blocks} workgroups)")

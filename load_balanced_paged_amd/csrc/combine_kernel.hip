@@ -26,7 +26,9 @@
 // (bitwise deterministic).  Workgroups have 256 threads (128 rows per round
 // trip); a grid of at most one workgroup per CU, which few split pairs with
 // many partials each give, uses 512 (256 rows): the wider workgroups cost
-// dispatch time only when there are many of them.
+// dispatch time only when there are many of them.  A larger grid with at
+// most 8 columns (decode at G <= 8: many split pairs of few partials) runs
+// combine_pairs_kernel instead, one workgroup per pair.
 #include "lse_merge.h"
 
 namespace lbp {
@@ -103,12 +105,57 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
   store_bf16x4(a.out, row, c4, L > 0.f ? tot / L : f32x4_t{0.f, 0.f, 0.f, 0.f});
 }
 
+// One workgroup per split pair, for many pairs of few partials each: 32
+// threads per query column (one float4 of the row each), each merging its
+// column's partials in order, kPairUnroll in flight.  One workgroup instead
+// of one per column makes the grid 8 times smaller at G = 8.
+constexpr int kPairThreads = 256;
+constexpr int kPairUnroll = 8;
+constexpr int kPairMaxCols = kPairThreads / kLanesPerRow;   // 8
+
+__global__ __launch_bounds__(kPairThreads) void combine_pairs_kernel(CombineArgs a) {
+  const int nsplit = a.header[kHdrSplits];
+  const int4 e = reinterpret_cast<const int4*>(a.split_list)[blockIdx.x];
+  asm volatile("" ::"s"(e.x), "s"(e.y), "s"(e.z));   // keeps the entry load above the exit
+  if (int(blockIdx.x) >= nsplit) return;
+  const int p = e.x, first = e.y, cnt = e.z;
+  const int C = a.ncols;
+  const int q = threadIdx.x / kLanesPerRow;
+  const int c4 = threadIdx.x % kLanesPerRow;
+  if (q >= C) return;
+  const int g = p / a.batch, r = p % a.batch;
+  const float* lse = a.lse_part + int64_t(first) * C + q;
+  const f32x4_t* o = reinterpret_cast<const f32x4_t*>(a.o_part + (int64_t(first) * C + q) * kHeadDim);
+  const int64_t stride4 = int64_t(C) * kLanesPerRow;
+  float m = -INFINITY, l = 0.f;
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  for (int k0 = 0; k0 < cnt; k0 += kPairUnroll) {
+    float ls[kPairUnroll];
+    f32x4_t v[kPairUnroll];
+#pragma unroll
+    for (int u = 0; u < kPairUnroll; ++u) {
+      if (k0 + u < cnt) {
+        ls[u] = lse[int64_t(k0 + u) * C];
+        v[u] = o[int64_t(k0 + u) * stride4 + c4];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kPairUnroll; ++u)
+      if (k0 + u < cnt) merge_into(m, l, acc, ls[u], v[u]);
+  }
+  store_bf16x4(a.out, query_row(r, g, q, a.q_len, a.group, a.num_q_heads), c4,
+               l > 0.f ? acc / l : f32x4_t{0.f, 0.f, 0.f, 0.f});
+}
+
 }  // namespace
 
 hipError_t launch_combine(const CombineArgs& a, int max_split, hipStream_t s) {
   if (max_split <= 0) return hipSuccess;
   CombineArgs copy = a;
   void* args[] = {&copy};
+  if (int64_t(max_split) * a.ncols > kWideGrid && a.ncols <= kPairMaxCols)
+    return hipLaunchKernel(reinterpret_cast<const void*>(&combine_pairs_kernel), dim3(max_split),
+                           dim3(kPairThreads), args, 0, s);
   const bool wide = int64_t(max_split) * a.ncols <= kWideGrid;
   const void* fn = wide ? reinterpret_cast<const void*>(&combine_kernel<512>)
                         : reinterpret_cast<const void*>(&combine_kernel<256>);

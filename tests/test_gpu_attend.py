@@ -129,6 +129,75 @@ def test_attend_bin_shapes(gpu_lib, W, F):
     compare(case, out, oracle_pairs(case, 0, all_pairs(case)), f"tiny W={W} F={F}")
 
 
+@pytest.mark.parametrize("form,batch,W,group", [("wide", 1, 600, 8), ("pairs", 40, 400, 8),
+                                                ("columns", 40, 400, 16)])
+def test_combine_rounds_every_form(gpu_lib, form, batch, W, group):
+    """A pair split into more partials than one round of the combine's loads
+    takes, through each combine form: 512 threads per column when the
+    (entries x columns) grid has at most 256 workgroups (600 partials, 256
+    rows per round); otherwise one workgroup per pair when there are at most
+    8 columns (300 partials, 8 per round per thread); else 256 threads per
+    column (300 partials, 128 rows per round)."""
+    n_long = 600 if batch == 1 else 300
+    wcfg = dataclasses.replace(CONFIGS["skewed"], name=f"rounds-{form}", batch=batch,
+                               num_q_heads=group)
+    case = build_case(wcfg, lengths=[64 * n_long] + [64] * (batch - 1), num_workgroups=W,
+                      min_tiles=1)
+    assert_taskmap_matches(case)
+    tm = lbp.read_taskmap(case.plan_ws, case.info)
+    assert int(tm["pair_count"].max()) == n_long
+    grid = min(batch, W - 1) * group
+    expected = "wide" if grid <= 256 else "pairs" if group <= 8 else "columns"
+    assert expected == form
+    out = run_attend(case)
+    compare(case, out, oracle_pairs(case, 0, all_pairs(case)), f"combine {form}")
+
+
+@pytest.mark.parametrize("kv,q_len,entry", [("bf16", 1, "attend"), ("bf16", 1, "fused"),
+                                             ("bf16", 3, "attend"), ("bf16", 6, "fused"),
+                                             ("fp8_e4m3", 1, "attend"), ("fp8_e4m3", 1, "fp8q")])
+def test_all_requests_empty(gpu_lib, kv, q_len, entry):
+    """Every length zero (T = 0: no tile, no descriptor, every bin empty):
+    every output row is exactly zero, and nothing is read from a KV cache
+    (and scales) holding only NaN."""
+    base = CONFIGS["tiny"] if kv == "bf16" else CONFIGS["fp8"]
+    wcfg = dataclasses.replace(base, name=f"empty-{kv}", batch=3)
+    case = build_case(wcfg, lengths=[0, 0, 0], max_pages_per_seq=1, q_len=q_len, poison=False)
+    assert_taskmap_matches(case)
+    lay = case.wl.layers[0]
+    H, D = wcfg.num_kv_heads, 128
+    if kv == "bf16":
+        kc = torch.full((1, H, 64, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+        vc, ks, vs = kc.clone(), None, None
+    else:
+        kc = torch.full((1, H, 64, D), 0x7F, dtype=torch.uint8, device="cuda")   # e4m3 NaN
+        vc = kc.clone()
+        ks = torch.full((1, H, 64), float("nan"), dtype=torch.float32, device="cuda")
+        vs = ks.clone()
+    q = torch.randn((3, q_len, wcfg.num_q_heads, D), device="cuda").to(torch.bfloat16)
+    if q_len == 1:
+        q = q[:, 0].contiguous()
+    out = torch.full_like(q, float("nan"))
+    if entry == "fp8q":
+        codes, scale = quantize_query_e4m3(q)
+        lbp.lbp_attend_fp8q(case.cfg, case.info, case.plan_ws, codes, scale, kc, vc, ks, vs,
+                            case.split_ws, out)
+    else:
+        fn = lbp.lbp_attend if entry == "attend" else lbp.lbp_attend_fused
+        fn(case.cfg, case.info, case.plan_ws, q, kc, vc, ks, vs, case.split_ws, out)
+    torch.cuda.synchronize()
+    assert torch.equal(out, torch.zeros_like(out)), f"{kv} q_len={q_len} {entry}"
+
+
+@pytest.mark.parametrize("W,F", [(1, 1), (5, 1), (64, 1), (256, 4), (1024, 1)])
+def test_attend_bin_shapes(gpu_lib, W, F):
+    """Many splits per pair, one bin for everything, more bins than tiles."""
+    case = build_case(CONFIGS["tiny"], num_workgroups=W, min_tiles=F)
+    assert_taskmap_matches(case)
+    out = run_attend(case)
+    compare(case, out, oracle_pairs(case, 0, all_pairs(case)), f"tiny W={W} F={F}")
+
+
 @pytest.mark.parametrize("batch,W,wide", [(1, 600, True), (40, 400, False)])
 def test_combine_rounds_both_widths(gpu_lib, batch, W, wide):
     """A pair split into more partials than one round of the combine's loads
