@@ -519,12 +519,16 @@ __device__ inline int wave_slices(int t, int e, int stride) {
 // scalar loads, which complete on the scalar counter.  Looking up the next
 // slice's page then never waits for the KV loads still in flight (vector
 // loads complete in order, so a vector load of the page index would).
+// The physical page of the slice at token tok of request r (its last page's
+// for a slice past the end e, which loads nothing).
+__device__ inline int page_of(const AttendArgs& a, const int32_t* __restrict__ pt, int r, int tok,
+                              int e) {
+  const int pidx = (tok < e ? tok : e - 1) >> 6;
+  return pt[int64_t(r) * a.page_table_stride + pidx];
+}
 template <class Kv>
-__device__ inline SliceRsrc slice_rsrc(const AttendArgs& a, const int32_t* __restrict__ pt, int g,
-                                       int r, int tok, int e) {
+__device__ inline SliceRsrc slice_rsrc_at(const AttendArgs& a, int g, int tok, int e, int page) {
   const bool valid = tok < e;
-  const int pidx = (valid ? tok : e - 1) >> 6;
-  const int page = pt[int64_t(r) * a.page_table_stride + pidx];
   const int nvalid = valid ? min(kSlice, e - tok) : 0;
   const int64_t row = (int64_t(page) * a.num_kv_heads + g) * kPageTokens + (tok & (kPageTokens - 1));
   SliceRsrc rs;
@@ -538,6 +542,11 @@ __device__ inline SliceRsrc slice_rsrc(const AttendArgs& a, const int32_t* __res
     rs.vs = rs.v;
   }
   return rs;
+}
+template <class Kv>
+__device__ inline SliceRsrc slice_rsrc(const AttendArgs& a, const int32_t* __restrict__ pt, int g,
+                                       int r, int tok, int e) {
+  return slice_rsrc_at<Kv>(a, g, tok, e, page_of(a, pt, r, tok, e));
 }
 
 struct WaveState {
@@ -745,6 +754,11 @@ __device__ inline void attend_bin(const AttendArgs& a, const int32_t* __restrict
     const bool single = pair_count[p] == 1;
     const bool has_next = d + 1 < d_end;
     const int4 dn = descs[has_next ? d + 1 : d];
+    // the next descriptor's first slice of this wave and its page, looked up
+    // now so that the lookup completes during this descriptor's loop instead
+    // of delaying the prefetch after it
+    const int next_tok = (has_next ? dn.z : dn.w) + wave * kSlice;
+    const int next_page = page_of(a, pt, dn.y, next_tok, dn.w);
     // causal limit of this lane's column in multi-token verification: query
     // token j of the request sits at position L - q_len + j, L being the
     // end of the pair's last descriptor
@@ -848,11 +862,9 @@ __device__ inline void attend_bin(const AttendArgs& a, const int32_t* __restrict
     // so that its round loop is entered with exactly the loads outstanding
     // that it loops with and the compiler's wait counts stay exact.
     auto prefetch_next = [&]() {
-      const int first = has_next ? dn.z : dn.w;
 #pragma unroll
       for (int t = 0; t < kNB; ++t) Kv::load_q(qb[t], a, ql[t], dn.x, dn.y, grp);
-      Kv::template issue<kStaged>(buf[0],
-                                  slice_rsrc<Kv>(a, pt, dn.x, dn.y, first + wave * kSlice, dn.w),
+      Kv::template issue<kStaged>(buf[0], slice_rsrc_at<Kv>(a, dn.x, next_tok, dn.w, next_page),
                                   lane);
     };
     if (!kStaged && has_next) prefetch_next();
