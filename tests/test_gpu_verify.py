@@ -78,10 +78,13 @@ def test_verify_shapes_short_requests(gpu_lib, group, hkv, T):
     assert torch.all(out[0, :T - 1] == 0) if T > 1 else True
 
 
-@pytest.mark.parametrize("group,hkv,T", [(8, 2, 6), (8, 1, 8), (4, 2, 5), (16, 1, 4), (3, 3, 7)])
+@pytest.mark.parametrize("group,hkv,T", [(8, 2, 6), (8, 1, 8), (4, 2, 5), (16, 1, 4), (3, 3, 7),
+                                         (1, 1, 32), (1, 2, 40), (2, 1, 30), (1, 1, 64)])
 def test_verify_column_blocks(gpu_lib, group, hkv, T):
-    """More than 16 query columns (up to 64): the workgroup's waves split
-    into column blocks that each walk every KV slice of a descriptor."""
+    """More than 16 query columns (up to 64): two 16-column tiles per wave up
+    to 32, staged column blocks past that (6 waves up to 48, 8 beyond); with
+    one or two heads per group, nearly every column has its own causal
+    limit."""
     wcfg = dataclasses.replace(CONFIGS["tiny"], name=f"vb{group}x{T}", batch=6,
                                num_q_heads=group * hkv, num_kv_heads=hkv)
     case = build_case(wcfg, lengths=[1, 5, 64, 200, 777, 2100], num_workgroups=9, min_tiles=1,
