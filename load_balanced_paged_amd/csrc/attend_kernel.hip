@@ -891,8 +891,12 @@ __device__ inline void attend_bin(const AttendArgs& a, const int32_t* __restrict
       }
     }
     __syncthreads();
-    for (int idx = threadIdx.x; idx < C * kHeadDim; idx += kThreads) {
-      const int q = idx >> 7, dim = idx & (kHeadDim - 1);
+    // each thread merges four consecutive dims of one column (one float4 of
+    // every wave's row), so an 8-column descriptor takes one pass of 256
+    // threads; per dim the arithmetic is the same as one dim at a time
+    constexpr int kD4 = kHeadDim / 4;
+    for (int idx = threadIdx.x; idx < C * kD4; idx += kThreads) {
+      const int q = idx / kD4, d4 = idx % kD4;
       // the waves of q's column block hold it, as their column qc
       const int qblk = kStaged ? q / cpb : 0;
       const int qc = q - qblk * cpb;
@@ -903,32 +907,34 @@ __device__ inline void attend_bin(const AttendArgs& a, const int32_t* __restrict
       // a column with no visible token in this descriptor (possible only
       // under a causal limit) gives an empty partial: o = 0, lse = -inf
       const float Mu = kCausal ? finite_or_zero(M) : M;
-      float L = 0.f, o = 0.f;
+      float L = 0.f;
+      f32x4_t o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int w = 0; w < wpb; ++w) {
         const float* rw = rb + w * red_stride;
         const float c = __builtin_amdgcn_exp2f(rw[qc] - Mu);
         L += rw[16 * kNB + qc] * c;
-        o += rw[kRedHead + qc * kRedRow + dim] * c;
+        o += *reinterpret_cast<const f32x4_t*>(rw + kRedHead + qc * kRedRow + 4 * d4) * c;
       }
       const bool empty = kCausal && !(L > 0.f);
-      const float on = empty ? 0.f : o / L;
+      const f32x4_t on = empty ? f32x4_t{0.f, 0.f, 0.f, 0.f} : o / L;
       if (single) {
         // the pair's only descriptor: this is already the final output
         const int64_t row = kCausal ? query_row(r, g, q, a.q_len, G, a.num_q_heads)
                                     : int64_t(r) * a.num_q_heads + int64_t(g) * G + q;
-        static_cast<__bf16*>(a.out)[row * kHeadDim + dim] = static_cast<__bf16>(on);
+        store_bf16x4(a.out, row, d4, on);
       } else {
-        float* po = a.o_part + (int64_t(d) * C + q) * kHeadDim + dim;
+        float* po = a.o_part + (int64_t(d) * C + q) * kHeadDim + 4 * d4;
         float* pl = a.lse_part + int64_t(d) * C + q;
         const float lse = empty ? -INFINITY : M + __builtin_amdgcn_logf(L);
         if (a.fuse) {
           // merged inside this launch, possibly by a workgroup on another XCD
-          store_coherent(po, on);
-          if (dim == 0) store_coherent(pl, lse);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) store_coherent(po + j, on[j]);
+          if (d4 == 0) store_coherent(pl, lse);
         } else {
-          *po = on;
-          if (dim == 0) *pl = lse;
+          *reinterpret_cast<f32x4_t*>(po) = on;
+          if (d4 == 0) *pl = lse;
         }
       }
     }
@@ -1114,8 +1120,16 @@ __device__ void finish_split_pairs(const AttendArgs& a, const int4* __restrict__
 // on a faster CU simply drains more bins; every workgroup draws exactly one
 // ticket past the last bin, and the one holding the final ticket returns the
 // counter to zero for the next launch.
+// One workgroup runs per CU (persistent bins), so more waves per SIMD than
+// its own (waves / 4, rounded up) can never be resident.  Saying so pins the
+// compiler's occupancy target: otherwise its scheduler squeezes the slice
+// loop's registers toward occupancies that never occur, and whenever that
+// loop is the kernel's register peak it stops issuing the next slice ahead
+// of the current slice's math.
 template <class Kv, bool kCausal, int kStagedW, int kNB>
-__global__ __launch_bounds__((waves_of<Kv, kStagedW>() * 64)) void attend_kernel(
+__global__ __launch_bounds__((waves_of<Kv, kStagedW>() * 64))
+__attribute__((amdgpu_waves_per_eu((waves_of<Kv, kStagedW>() + 3) / 4,
+                                   (waves_of<Kv, kStagedW>() + 3) / 4))) void attend_kernel(
     AttendArgs a, const int32_t* __restrict__ page_table, const int4* __restrict__ descs,
     const int32_t* __restrict__ pair_count, const int32_t* __restrict__ bin_offset,
     const int32_t* __restrict__ pair_first, const int4* __restrict__ bin_first) {
