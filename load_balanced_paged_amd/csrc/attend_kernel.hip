@@ -167,32 +167,20 @@ __device__ inline void partners16(float x, float& lo, float& hi) {
   lo = a;   // the value of lane l & ~16
   hi = b;   // the value of lane l | 16
 }
-// kSwap: the lane swaps above, else cross-lane shuffles through the LDS
-// crossbar (measured faster for FP8 KV with a BF16 query, whose loop spends
-// its VALU slots on widening the codes).
-template <bool kSwap>
+// The column reductions over the four lane groups use the swaps above rather
+// than cross-lane shuffles through the LDS crossbar: measured faster in every
+// KV format.
 __device__ inline float wave_max_across_groups(float x) {
-  if constexpr (kSwap) {
-    float a, b;
-    partners32(x, a, b);
-    partners16(fmaxf(a, b), a, b);
-    return fmaxf(a, b);
-  } else {
-    x = fmaxf(x, __shfl_xor(x, 16, 64));
-    return fmaxf(x, __shfl_xor(x, 32, 64));
-  }
+  float a, b;
+  partners32(x, a, b);
+  partners16(fmaxf(a, b), a, b);
+  return fmaxf(a, b);
 }
-template <bool kSwap>
 __device__ inline float wave_sum_across_groups(float x) {
-  if constexpr (kSwap) {
-    float a, b;
-    partners32(x, a, b);
-    partners16(a + b, a, b);
-    return a + b;
-  } else {
-    x += __shfl_xor(x, 16, 64);
-    return x + __shfl_xor(x, 32, 64);
-  }
+  float a, b;
+  partners32(x, a, b);
+  partners16(a + b, a, b);
+  return a + b;
 }
 
 // ---------------------------------------------------------------------------
@@ -253,7 +241,6 @@ struct Bf16Kv {
   static constexpr bool kScaled = false;
   static constexpr bool kSplitP = LBP_BF16_SPLIT_P;   // P.V with P as BF16 hi + lo
   static constexpr int kWaves = LBP_BF16_WAVES;    // waves per workgroup
-  static constexpr bool kLaneSwap = true;          // column reductions by lane swaps
   struct Buf {
     i32x4_t k[4];   // K A-operand, one per 32-dim k-step
     i32x4_t v[4];   // V rows 4*grp+i, dims [8c, 8c+8)
@@ -324,7 +311,6 @@ struct Fp8Kv {
   // the FP8 tolerance leaves room for P in plain BF16, and this format needs
   // its issue slots for the code widening
   static constexpr bool kSplitP = false;
-  static constexpr bool kLaneSwap = false;
   // waves per workgroup: FP8 moves half the bytes per token, but 6 waves with
   // two slices each keep enough loads in flight, and fewer waves make each
   // descriptor's merge cheaper
@@ -415,8 +401,6 @@ struct Fp8Kv {
 // probabilities take the FP8 KV path above.
 struct Fp8KvQ8 : Fp8Kv {
   static constexpr int kWaves = LBP_FP8Q_WAVES;
-  // no code widening on the score side leaves VALU slots for lane swaps
-  static constexpr bool kLaneSwap = true;
   struct Q {
     i32x4_t c[2];   // codes of dims [32grp, 32grp + 32) of head n
     float scale;    // the head's Q scale (0 for columns past the group)
@@ -477,7 +461,6 @@ struct Staged {
   using Buf = StagedSlice<Kv>;
   using Q = typename Kv::Q;
   static constexpr bool kSplitP = Kv::kSplitP;
-  static constexpr bool kLaneSwap = true;
   static constexpr bool kScaled = Kv::kScaled;
   __device__ static Buf build(const typename Kv::Buf& b) {
     Buf t;
@@ -573,7 +556,7 @@ __device__ inline void consume(WaveState& st, const typename Kv::Buf& b, const t
     x[j] = (tok + 4 * grp + j < (kCausal ? min(e, lim) : e)) ? s[j] * ks[j] * scale_log2
                                                              : -INFINITY;
   float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-  mx = wave_max_across_groups<Kv::kLaneSwap>(mx);
+  mx = wave_max_across_groups(mx);
   const float m_new = fmaxf(st.m, mx);
   // without a causal limit every slice has a visible token in every column,
   // so the running max is finite after the first one
@@ -873,7 +856,7 @@ __device__ inline void attend_bin(const AttendArgs& a, const int32_t* __restrict
 #pragma unroll
     for (int t = 0; t < kNB; ++t) {
       const WaveState& w = st[t];
-      const float l = wave_sum_across_groups<kStaged || Kv::kLaneSwap>(w.l);
+      const float l = wave_sum_across_groups(w.l);
       if (n < tile_cols(t)) {
         const int c = 16 * t + n;   // the column within this wave's columns
         if (grp == 0) {
