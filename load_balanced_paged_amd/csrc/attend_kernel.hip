@@ -87,7 +87,7 @@ namespace {
 #ifndef LBP_KV_LOAD_AUX
 #define LBP_KV_LOAD_AUX 2
 #endif
-constexpr int kLoadAux = LBP_KV_LOAD_AUX;  // KV loads: 2 = non-temporal (read once, stream)
+constexpr int kLoadAux = LBP_KV_LOAD_AUX;  // KV and scale loads: 2 = non-temporal (read once, stream)
 constexpr int kSlice = 16;
 constexpr int kRedRow = kHeadDim + 4;  // padded LDS row (floats) for the merge
 // s_waitcnt operand (gfx9 encoding) waiting for vmcnt = 0 only
@@ -349,9 +349,9 @@ struct Fp8Kv {
       b.v[i] = __builtin_amdgcn_raw_buffer_load_b64(rs.v, (4 * grp + i) * kRowBytes + 8 * m, 0, kLoadAux);
       keep_order<kOrdered>();
     }
-    b.ks = __builtin_amdgcn_raw_buffer_load_b128(rs.ks, 16 * grp, 0, 0);
+    b.ks = __builtin_amdgcn_raw_buffer_load_b128(rs.ks, 16 * grp, 0, kLoadAux);
     keep_order<kOrdered>();
-    b.vs = __builtin_amdgcn_raw_buffer_load_b128(rs.vs, 16 * grp, 0, 0);
+    b.vs = __builtin_amdgcn_raw_buffer_load_b128(rs.vs, 16 * grp, 0, kLoadAux);
   }
 
   // Two e4m3 codes (the low or high 16-bit word of `codes`) to two bf16, exactly.
