@@ -543,8 +543,9 @@ struct WaveState {
 // so far keeps an empty state (m = -inf, l = 0, acc = 0).  Kv: the slice
 // format (a KV format, or its staged form).  kLazy: skip the rescale of the
 // running state when no lane's maximum grew; its factor would be exactly 1,
-// so the result is the same bit for bit.
-template <class Kv, bool kCausal, bool kLazy = false>
+// so the result is the same bit for bit.  kOneP: P as one BF16 value even
+// where the format asks for the pair (see below).
+template <class Kv, bool kCausal, bool kLazy = false, bool kOneP = false>
 __device__ inline void consume(WaveState& st, const typename Kv::Buf& b, const typename Kv::Q& q,
                                int tok, int e, float scale_log2, int grp, int lim) {
   f32x4_t s = Kv::scores(b, q);
@@ -571,11 +572,21 @@ __device__ inline void consume(WaveState& st, const typename Kv::Buf& b, const t
     for (int mb = 0; mb < 8; ++mb) st.acc[mb] *= alpha;
   }
   st.m = m_new;
+  // BF16 KV: P enters the P.V product as a BF16 pair (below), which the
+  // HBM-bound decode loop pays nothing for.  The verification instances past
+  // 16 columns, bound by their math, take one BF16 P instead (kOneP) and sum
+  // the same rounded values into l: the output is then an exact convex
+  // combination of the V rows under the rounded weights, whose error scales
+  // with |v - o| rather than |v| (a row with one dominant token stays
+  // exact).  The FP8 formats fold the V scale into P and keep one BF16 P with
+  // l from the unrounded values.
+  constexpr bool kSplit = Kv::kSplitP && !kOneP;
+  constexpr bool kRoundedSum = Kv::kSplitP && kOneP;
   float p[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) p[j] = __builtin_amdgcn_exp2f(x[j] - ref);
-  st.l += (p[0] + p[1]) + (p[2] + p[3]);
-  if constexpr (Kv::kSplitP) {
+  if constexpr (!kRoundedSum) st.l += (p[0] + p[1]) + (p[2] + p[3]);
+  if constexpr (kSplit) {
     const float pv[4] = {p[0] * vs[0], p[1] * vs[1], p[2] * vs[2], p[3] * vs[3]};
     i32x2_t pb2 = {int(pack_bf16(pv[0], pv[1])), int(pack_bf16(pv[2], pv[3]))};
     const i16x4_t pb = __builtin_bit_cast(i16x4_t, pb2);
@@ -599,6 +610,11 @@ __device__ inline void consume(WaveState& st, const typename Kv::Buf& b, const t
   } else {
     i32x2_t pb2 = {int(pack_bf16(p[0] * vs[0], p[1] * vs[1])),
                    int(pack_bf16(p[2] * vs[2], p[3] * vs[3]))};
+    if constexpr (kRoundedSum) {
+      const uint32_t h01 = uint32_t(pb2[0]), h23 = uint32_t(pb2[1]);
+      st.l += (__builtin_bit_cast(float, h01 << 16) + __builtin_bit_cast(float, h01 & 0xFFFF0000u)) +
+              (__builtin_bit_cast(float, h23 << 16) + __builtin_bit_cast(float, h23 & 0xFFFF0000u));
+    }
     const i16x4_t pb = __builtin_bit_cast(i16x4_t, pb2);
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb)
@@ -782,7 +798,7 @@ __device__ inline void attend_bin(const AttendArgs& a, const int32_t* __restrict
           const int tok = base + j * kSlice;
           if (tok >= t_end) break;
           const typename S::Buf b = BufImage<S>::load(stage + j * (kImg / 16), lane);
-          consume<S, kCausal, true>(st[0], b, qb[0], tok, t_end,
+          consume<S, kCausal, true, true>(st[0], b, qb[0], tok, t_end,
                                     Kv::score_scale(qb[0], a.scale_log2), grp, lim[0]);
         }
         base += step;
@@ -814,9 +830,9 @@ __device__ inline void attend_bin(const AttendArgs& a, const int32_t* __restrict
       const float sc0 = Kv::score_scale(qb[0], a.scale_log2);
       const float sc1 = kNB > 1 ? Kv::score_scale(qb[kNB - 1], a.scale_log2) : sc0;
       auto compute = [&](const typename Kv::Buf& cur) {
-        consume<Kv, kCausal>(st[0], cur, qb[0], tok, t_end, sc0, grp, lim[0]);
+        consume<Kv, kCausal, false, (kNB > 1)>(st[0], cur, qb[0], tok, t_end, sc0, grp, lim[0]);
         if constexpr (kNB > 1)
-          consume<Kv, kCausal>(st[1], cur, qb[1], tok, t_end, sc1, grp, lim[1]);
+          consume<Kv, kCausal, false, true>(st[1], cur, qb[1], tok, t_end, sc1, grp, lim[1]);
       };
       auto step_on = [&](const typename Kv::Buf& cur, typename Kv::Buf& nxt) {
         Kv::issue(nxt, slice_rsrc<Kv>(a, pt, g, r, tok + step, t_end), lane);
