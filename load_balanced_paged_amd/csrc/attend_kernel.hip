@@ -240,6 +240,7 @@ struct Bf16Kv {
   static constexpr int kRowBytes = kHeadDim * 2;
   static constexpr bool kScaled = false;
   static constexpr bool kSplitP = LBP_BF16_SPLIT_P;   // P.V with P as BF16 hi + lo
+  static constexpr bool kWidenK = false;              // K is BF16 already
   static constexpr int kWaves = LBP_BF16_WAVES;    // waves per workgroup
   struct Buf {
     i32x4_t k[4];   // K A-operand, one per 32-dim k-step
@@ -361,17 +362,23 @@ struct Fp8Kv {
                               __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(int(codes), 1.0f, kHiWord));
   }
 
+  // K operand of k-step k as eight BF16 values (exact)
+  template <class B>
+  __device__ static i32x4_t k_bf16(const B& b, int k) {
+    uint32_t c0 = b.k[k >> 1][2 * (k & 1)], c1 = b.k[k >> 1][2 * (k & 1) + 1];
+    return i32x4_t{int(widen2<false>(c0)), int(widen2<true>(c0)), int(widen2<false>(c1)),
+                   int(widen2<true>(c1))};
+  }
+  // the staged image may hold K already widened (Fp8KvQ8 scores on the codes)
+  static constexpr bool kWidenK = true;
+
   template <class B>
   __device__ static f32x4_t scores(const B& b, const Q& q) {
     f32x4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      uint32_t c0 = b.k[k >> 1][2 * (k & 1)], c1 = b.k[k >> 1][2 * (k & 1) + 1];
-      i32x4_t w = {int(widen2<false>(c0)), int(widen2<true>(c0)), int(widen2<false>(c1)),
-                   int(widen2<true>(c1))};
-      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, w), q.v[k], s, 0,
-                                                  0, 0);
-    }
+    for (int k = 0; k < 4; ++k)
+      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, k_bf16(b, k)),
+                                                  q.v[k], s, 0, 0, 0);
     return s;
   }
   __device__ static f32x4_t k_scales(const Buf& b) { return __builtin_bit_cast(f32x4_t, b.ks); }
@@ -401,6 +408,7 @@ struct Fp8Kv {
 // probabilities take the FP8 KV path above.
 struct Fp8KvQ8 : Fp8Kv {
   static constexpr int kWaves = LBP_FP8Q_WAVES;
+  static constexpr bool kWidenK = false;
   struct Q {
     i32x4_t c[2];   // codes of dims [32grp, 32grp + 32) of head n
     float scale;    // the head's Q scale (0 for columns past the group)
@@ -443,7 +451,7 @@ struct Fp8KvQ8 : Fp8Kv {
 // the eight P.V A operands already built (for FP8: already widened), and the
 // FP8 scales.  The wave that loads a slice builds this once; every column
 // block then reads it ready for the MFMAs.  128 bytes per lane in every
-// format.
+// format (160 in the widened-K form below).
 template <class Kv, bool kScaled = Kv::kScaled>
 struct StagedSlice {
   decltype(Kv::Buf::k) k;
@@ -456,16 +464,31 @@ struct StagedSlice<Kv, true> {
   i32x4_t ks, vs;
 };
 
-template <class Kv>
+// FP8 KV with a BF16 query, K widened to BF16 once by the loading wave
+// instead of once per column block: 160 bytes per lane.
+struct StagedSliceWideK {
+  i32x4_t k[4];   // K operand per 32-dim k-step, as BF16
+  i16x4_t v[8];
+  i32x4_t ks, vs;
+};
+
+// kWide: the image holds K widened (StagedSliceWideK); only where the ring
+// of 2 x waves images still fits the CU's LDS.
+template <class Kv, bool kWide = false>
 struct Staged {
-  using Buf = StagedSlice<Kv>;
+  using Buf = std::conditional_t<kWide, StagedSliceWideK, StagedSlice<Kv>>;
   using Q = typename Kv::Q;
   static constexpr bool kSplitP = Kv::kSplitP;
   static constexpr bool kScaled = Kv::kScaled;
   __device__ static Buf build(const typename Kv::Buf& b) {
     Buf t;
+    if constexpr (kWide) {
 #pragma unroll
-    for (int i = 0; i < int(sizeof(t.k) / sizeof(t.k[0])); ++i) t.k[i] = b.k[i];
+      for (int k = 0; k < 4; ++k) t.k[k] = Kv::k_bf16(b, k);
+    } else {
+#pragma unroll
+      for (int i = 0; i < int(sizeof(t.k) / sizeof(t.k[0])); ++i) t.k[i] = b.k[i];
+    }
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb) t.v[mb] = Kv::v_operand(b, mb);
     if constexpr (kScaled) {
@@ -474,7 +497,18 @@ struct Staged {
     }
     return t;
   }
-  __device__ static f32x4_t scores(const Buf& b, const Q& q) { return Kv::scores(b, q); }
+  __device__ static f32x4_t scores(const Buf& b, const Q& q) {
+    if constexpr (kWide) {
+      f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, b.k[k]), q.v[k],
+                                                    s, 0, 0, 0);
+      return s;
+    } else {
+      return Kv::scores(b, q);
+    }
+  }
   __device__ static f32x4_t k_scales(const Buf& b) {
     if constexpr (kScaled) return __builtin_bit_cast(f32x4_t, b.ks);
     else return f32x4_t{1.f, 1.f, 1.f, 1.f};
@@ -632,6 +666,12 @@ __device__ inline void consume(WaveState& st, const typename Kv::Buf& b, const t
 constexpr int kStagedWaves = 8;
 constexpr int kStagedWaves33To48 = 6;
 
+// The staged form of format Kv at kStagedW waves: K widened in the image
+// where the format allows it and the ring of 2 x 6 images (120 KB) fits;
+// at 8 waves it would need the CU's whole 160 KB.
+template <class Kv, int kStagedW>
+using StagedOf = Staged<Kv, Kv::kWidenK && kStagedW == kStagedWaves33To48>;
+
 // kStagedW: 0 for the decode and causal instances (the format's own wave
 // count), else the staged instance's wave count.
 template <class Kv, int kStagedW>
@@ -779,7 +819,7 @@ __device__ inline void attend_bin(const AttendArgs& a, const int32_t* __restrict
     // buf[0] already holds (or is loading) this wave's first slice of d; a
     // slice past t_end loads nothing
     if constexpr (kStaged) {
-      using S = Staged<Kv>;
+      using S = StagedOf<Kv, kStagedW>;
       constexpr int kImg = BufImage<S>::kBytes;
       i32x4_t* ring = reinterpret_cast<i32x4_t*>(smem);   // [2 stages][kWaves slices][image]
       int base = t_begin;          // round: tokens [base, base + step), slice w at base + 16 w
@@ -1210,7 +1250,10 @@ void pick_instance(bool causal, int tiles, int staged_w, const void** fn, int* w
                  : reinterpret_cast<const void*>(&attend_kernel<Kv, false, 0, 1>);
   }
   *waves = staged_w > 0 ? staged_w : Kv::kWaves;
-  if (staged_w > 0) *ring = 2 * size_t(staged_w) * BufImage<Staged<Kv>>::kBytes;
+  if (staged_w == kStagedWaves)
+    *ring = 2 * size_t(staged_w) * BufImage<StagedOf<Kv, kStagedWaves>>::kBytes;
+  else if (staged_w == kStagedWaves33To48)
+    *ring = 2 * size_t(staged_w) * BufImage<StagedOf<Kv, kStagedWaves33To48>>::kBytes;
 }
 
 hipError_t launch_attend(const AttendArgs& a, AttendKind kind, int grid, hipStream_t s) {
