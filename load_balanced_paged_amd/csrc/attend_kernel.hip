@@ -9,11 +9,13 @@
 // a relaunch.
 //
 // gfx950 mapping (our design, not the pages'):
-//  * A workgroup is 8 waves.  A descriptor's tokens are cut into 16-token
-//    slices (a slice never crosses a 64-token page because descriptors start
-//    on page boundaries); slice i goes to wave i % 8.  Each wave keeps its
-//    own running max, sum and output for the group, so there is no barrier
-//    inside a descriptor; the 8 states are merged through LDS at its end.
+//  * A workgroup is W waves (8 for BF16 KV and for FP8 KV with an FP8
+//    query, 6 for FP8 KV with a BF16 query).  A descriptor's tokens are cut
+//    into 16-token slices (a slice never crosses a 64-token page because
+//    descriptors start on page boundaries); slice i goes to wave i % W.  Each
+//    wave keeps its own running max, sum and output for the group, so there
+//    is no barrier inside a descriptor; the W states are merged through LDS
+//    at its end.
 //  * Scores use MFMA 16x16x32 bf16 with the 16 slice tokens as rows and the
 //    query heads as columns (S^T = K Q^T; G <= 16 heads, unused columns are
 //    zero).  P.V uses MFMA 16x16x16 bf16 as O^T = V^T P^T, whose B operand
