@@ -13,7 +13,7 @@ import torch
 import load_balanced_paged_amd as lbp
 import oracle
 from gpu_support import (all_pairs, assert_taskmap_matches, bf16_to_f64, bits, build_case,
-                         compare, oracle_pairs, run_attend, sample_pairs, say)
+                         compare, oracle_layer, oracle_pairs, run_attend, sample_pairs, say)
 from workloads import CONFIGS, quantize_query_e4m3
 
 pytestmark = pytest.mark.gpu
@@ -29,21 +29,28 @@ def test_attend_full_parity(gpu_lib, name):
 
 
 def test_attend_mixed_eight_layers(gpu_lib):
-    """One task map reused by 8 layers with different KV; sampled pairs per layer."""
+    """One task map reused by 8 layers with different KV: every pair of the
+    first and the last layer against the oracle (the relative RMS over the
+    whole output tensor), sampled pairs of the layers between."""
     case = build_case(CONFIGS["mixed"], layers=8)
     assert_taskmap_matches(case)
-    pairs = sample_pairs(case, 12)
     outs = [run_attend(case, layer) for layer in range(8)]
-    for layer in (0, 3, 7):
-        compare(case, outs[layer], oracle_pairs(case, layer, pairs), f"mixed layer {layer}")
+    pairs = sample_pairs(case, 12)
+    for layer in range(8):
+        full = layer in (0, 7)
+        ref = oracle_layer(case, layer, None if full else pairs)
+        compare(case, outs[layer], ref, f"mixed layer {layer} {'all pairs' if full else 'sampled'}")
     assert not torch.equal(outs[0], outs[7])
 
 
 def test_attend_fp8_parity(gpu_lib):
+    """Every (KV head, request) pair of the FP8 workload (1024 pairs, up to
+    262144 tokens): whole-tensor relative RMS and the per-pair bound, which
+    a lost or zeroed long row cannot pass."""
     case = build_case(CONFIGS["fp8"])
     assert_taskmap_matches(case)
     out = run_attend(case)
-    compare(case, out, oracle_pairs(case, 0, sample_pairs(case, 12)), "fp8")
+    compare(case, out, oracle_layer(case, 0), "fp8 all pairs")
 
 
 def test_attend_fp8_small_full(gpu_lib):
@@ -153,69 +160,6 @@ def test_combine_rounds_every_form(gpu_lib, form, batch, W, group):
     compare(case, out, oracle_pairs(case, 0, all_pairs(case)), f"combine {form}")
 
 
-@pytest.mark.parametrize("kv,q_len,entry", [("bf16", 1, "attend"), ("bf16", 1, "fused"),
-                                             ("bf16", 3, "attend"), ("bf16", 6, "fused"),
-                                             ("fp8_e4m3", 1, "attend"), ("fp8_e4m3", 1, "fp8q")])
-def test_all_requests_empty(gpu_lib, kv, q_len, entry):
-    """Every length zero (T = 0: no tile, no descriptor, every bin empty):
-    every output row is exactly zero, and nothing is read from a KV cache
-    (and scales) holding only NaN."""
-    base = CONFIGS["tiny"] if kv == "bf16" else CONFIGS["fp8"]
-    wcfg = dataclasses.replace(base, name=f"empty-{kv}", batch=3)
-    case = build_case(wcfg, lengths=[0, 0, 0], max_pages_per_seq=1, q_len=q_len, poison=False)
-    assert_taskmap_matches(case)
-    lay = case.wl.layers[0]
-    H, D = wcfg.num_kv_heads, 128
-    if kv == "bf16":
-        kc = torch.full((1, H, 64, D), float("nan"), dtype=torch.bfloat16, device="cuda")
-        vc, ks, vs = kc.clone(), None, None
-    else:
-        kc = torch.full((1, H, 64, D), 0x7F, dtype=torch.uint8, device="cuda")   # e4m3 NaN
-        vc = kc.clone()
-        ks = torch.full((1, H, 64), float("nan"), dtype=torch.float32, device="cuda")
-        vs = ks.clone()
-    q = torch.randn((3, q_len, wcfg.num_q_heads, D), device="cuda").to(torch.bfloat16)
-    if q_len == 1:
-        q = q[:, 0].contiguous()
-    out = torch.full_like(q, float("nan"))
-    if entry == "fp8q":
-        codes, scale = quantize_query_e4m3(q)
-        lbp.lbp_attend_fp8q(case.cfg, case.info, case.plan_ws, codes, scale, kc, vc, ks, vs,
-                            case.split_ws, out)
-    else:
-        fn = lbp.lbp_attend if entry == "attend" else lbp.lbp_attend_fused
-        fn(case.cfg, case.info, case.plan_ws, q, kc, vc, ks, vs, case.split_ws, out)
-    torch.cuda.synchronize()
-    assert torch.equal(out, torch.zeros_like(out)), f"{kv} q_len={q_len} {entry}"
-
-
-@pytest.mark.parametrize("W,F", [(1, 1), (5, 1), (64, 1), (256, 4), (1024, 1)])
-def test_attend_bin_shapes(gpu_lib, W, F):
-    """Many splits per pair, one bin for everything, more bins than tiles."""
-    case = build_case(CONFIGS["tiny"], num_workgroups=W, min_tiles=F)
-    assert_taskmap_matches(case)
-    out = run_attend(case)
-    compare(case, out, oracle_pairs(case, 0, all_pairs(case)), f"tiny W={W} F={F}")
-
-
-@pytest.mark.parametrize("batch,W,wide", [(1, 600, True), (40, 400, False)])
-def test_combine_rounds_both_widths(gpu_lib, batch, W, wide):
-    """A pair split into more partials than one round of the combine's loads
-    takes: 600 partials through the 512-thread form (a grid of at most 256
-    workgroups, 256 rows per round) and 300 through the 256-thread form
-    (128 rows per round)."""
-    n_long = 600 if batch == 1 else 300
-    wcfg = dataclasses.replace(CONFIGS["skewed"], name=f"rounds{batch}", batch=batch)
-    case = build_case(wcfg, lengths=[64 * n_long] + [64] * (batch - 1), num_workgroups=W,
-                      min_tiles=1)
-    assert_taskmap_matches(case)
-    tm = lbp.read_taskmap(case.plan_ws, case.info)
-    assert int(tm["pair_count"].max()) == n_long
-    assert (min(batch, W - 1) * wcfg.num_q_heads <= 256) == wide
-    out = run_attend(case)
-    compare(case, out, oracle_pairs(case, 0, all_pairs(case)), f"combine rounds B={batch}")
-
-
 @pytest.mark.parametrize("policy,param", [(lbp.LBP_POLICY_STATIC_SPLITS, 1),
                                           (lbp.LBP_POLICY_STATIC_SPLITS, 7),
                                           (lbp.LBP_POLICY_STATIC_CHUNK, 2)])
@@ -277,8 +221,10 @@ def test_traced_run_records_every_workgroup(gpu_lib):
     tm = lbp.read_taskmap(case.plan_ws, case.info)
     assert np.all(t[:, 1] >= t[:, 0]) and np.all(t[:, 0] > 0)
     assert np.array_equal(t[:, 3], np.diff(tm["bin_offset"]))
-    xcc = t[:, 2] >> 32
-    assert len(set(xcc.tolist())) >= 1
+    # MI355X has 8 XCDs; 256 workgroups (one per CU) land on more than one
+    xcc = set((t[:, 2] >> 32).tolist())
+    assert xcc <= set(range(8)), xcc
+    assert case.info.num_bins < 8 or len(xcc) > 1, xcc
 
 
 def test_workspace_reuse_across_batches(gpu_lib):

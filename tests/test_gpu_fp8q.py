@@ -13,7 +13,7 @@ import torch
 
 import load_balanced_paged_amd as lbp
 import oracle
-from gpu_support import all_pairs, build_case, compare, oracle_pairs, sample_pairs, say
+from gpu_support import all_pairs, build_case, compare, oracle_layer, oracle_pairs, say
 from workloads import CONFIGS, TABLE3, quantize_query_e4m3
 
 pytestmark = pytest.mark.gpu
@@ -30,10 +30,11 @@ def run_fp8q(case, layer=0):
     return out, q64
 
 
-def test_fp8q_fp8_workload_sampled(gpu_lib):
+def test_fp8q_fp8_workload_all_pairs(gpu_lib):
+    """Every pair of the FP8 workload with the FP8 query."""
     case = build_case(CONFIGS["fp8"])
     out, q64 = run_fp8q(case)
-    compare(case, out, oracle_pairs(case, 0, sample_pairs(case, 12), q64), "fp8q fp8")
+    compare(case, out, oracle_layer(case, 0, q64=q64), "fp8q fp8 all pairs")
 
 
 def test_fp8q_small_ragged_all_rows(gpu_lib):

@@ -16,7 +16,7 @@ import torch
 
 import load_balanced_paged_amd as lbp
 from gpu_support import (all_pairs, assert_taskmap_matches, bf16_to_f64, build_case, compare,
-                         oracle_pairs, run_attend, sample_pairs, say)
+                         oracle_layer, oracle_pairs, run_attend, sample_pairs, say)
 from workloads import CONFIGS
 
 pytestmark = pytest.mark.gpu
@@ -104,7 +104,8 @@ def test_fused_mixed_layers_and_fp8(gpu_lib):
     for layer in range(2):
         for _ in range(3):
             got = fused(case, layer)
-        compare(case, got, oracle_pairs(case, layer, pairs), f"fused mixed layer {layer}")
+        ref = oracle_layer(case, layer, None if layer == 0 else pairs)
+        compare(case, got, ref, f"fused mixed layer {layer}")
         assert_close_to_two_launch(got, run_attend(case, layer))
     assert_counters_zero(case)
     wcfg = dataclasses.replace(CONFIGS["fp8"], name="fp8-fused", batch=5)
