@@ -15,7 +15,8 @@
  * Conventions for every function below:
  *  - Pointers named *_dev are device pointers; everything else is host
  *    memory.  The caller allocates and owns every buffer; the library keeps
- *    no device allocation and no per-call state.
+ *    no per-call state and no device memory of its own, except the fixed
+ *    split-buffer array of lbp_attend_noalloc.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *    Every launching call is asynchronous on that stream, performs no
  *    host<->device copy and no synchronisation, so it can be captured into
@@ -54,6 +55,9 @@ extern "C" {
 #define LBP_MAX_GROUP 16
 #define LBP_MAX_QUERY_COLUMNS 64 /* (Hq / H_kv) * q_len */
 #define LBP_PLAN_MAGIC 0x4C425031u /* "LBP1" */
+/* Size of the fixed device array that lbp_attend_noalloc keeps its split
+ * buffer in, one per GPU the library runs on (held until the process ends). */
+#define LBP_NOALLOC_SCRATCH_BYTES (32u << 20)
 
 typedef enum lbp_status {
   LBP_OK = 0,
@@ -61,7 +65,9 @@ typedef enum lbp_status {
   LBP_ERR_UNSUPPORTED = 2,         /* head_dim != 128, page != 64, group * q_len > 64 */
   LBP_ERR_WORKSPACE_TOO_SMALL = 3, /* a caller workspace is below the query */
   LBP_ERR_MISMATCH = 4,            /* plan info does not match the config */
-  LBP_ERR_HIP = 5                  /* the HIP runtime refused a launch/query */
+  LBP_ERR_HIP = 5,                 /* the HIP runtime refused a launch/query */
+  LBP_ERR_SCRATCH_LIMIT = 6        /* lbp_attend_noalloc: the split buffer the call needs is
+                                      larger than LBP_NOALLOC_SCRATCH_BYTES */
 } lbp_status;
 
 typedef enum lbp_kv_dtype { LBP_KV_BF16 = 0, LBP_KV_FP8_E4M3 = 1 } lbp_kv_dtype;
@@ -327,6 +333,30 @@ lbp_status lbp_attend_traced(const lbp_config* cfg, const lbp_plan_info* info,
                              const void* v_cache_dev, const float* k_scale_dev,
                              const float* v_scale_dev, void* split_ws_dev, size_t split_ws_bytes,
                              void* out_dev, uint64_t* trace_dev, void* stream);
+
+/* lbp_attend for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * The same two launches, with the same results bit for bit, but the split
+ * buffer lives in a fixed device array of LBP_NOALLOC_SCRATCH_BYTES that the
+ * library holds on every GPU it runs on (until the process ends) instead of
+ * a caller workspace.  The caller still passes the plan workspace (the input
+ * lbp_plan filled), the inputs and the output.  The call allocates nothing:
+ * no hipMalloc, hipFree or allocating library routine.  Its first call on a
+ * device looks up that device's copy of the array (hipGetSymbolAddress),
+ * with the device current.  Nothing in the array needs to start at zero:
+ * every partial the combine reads is written by the same call's attention
+ * kernel first.  Every call on one GPU shares that GPU's array and leaves the
+ * last call's partials in it, so calls that overlap on one GPU (other
+ * streams, other threads) race and give wrong results: order them on one
+ * stream.  A plan whose split buffer (max_desc x C x 128 x 4 + max_desc x C x
+ * 4 bytes, 256-aligned, C = G * q_len; see lbp_query_workspace) exceeds
+ * LBP_NOALLOC_SCRATCH_BYTES returns LBP_ERR_SCRATCH_LIMIT and launches
+ * nothing.  Other arguments, guards and errors as for lbp_attend. */
+lbp_status lbp_attend_noalloc(const lbp_config* cfg, const lbp_plan_info* info,
+                              const void* plan_ws_dev, const void* q_dev,
+                              const void* k_cache_dev, const void* v_cache_dev,
+                              const float* k_scale_dev, const float* v_scale_dev, void* out_dev,
+                              void* stream);
 
 lbp_status lbp_combine(const lbp_config* cfg, const lbp_plan_info* info,
                        const void* plan_ws_dev, const void* split_ws_dev,

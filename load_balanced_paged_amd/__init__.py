@@ -23,6 +23,8 @@ LBP_ERR_UNSUPPORTED = 2
 LBP_ERR_WORKSPACE_TOO_SMALL = 3
 LBP_ERR_MISMATCH = 4
 LBP_ERR_HIP = 5
+LBP_ERR_SCRATCH_LIMIT = 6
+NOALLOC_SCRATCH_BYTES = 32 << 20   # LBP_NOALLOC_SCRATCH_BYTES
 
 LBP_KV_BF16 = 0
 LBP_KV_FP8_E4M3 = 1
@@ -39,7 +41,7 @@ EXPORTED_SYMBOLS = (
     "lbp_status_string", "lbp_version", "lbp_query_workspace", "lbp_plan", "lbp_plan_static",
     "lbp_plan_layout", "lbp_attend", "lbp_attend_fused", "lbp_attend_partials",
     "lbp_attend_traced", "lbp_attend_fp8q", "lbp_prologue",
-    "lbp_combine", "lbp_read_stream",
+    "lbp_combine", "lbp_read_stream", "lbp_attend_noalloc",
 )
 
 
@@ -110,7 +112,8 @@ class LbpError(RuntimeError):
 
 _lib = None
 _STATUS_NAMES = {0: "LBP_OK", 1: "LBP_ERR_INVALID_ARG", 2: "LBP_ERR_UNSUPPORTED",
-                 3: "LBP_ERR_WORKSPACE_TOO_SMALL", 4: "LBP_ERR_MISMATCH", 5: "LBP_ERR_HIP"}
+                 3: "LBP_ERR_WORKSPACE_TOO_SMALL", 4: "LBP_ERR_MISMATCH", 5: "LBP_ERR_HIP",
+                 6: "LBP_ERR_SCRATCH_LIMIT"}
 
 
 def status_name(s: int) -> str:
@@ -144,6 +147,7 @@ def load(path: str = LIB_PATH):
         "lbp_prologue": (I32, [cfgp, I32, ctypes.POINTER(lbp_prologue_args), P]),
         "lbp_combine": (I32, [cfgp, infop, P, P, SZ, P, P]),
         "lbp_read_stream": (I32, [P, SZ, P, I32, P]),
+        "lbp_attend_noalloc": (I32, [cfgp, infop, P, P, P, P, P, P, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -275,6 +279,18 @@ def lbp_attend_fused(cfg, info, plan_ws, q, k_cache, v_cache, k_scale, v_scale, 
                      stream=None):
     _attend(load().lbp_attend_fused, "lbp_attend_fused", cfg, info, plan_ws, q, k_cache, v_cache,
             k_scale, v_scale, split_ws, out, stream)
+
+
+def lbp_attend_noalloc(cfg, info, plan_ws, q, k_cache, v_cache, k_scale, v_scale, out,
+                       stream=None):
+    """lbp_attend with the split buffer in the library's fixed device array
+    (no workspace argument; nothing is allocated)."""
+    import torch
+    kp, vp, ksp, vsp = _kv_ptrs(cfg, k_cache, v_cache, k_scale, v_scale)
+    _check(load().lbp_attend_noalloc(ctypes.byref(cfg), ctypes.byref(info),
+                                     _ptr(plan_ws, "plan_ws"), _ptr(q, "q", torch.bfloat16),
+                                     kp, vp, ksp, vsp, _ptr(out, "out", torch.bfloat16),
+                                     _stream(stream)), "lbp_attend_noalloc")
 
 
 def lbp_attend_fp8q(cfg, info, plan_ws, q_codes, q_scale, k_cache, v_cache, k_scale, v_scale,

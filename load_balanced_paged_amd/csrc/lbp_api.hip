@@ -4,13 +4,41 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "lbp_internal.h"
+
+// The split buffer of lbp_attend_noalloc: one fixed array per GPU, which the
+// HIP runtime places in each device's memory when it loads the library's
+// code object there.  In host code this name is only a stand-in for the
+// symbol: kernels and copies receive the device address that
+// hipGetSymbolAddress gives for the current device.
+static __device__ __align__(256) unsigned char scratch[LBP_NOALLOC_SCRATCH_BYTES];
 
 namespace lbp {
 namespace {
 
 constexpr int kMaxDevices = 64;
 int g_cu_count[kMaxDevices];  // cached per device; 0 = not queried yet
+
+std::mutex g_scratch_mutex;
+void* g_scratch_addr[kMaxDevices];  // device address of `scratch`; null = not looked up yet
+
+// The current device's copy of `scratch`, looked up once per device (with
+// that device current, on its first no-allocation call).
+lbp_status scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return LBP_ERR_HIP;
+  if (dev >= kMaxDevices) return LBP_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return LBP_ERR_HIP;
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return LBP_OK;
+}
 
 lbp_status cu_count(int* out) {
   int dev = 0;
@@ -182,6 +210,7 @@ const char* lbp_status_string(lbp_status s) {
     case LBP_ERR_WORKSPACE_TOO_SMALL: return "LBP_ERR_WORKSPACE_TOO_SMALL";
     case LBP_ERR_MISMATCH: return "LBP_ERR_MISMATCH";
     case LBP_ERR_HIP: return "LBP_ERR_HIP";
+    case LBP_ERR_SCRATCH_LIMIT: return "LBP_ERR_SCRATCH_LIMIT";
   }
   return "LBP_ERR_UNKNOWN";
 }
@@ -361,6 +390,29 @@ lbp_status lbp_attend(const lbp_config* cfg, const lbp_plan_info* info, const vo
                       size_t split_ws_bytes, void* out_dev, void* stream) {
   return attend_full(cfg, info, plan_ws_dev, q_dev, k_cache_dev, v_cache_dev, k_scale_dev,
                      v_scale_dev, split_ws_dev, split_ws_bytes, out_dev, nullptr, false, stream);
+}
+
+lbp_status lbp_attend_noalloc(const lbp_config* cfg, const lbp_plan_info* info,
+                              const void* plan_ws_dev, const void* q_dev,
+                              const void* k_cache_dev, const void* v_cache_dev,
+                              const float* k_scale_dev, const float* v_scale_dev, void* out_dev,
+                              void* stream) {
+  // every guard of lbp_attend that needs no device comes first, then the
+  // size of the split buffer against the fixed array, then its address
+  lbp_status st = check_config(cfg);
+  if (st != LBP_OK) return st;
+  if ((st = check_info(cfg, info)) != LBP_OK) return st;
+  if (!plan_ws_dev || !q_dev || !k_cache_dev || !v_cache_dev || !out_dev)
+    return LBP_ERR_INVALID_ARG;
+  if (cfg->kv_dtype == LBP_KV_FP8_E4M3 && (!k_scale_dev || !v_scale_dev))
+    return LBP_ERR_INVALID_ARG;
+  if (split_bytes(info->max_desc, ncols_of(cfg)) > LBP_NOALLOC_SCRATCH_BYTES)
+    return LBP_ERR_SCRATCH_LIMIT;
+  void* split = nullptr;
+  if ((st = scratch_address(&split)) != LBP_OK) return st;
+  return attend_full(cfg, info, plan_ws_dev, q_dev, k_cache_dev, v_cache_dev, k_scale_dev,
+                     v_scale_dev, split, LBP_NOALLOC_SCRATCH_BYTES, out_dev, nullptr, false,
+                     stream);
 }
 
 lbp_status lbp_attend_fused(const lbp_config* cfg, const lbp_plan_info* info,

@@ -213,6 +213,33 @@ def test_attend_guards(lib):
     assert st == lbp.LBP_ERR_MISMATCH
 
 
+def test_noalloc_guards(lib):
+    """lbp_attend_noalloc checks everything lbp_attend checks, then the split
+    buffer the plan needs against its fixed array, before any device call."""
+    c = cfg()
+    info = good_info(c)
+
+    def call(config=c, inf=info, plan_ws=FAKE, q=FAKE, k=FAKE, v=FAKE, ks=None, vs=None, out=FAKE):
+        return lib.lbp_attend_noalloc(ctypes.byref(config), ctypes.byref(inf), plan_ws, q, k, v,
+                                      ks, vs, out, None)
+    bad = good_info(c)
+    bad.magic = 0
+    assert call(inf=bad) == lbp.LBP_ERR_MISMATCH
+    assert call(q=None) == lbp.LBP_ERR_INVALID_ARG
+    assert call(out=None) == lbp.LBP_ERR_INVALID_ARG
+    assert call(plan_ws=None) == lbp.LBP_ERR_INVALID_ARG
+    c8 = cfg(kv_dtype="fp8_e4m3")
+    assert call(config=c8, inf=good_info(c8)) == lbp.LBP_ERR_INVALID_ARG   # FP8 without scales
+    assert call(config=cfg(head_dim=64)) == lbp.LBP_ERR_UNSUPPORTED
+    # 64 columns per slot: 1016 slots fit in 32 MiB, 1100 do not
+    c64 = cfg(q_len=8)
+    assert call(config=c64, inf=good_info(c64, max_desc=1100)) == lbp.LBP_ERR_SCRATCH_LIMIT
+    assert lbp.lbp_status_string(lbp.LBP_ERR_SCRATCH_LIMIT) == "LBP_ERR_SCRATCH_LIMIT"
+    # the decode workloads' plans fit: FP8 (128 requests x 8 KV heads + 255 slots of 8 columns)
+    st, _, sb = query(cfg(max_batch=128))
+    assert st == lbp.LBP_OK and sb <= lbp.NOALLOC_SCRATCH_BYTES
+
+
 def test_fp8q_guards(lib):
     c = cfg()
     info = good_info(c)
