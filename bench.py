@@ -106,11 +106,21 @@ class Bench:
             plan_ws = torch.empty(pb, dtype=torch.uint8, device="cuda")
             split_ws = torch.empty(sb, dtype=torch.uint8, device="cuda")
             if policy == lbp.LBP_POLICY_DYNAMIC:
-                info = lbp.lbp_plan(self.cfg, self.seq, self.table, plan_ws)
+                # param > 0: the minimum-work floor F for this plan
+                cfg = self.cfg
+                if param > 0:
+                    cfg = lbp.lbp_config.from_buffer_copy(self.cfg)
+                    cfg.min_tiles_per_bin = param
+                info = lbp.lbp_plan(cfg, self.seq, self.table, plan_ws)
             else:
                 info = lbp.lbp_plan_static(self.cfg, policy, param, self.seq, self.table, plan_ws)
             self.plans[key] = (info, plan_ws, split_ws)
         return self.plans[key]
+
+    def used_bins(self, F=0):
+        """U, the bins with work, of the dynamic plan with floor F (header word 8)."""
+        info, plan_ws, _ = self.plan(self.lbp.LBP_POLICY_DYNAMIC, F)
+        return int(self.lbp.read_taskmap(plan_ws, info)["header"][3])
 
     def verify_setup(self, q_len):
         """Config, dynamic plan, queries and outputs for multi-token
@@ -225,25 +235,37 @@ class Bench:
         return ms, mode
 
     def time_attend_kernel(self, steps):
-        """Average duration of the persistent attention kernel alone (HIP events
-        recorded on the launch stream around each lbp_attend_partials)."""
+        """Average duration of the persistent attention kernel alone:
+        `steps` lbp_attend_partials launches over the rotating layers captured
+        in one HIP graph, timed with HIP events on the capture stream around
+        a replay (so launches are back to back, as under the profiler, and
+        the host's launch cost stays out).  Returns (mean µs per launch,
+        spread over `reps` replays as (min, max))."""
+        import ctypes
         lbp = self.lbp
         lib = lbp.load()
-        _, args = self.step_fn()
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(steps)]
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(s):
+            _, args = self.step_fn()          # marshalled on the capture stream
+            with torch.cuda.graph(g, stream=s):
+                for i in range(steps):
+                    st = lib.lbp_attend_partials(*args[i % self.layers])
+                    if st != 0:
+                        raise RuntimeError(lbp.status_name(st))
+        torch.cuda.current_stream().wait_stream(s)
+        g.replay()
         torch.cuda.synchronize()
-        for i in range(steps):
-            a = args[i % self.layers]
-            evs[i][0].record()
-            st = lib.lbp_attend_partials(*a)
-            evs[i][1].record()
-            if st != 0:
-                raise RuntimeError(lbp.status_name(st))
-            lib.lbp_combine(a[0], a[1], a[2], a[8], a[9], a[10], a[11])
-        torch.cuda.synchronize()
-        ts = np.array([e0.elapsed_time(e1) for e0, e1 in evs]) * 1e3
-        return float(ts.mean()), float(np.median(ts)), float(ts.min()), float(ts.max())
+        per = []
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            per.append(e0.elapsed_time(e1) * 1e3 / steps)
+        return float(np.mean(per)), float(min(per)), float(max(per))
 
     def time_prologue(self, steps):
         """lbp_prologue for the workload's batch (one new token per request into
@@ -458,19 +480,27 @@ def cpu_baseline(b: Bench, seconds: float):
 
 # ---------------------------------------------------------------------------
 
+def attend_src_sha():
+    return hashlib.sha256(open(ATTEND_SRC, "rb").read()).hexdigest()[:16]
+
+
 def traffic_record(workload):
-    """HBM bytes per launch from committed rocprofv3 counter runs on this
-    workload, if they were taken on the current attention kernel source;
-    else None."""
+    """(HBM bytes per launch, source) from the committed rocprofv3 counter
+    runs on this workload (FETCH_SIZE and WRITE_SIZE, calibrated against a
+    copy), if they were taken on the current attention kernel source; else
+    (None, reason).  The counters are not collected in this run."""
     try:
         rec = json.load(open(TRAFFIC_FILE))
     except Exception:
-        return None
-    src_hash = hashlib.sha256(open(ATTEND_SRC, "rb").read()).hexdigest()[:16]
+        return None, "no committed counter record"
     entry = rec.get(workload)
-    if not entry or entry.get("attend_src_sha") != src_hash:
-        return None
-    return entry.get("hbm_bytes_per_launch")
+    sha = attend_src_sha()
+    if not entry:
+        return None, f"no committed counter record for {workload}"
+    if entry.get("attend_src_sha") != sha:
+        return None, (f"counters taken on attend_kernel.hip {entry.get('attend_src_sha')}, "
+                      f"source is now {sha}")
+    return entry.get("hbm_bytes_per_launch"), f"profiles/attend_traffic.json@{sha}"
 
 
 def bench_one(name, lbp, args, headline, stream_gbs=None):
@@ -493,9 +523,11 @@ def bench_one(name, lbp, args, headline, stream_gbs=None):
     if b.wcfg.kv_dtype == "fp8_e4m3" and not args.no_fused:
         qms, _ = b.time_steps(args.steps, args.warmup, eager=args.eager, fp8q=True)
         res["fp8q_us_per_step"] = round(qms * 1e3, 2)       # lbp_attend_fp8q: e4m3 query
-    k_mean, k_med, k_min, k_max = b.time_attend_kernel(max(20, min(args.steps, 100)))
-    res["attend_kernel_us"] = {"mean": round(k_mean, 2), "median": round(k_med, 2),
-                               "min": round(k_min, 2), "max": round(k_max, 2)}
+    k_mean, k_min, k_max = b.time_attend_kernel(max(20, min(args.steps, 100)))
+    res["attend_kernel_us"] = {"mean": round(k_mean, 2), "min_of_replays": round(k_min, 2),
+                               "max_of_replays": round(k_max, 2),
+                               "timing": "HIP graph of attention-only launches "
+                                         "(lbp_attend_partials), events around 3 replays"}
     res["plan_us"] = round(b.time_plan(), 2)
     res["prologue"] = b.time_prologue(min(args.steps, 100))
     if not args.no_verify:
@@ -529,11 +561,12 @@ def bench_one(name, lbp, args, headline, stream_gbs=None):
     if headline and not args.no_cpu_baseline:
         log(f"{name}: CPU oracle baseline ({args.cpu_seconds:.0f}s budget)")
         res["cpu_baseline"] = cpu_baseline(b, args.cpu_seconds)
-    traffic = traffic_record(name)
+    traffic, traffic_source = traffic_record(name)
     achieved = b.wl.kv_bytes / (k_mean * 1e-6) / 1e9
     res["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                        "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                       "traffic": traffic, "kernel": ATTEND_KERNEL[b.wcfg.kv_dtype],
+                       "traffic": traffic, "traffic_source": traffic_source,
+                       "kernel": ATTEND_KERNEL[b.wcfg.kv_dtype],
                        "algorithmic_bytes_per_launch": b.wl.kv_bytes,
                        "avg_kernel_us": round(k_mean, 2),
                        "read_stream_gbs": stream_gbs,
@@ -581,6 +614,13 @@ def bench_table3(lbp, args):
                                   eager=args.eager)
             static[S] = sms * 1e3
         best = min(static, key=static.get)
+        # the minimum-work floor F (tiles per bin) of the dynamic plan; the
+        # default is 4, which binds only while T <= 3 W
+        by_f = {}
+        for F in (1, 2, 4):
+            fms_f, _ = b.time_steps(min(args.steps, 50), 2, lbp.LBP_POLICY_DYNAMIC, F,
+                                    eager=args.eager)
+            by_f[F] = {"us_per_step": round(fms_f * 1e3, 2), "bins_used": b.used_bins(F)}
         h20 = H20_TABLE3[mix]
         out[mix] = {
             "us_per_step": round(us, 2), "fused_us_per_step": round(fms * 1e3, 2),
@@ -592,6 +632,7 @@ def bench_table3(lbp, args):
             "dynamic_vs_static_grid_matched": round(static[s_grid] / us, 3),
             "dynamic_vs_static_best": round(static[best] / us, 3),
             "static_us_by_S": {str(k): round(v, 2) for k, v in static.items()},
+            "dynamic_by_min_tiles_per_bin": {str(k): v for k, v in by_f.items()},
             "h20_context": {"dynamic_us": h20[0] * 1e3, "static_us": h20[1] * 1e3,
                             "dynamic_vs_static": h20[2]},
         }
