@@ -52,10 +52,12 @@
 //    device-scope fence would write back or invalidate a whole L2 (hundreds
 //    of such fences serialise and stall every workgroup's streaming), so
 //    split partials are instead written and read with device-coherent
-//    accesses (agent-scope atomic stores and loads, which bypass the
-//    non-coherent cache levels); a workgroup waits for its partial stores to
-//    complete before it counts its arrival.  The last arriver returns each
-//    counter to zero.
+//    accesses (the sc1 cache policy of agent-scope relaxed atomics, which
+//    writes through and reads past the per-XCD caches, at 16 bytes per lane);
+//    a workgroup waits for its partial stores to complete before it counts
+//    its arrival, once per bin for both of the bin's split pairs (only its
+//    first and last descriptor can be split), whose arrivals it counts in
+//    parallel.  The last arriver returns each counter to zero.
 //  * FP8 KV (OCP e4m3 codes with one fp32 scale per token and KV head): codes
 //    are widened to bf16 exactly in registers; the K scale multiplies the
 //    score of its token, the V scale is folded into the probability before
@@ -115,13 +117,35 @@ __device__ inline uint32_t pack_bf16(float lo, float hi) {
 }
 
 // Device-coherent accesses for everything one workgroup writes and another
-// merges: agent-scope relaxed atomics, i.e. stores that write through and
-// loads that bypass the per-XCD caches.
-__device__ inline void store_coherent(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// merges (the split partials of the in-kernel merge): the cache policy of an
+// agent-scope relaxed atomic on gfx950 (sc1: stores write through and loads
+// bypass the per-XCD caches), 16 bytes per lane for the partial rows.  They
+// go through buffer resources over the split buffer's two sections, which
+// are uniform, so each access is one instruction with a per-lane offset.
+constexpr int kCoherentAux = 16;   // sc1
+struct SplitRsrc {
+  rsrc_t o, lse;
+};
+__device__ inline SplitRsrc split_rsrc(const AttendArgs& a) {
+  return SplitRsrc{make_rsrc(a.o_part, a.o_part_bytes), make_rsrc(a.lse_part, a.lse_part_bytes)};
 }
-__device__ inline float load_coherent(const float* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// row = descriptor slot * columns + column; c4 = float4 of the row
+__device__ inline void store_row_coherent(const SplitRsrc& r, int64_t row, int c4, f32x4_t v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4_t, v), r.o,
+                                         int(row * kHeadDim * 4 + 16 * c4), 0, kCoherentAux);
+}
+__device__ inline f32x4_t load_row_coherent(const SplitRsrc& r, int64_t row, int c4) {
+  return __builtin_bit_cast(
+      f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r.o, int(row * kHeadDim * 4 + 16 * c4), 0,
+                                                     kCoherentAux));
+}
+__device__ inline void store_lse_coherent(const SplitRsrc& r, int64_t row, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, v), r.lse, int(row * 4), 0,
+                                        kCoherentAux);
+}
+__device__ inline float load_lse_coherent(const SplitRsrc& r, int64_t row) {
+  return __builtin_bit_cast(float,
+                            __builtin_amdgcn_raw_buffer_load_b32(r.lse, int(row * 4), 0, kCoherentAux));
 }
 
 // Keeps the memory operations on either side in program order (an empty
@@ -970,9 +994,9 @@ __device__ inline void attend_bin(const AttendArgs& a, const int32_t* __restrict
         const float lse = empty ? -INFINITY : M + __builtin_amdgcn_logf(L);
         if (a.fuse) {
           // merged inside this launch, possibly by a workgroup on another XCD
-#pragma unroll
-          for (int j = 0; j < 4; ++j) store_coherent(po + j, on[j]);
-          if (d4 == 0) store_coherent(pl, lse);
+          const SplitRsrc sr = split_rsrc(a);
+          store_row_coherent(sr, int64_t(d) * C + q, d4, on);
+          if (d4 == 0) store_lse_coherent(sr, int64_t(d) * C + q, lse);
         } else {
           *reinterpret_cast<f32x4_t*>(po) = on;
           if (d4 == 0) *pl = lse;
@@ -1023,6 +1047,7 @@ __device__ void merge_columns(const AttendArgs& a, float* smem, int slot0, int s
   const int rg = (t >> 5) / Cc;
   float m = -INFINITY, l = 0.f;
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  const SplitRsrc sr = split_rsrc(a);
   if (rg < R) {
     for (int i0 = rg; i0 < n; i0 += kMergeUnroll * R) {
       float ls[kMergeUnroll];
@@ -1032,10 +1057,8 @@ __device__ void merge_columns(const AttendArgs& a, float* smem, int slot0, int s
         const int i = i0 + u * R;
         if (i < n) {
           const int64_t e = int64_t(slot0 + i * stride) * C + q;
-          const float* row = a.o_part + e * kHeadDim + 4 * c4;
-          ls[u] = load_coherent(a.lse_part + e);
-          v[u] = f32x4_t{load_coherent(row), load_coherent(row + 1), load_coherent(row + 2),
-                         load_coherent(row + 3)};
+          ls[u] = load_lse_coherent(sr, e);
+          v[u] = load_row_coherent(sr, e, c4);
         }
       }
 #pragma unroll
@@ -1072,10 +1095,8 @@ __device__ void merge_columns(const AttendArgs& a, float* smem, int slot0, int s
       store_bf16x4(a.out, query_row(r, g, q, a.q_len, a.group, a.num_q_heads), c4, o);
     } else {
       const int64_t e = int64_t(dst) * C + q;
-      float* row = a.o_part + e * kHeadDim + 4 * c4;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) store_coherent(row + j, o[j]);
-      if (c4 == 0) store_coherent(a.lse_part + e, empty ? -INFINITY : M + __builtin_amdgcn_logf(L));
+      store_row_coherent(sr, e, c4, o);
+      if (c4 == 0) store_lse_coherent(sr, e, empty ? -INFINITY : M + __builtin_amdgcn_logf(L));
     }
   }
   __syncthreads();
@@ -1119,38 +1140,70 @@ __device__ inline bool arrive(int32_t* counter, int target, int* flag) {
 }
 
 // After a bin is drained: arrivals (and, for the last arriver, the merge)
-// for every split pair among its descriptors.
+// for every split pair among its descriptors.  A dynamic bin is one run of
+// flat tiles, so only its first and its last descriptor can belong to a pair
+// split over several bins; both are published together (one wait for the
+// workgroup's stores) and their arrivals are counted in parallel, by two
+// waves, so that a bin with two split pairs pays one chain, not two.
 template <int kThreads>
 __device__ void finish_split_pairs(const AttendArgs& a, const int4* __restrict__ descs,
                                    const int32_t* __restrict__ pair_count,
                                    const int32_t* __restrict__ pair_first, float* smem, int* flag,
                                    int d_begin, int d_end) {
-  for (int d = d_begin; d < d_end; ++d) {
+  int sd[2];
+  int nsd = 0;
+  for (int d = d_begin; d < d_end; d = (d == d_begin && d_end - 1 > d_begin) ? d_end - 1 : d_end) {
     const int4 ds = descs[d];
+    if (pair_count[ds.x * a.batch + ds.y] >= 2) sd[nsd++] = d;
+  }
+  if (nsd == 0) return;
+  publish_workgroup();
+  // the first arrival of each split descriptor: at its group's counter when
+  // the pair merges in two levels, else at the pair's
+  for (int j = 0; j < nsd; ++j) {
+    if (int(threadIdx.x) != 64 * j) continue;
+    const int4 ds = descs[sd[j]];
     const int p = ds.x * a.batch + ds.y;
     const int cnt = pair_count[p];
-    if (cnt < 2) continue;
-    publish_workgroup();
+    const int first = pair_first[p];
+    const int f = merge_group_size(cnt);
+    int32_t* counter;
+    int target;
+    if ((cnt + f - 1) / f > 1) {
+      const int lead = first + (sd[j] - first) / f * f;
+      counter = a.arrive_group + lead;
+      target = min(f, first + cnt - lead);
+    } else {
+      counter = a.arrive_pair + first;
+      target = cnt;
+    }
+    const int old = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const bool last = old == target - 1;
+    if (last) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    flag[1 + j] = last;
+  }
+  __syncthreads();
+  const bool last0 = flag[1] != 0, last1 = nsd > 1 && flag[2] != 0;
+  __syncthreads();   // the flags are read before any later arrival rewrites them
+  for (int j = 0; j < nsd; ++j) {
+    if (!(j == 0 ? last0 : last1)) continue;
+    const int4 ds = descs[sd[j]];
+    const int p = ds.x * a.batch + ds.y;
+    const int cnt = pair_count[p];
     const int first = pair_first[p];
     const int f = merge_group_size(cnt);
     const int ngroups = (cnt + f - 1) / f;
-    // level 1 (only with several groups): this descriptor's group, merged
-    // into the group's first slot; level 2: the pair, merged into `out`
-    const int lead = first + (d - first) / f * f;
-    const int members = min(f, first + cnt - lead);
-    bool grouped = ngroups > 1;
-    if (!(grouped ? arrive(a.arrive_group + lead, members, flag)
-                  : arrive(a.arrive_pair + first, cnt, flag)))
+    if (ngroups == 1) {
+      merge_run<kThreads>(a, smem, first, 1, cnt, -1, ds.x, ds.y);
       continue;
-    for (;;) {
-      merge_run<kThreads>(a, smem, grouped ? lead : first, grouped || ngroups == 1 ? 1 : f,
-                          grouped ? members : ngroups > 1 ? ngroups : cnt, grouped ? lead : -1,
-                          ds.x, ds.y);
-      if (!grouped) break;
-      grouped = false;
-      publish_workgroup();
-      if (!arrive(a.arrive_pair + first, ngroups, flag)) break;
     }
+    // level 1: this descriptor's group, into the group's first slot; level 2
+    // (for the last group to finish): the group results, into `out`
+    const int lead = first + (sd[j] - first) / f * f;
+    merge_run<kThreads>(a, smem, lead, 1, min(f, first + cnt - lead), lead, ds.x, ds.y);
+    publish_workgroup();
+    if (arrive(a.arrive_pair + first, ngroups, flag))
+      merge_run<kThreads>(a, smem, first, f, ngroups, -1, ds.x, ds.y);
   }
 }
 
@@ -1177,7 +1230,7 @@ __attribute__((amdgpu_waves_per_eu((waves_of<Kv, kStagedW>() + 3) / 4,
   constexpr int kThreads = waves_of<Kv, kStagedW>() * 64;
   extern __shared__ __attribute__((aligned(16))) float smem[];   // f32x4 rows are stored in it
   __shared__ int ticket_lds;
-  __shared__ int arrive_lds;
+  __shared__ int arrive_lds[3];   // the merge's arrival flags
   uint64_t t_start = 0;
   if (a.trace) t_start = __builtin_amdgcn_s_memrealtime();
   int drained = 0;
@@ -1197,7 +1250,7 @@ __attribute__((amdgpu_waves_per_eu((waves_of<Kv, kStagedW>() + 3) / 4,
                                            bin_first, pair_first, smem, bin);
     const int d_begin = bin_offset[bin], d_end = bin_offset[bin + 1];
     if (a.fuse)
-      finish_split_pairs<kThreads>(a, descs, pair_count, pair_first, smem, &arrive_lds, d_begin,
+      finish_split_pairs<kThreads>(a, descs, pair_count, pair_first, smem, arrive_lds, d_begin,
                                    d_end);
     drained += d_end - d_begin;
     if (!a.grab_counter) break;

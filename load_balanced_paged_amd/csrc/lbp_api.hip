@@ -293,6 +293,13 @@ static lbp_status attend_impl(const lbp_config* cfg, const lbp_plan_info* info,
   a.o_part = static_cast<float*>(split_ws_dev);
   a.lse_part = reinterpret_cast<float*>(static_cast<char*>(split_ws_dev) +
                                         split_lse_offset(info->max_desc, ncols_of(cfg)));
+  // buffer resources address the split buffer with 32-bit offsets
+  const uint64_t o_bytes = split_lse_offset(info->max_desc, ncols_of(cfg));
+  const uint64_t lse_bytes = uint64_t(info->max_desc) * ncols_of(cfg) * 4;
+  if (fuse && info->policy == LBP_POLICY_DYNAMIC && o_bytes > uint64_t(INT32_MAX))
+    return LBP_ERR_UNSUPPORTED;
+  a.o_part_bytes = int32_t(o_bytes < uint64_t(INT32_MAX) ? o_bytes : uint64_t(INT32_MAX));
+  a.lse_part_bytes = int32_t(lse_bytes < uint64_t(INT32_MAX) ? lse_bytes : uint64_t(INT32_MAX));
   a.out = out_dev;
   a.trace = trace_dev;
   a.num_bins = info->num_bins;

@@ -104,6 +104,8 @@ struct AttendArgs {
   const float* v_scale;
   float* o_part;             // [max_desc][G][128]
   float* lse_part;           // [max_desc][G]
+  int32_t o_part_bytes;      // bytes of the two sections (the in-kernel merge
+  int32_t lse_part_bytes;    // reads and writes them through buffer resources)
   void* out;                 // [B][Hq][128] bf16: single-descriptor pairs land here
   uint64_t* trace;           // optional [grid][4] workgroup records, or null
   int32_t* grab_counter;     // null: workgroup b drains bin b; else the ticket counter
