@@ -63,6 +63,9 @@ def parse_args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-verify", action="store_true",
                     help="skip the multi-token verification timings (q_len 2, 4, 6)")
+    ap.add_argument("--verify-qlens", default="2,4,6",
+                    help="comma list of the verification widths (query tokens per request) "
+                         "timed after decode")
     ap.add_argument("--no-table3", action="store_true",
                     help="skip the six FP8-KV length mixes of the vLLM x HPC-Ops page, Table 3")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -533,7 +536,9 @@ def bench_one(name, lbp, args, headline, stream_gbs=None):
     if not args.no_verify:
         # multi-token verification: the same KV, q_len query tokens per request
         res["verify"] = {}
-        for T in (2, 4, 6):
+        for T in sorted({int(x) for x in args.verify_qlens.split(",") if x.strip()}):
+            if T < 2:
+                continue
             if b.wcfg.num_q_heads // b.wcfg.num_kv_heads * T > 64:
                 continue
             vms, _ = b.time_steps(args.steps, args.warmup, eager=args.eager, q_len=T)

@@ -25,6 +25,13 @@
  *    argument returns an error status and launches nothing.  Faults inside
  *    a kernel surface at the caller's next synchronisation, as for any HIP
  *    call.  No C++ exception crosses this interface.
+ *  - Concurrency: the attend calls read a plan workspace but may also update
+ *    counters in it (the bin ticket counter of a DYNAMIC plan with more bins
+ *    than CUs, the arrival counters of lbp_attend_fused), each back at zero
+ *    when the launch completes.  Calls that share a plan workspace must
+ *    therefore be ordered on one stream (the layers of a step are); calls
+ *    that run concurrently need their own plan workspace (lbp_plan into each)
+ *    and their own split workspace.
  *
  * Fixed data layouts (all contiguous, row-major):
  *  - q        [batch][q_len][num_q_heads][128]          bf16
@@ -227,8 +234,8 @@ lbp_status lbp_plan_layout(const lbp_plan_info* info, lbp_plan_offsets* offsets)
  * the combine kernel merges each such pair under the global softmax
  * normalisation into out_dev (BF16, round to nearest even).  A pair with no
  * tokens gets zeros.  k_scale_dev / v_scale_dev are required for FP8 KV and
- * ignored for BF16.  Concurrent calls that share a plan need their own split
- * workspaces. */
+ * ignored for BF16.  Calls sharing the plan workspace run in stream order
+ * (see Concurrency above). */
 lbp_status lbp_attend(const lbp_config* cfg, const lbp_plan_info* info,
                       const void* plan_ws_dev, const void* q_dev, const void* k_cache_dev,
                       const void* v_cache_dev, const float* k_scale_dev,
