@@ -23,10 +23,17 @@ LIB = os.path.join(PKG, "liblbp.so")
 ARCH = os.environ.get("LBP_OFFLOAD_ARCH", "gfx950")
 
 # Packed-FP32 instructions are kept out of the generated code (the compiler
-# may not form v_pk_{add,mul,fma}_f32 from scalar float code).
+# may not form v_pk_{add,mul,fma}_f32 from scalar float code).  MFMA results
+# go to ordinary VGPRs in every kernel: a kernel allowed more than 256
+# registers (one wave per SIMD) would otherwise keep its accumulators in
+# AGPRs and copy them to VGPRs and back around every vector operation on
+# them (the rescale of the running softmax state); the AGPRs then serve as
+# spill space only.  Kernels limited to 256 registers compile the same
+# either way.
 HIP_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wall", "-Wno-unused-function",
 ]
 

@@ -88,6 +88,23 @@ namespace {
 #ifndef LBP_FP8Q_WAVES
 #define LBP_FP8Q_WAVES 8
 #endif
+// Multi-token verification: 33-48 query columns as three 16-column tiles per
+// wave (1) or through the staged instance (0), and the wave counts of the
+// two- and three-tile instances (0: the format's own).
+#ifndef LBP_TILE3
+#define LBP_TILE3 1
+#endif
+#ifndef LBP_TILE3_WAVES
+#define LBP_TILE3_WAVES 4
+#endif
+#ifndef LBP_TILE2_WAVES
+#define LBP_TILE2_WAVES 0
+#endif
+// Tokens per step of a wave in the tile forms: 16 (1) or 32 (2, one K = 32
+// P.V product per pair of 16-token sub-slices).
+#ifndef LBP_TILE_SUB
+#define LBP_TILE_SUB 2
+#endif
 #ifndef LBP_KV_LOAD_AUX
 #define LBP_KV_LOAD_AUX 2
 #endif
@@ -683,6 +700,105 @@ __device__ inline void consume(WaveState& st, const typename Kv::Buf& b, const t
   }
 }
 
+// consume for kNB column tiles of one slice (the causal tile forms), in
+// phases across the tiles: every tile's scores and running max first, then a
+// single rescale of all tiles when any lane of any tile saw its maximum grow
+// (a tile that did not grow is multiplied by exactly 1, so the results are
+// those of a rescale per tile, bit for bit), then every tile's probabilities
+// and P.V products.  The tiles' chains are independent, and with one branch
+// per slice instead of one per tile the scheduler can interleave them, which
+// a wave alone on its SIMD needs to hide the MFMA and transcendental
+// latencies.  P enters the P.V product as one BF16 value (kOneP in consume).
+// kSub = 2: the slice is 32 tokens, two 16-token sub-slices b[0] and b[1],
+// whose P.V is a single MFMA with K = 32 per output block.
+template <class Kv, bool kCausal, int kNB, int kSub>
+__device__ inline void consume_tiles(WaveState (&st)[kNB], const typename Kv::Buf (&b)[kSub],
+                                     const typename Kv::Q (&q)[kNB], int tok, int e,
+                                     const float (&scale_log2)[kNB], int grp,
+                                     const int (&lim)[kNB]) {
+  static_assert(kSub == 1 || kSub == 2, "one or two 16-token sub-slices");
+  f32x4_t ks[kSub], vs[kSub];
+#pragma unroll
+  for (int u = 0; u < kSub; ++u) {
+    ks[u] = Kv::k_scales(b[u]);
+    vs[u] = Kv::v_scales(b[u]);
+  }
+  float x[kNB][kSub][4];
+  float m_new[kNB];
+  bool grew = false;
+#pragma unroll
+  for (int t = 0; t < kNB; ++t) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < kSub; ++u) {
+      const f32x4_t sc = Kv::scores(b[u], q[t]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        x[t][u][j] = (tok + kSlice * u + 4 * grp + j < (kCausal ? min(e, lim[t]) : e))
+                         ? sc[j] * ks[u][j] * scale_log2[t]
+                         : -INFINITY;
+      mx = fmaxf(mx, fmaxf(fmaxf(x[t][u][0], x[t][u][1]), fmaxf(x[t][u][2], x[t][u][3])));
+    }
+    mx = wave_max_across_groups(mx);
+    m_new[t] = fmaxf(st[t].m, mx);
+    grew = grew || m_new[t] > st[t].m;
+  }
+  if (__ballot(grew) != 0) {
+    asm volatile("");   // keeps the skip a branch (see consume)
+#pragma unroll
+    for (int t = 0; t < kNB; ++t) {
+      const float ref = kCausal ? finite_or_zero(m_new[t]) : m_new[t];
+      const float alpha = __builtin_amdgcn_exp2f(st[t].m - ref);
+      st[t].l *= alpha;
+#pragma unroll
+      for (int mb = 0; mb < 8; ++mb) st[t].acc[mb] *= alpha;
+    }
+  }
+  constexpr bool kRoundedSum = Kv::kSplitP;
+#pragma unroll
+  for (int t = 0; t < kNB; ++t) {
+    st[t].m = m_new[t];
+    const float ref = kCausal ? finite_or_zero(m_new[t]) : m_new[t];
+    i32x2_t pb2[kSub];
+#pragma unroll
+    for (int u = 0; u < kSub; ++u) {
+      float p[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) p[j] = __builtin_amdgcn_exp2f(x[t][u][j] - ref);
+      if constexpr (!kRoundedSum) st[t].l += (p[0] + p[1]) + (p[2] + p[3]);
+      pb2[u] = i32x2_t{int(pack_bf16(p[0] * vs[u][0], p[1] * vs[u][1])),
+                       int(pack_bf16(p[2] * vs[u][2], p[3] * vs[u][3]))};
+      if constexpr (kRoundedSum) {
+        const uint32_t h01 = uint32_t(pb2[u][0]), h23 = uint32_t(pb2[u][1]);
+        st[t].l += (__builtin_bit_cast(float, h01 << 16) +
+                    __builtin_bit_cast(float, h01 & 0xFFFF0000u)) +
+                   (__builtin_bit_cast(float, h23 << 16) +
+                    __builtin_bit_cast(float, h23 & 0xFFFF0000u));
+      }
+    }
+    if constexpr (kSub == 1) {
+      const i16x4_t pb = __builtin_bit_cast(i16x4_t, pb2[0]);
+#pragma unroll
+      for (int mb = 0; mb < 8; ++mb)
+        st[t].acc[mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(Kv::v_operand(b[0], mb), pb,
+                                                                   st[t].acc[mb], 0, 0, 0);
+    } else {
+      // one K = 32 product over both sub-slices: contraction index 8 grp + i
+      // is token 4 grp + (i mod 4) of sub-slice i / 4, in P and in V alike
+      const i32x4_t pw = {pb2[0][0], pb2[0][1], pb2[1][0], pb2[1][1]};
+      const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pw);
+#pragma unroll
+      for (int mb = 0; mb < 8; ++mb) {
+        const i32x2_t v0 = __builtin_bit_cast(i32x2_t, Kv::v_operand(b[0], mb));
+        const i32x2_t v1 = __builtin_bit_cast(i32x2_t, Kv::v_operand(b[1], mb));
+        const i32x4_t vw = {v0[0], v0[1], v1[0], v1[1]};
+        st[t].acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, vw),
+                                                                pb, st[t].acc[mb], 0, 0, 0);
+      }
+    }
+  }
+}
+
 // Waves of the staged instances (column blocks, more than 32 query columns),
 // for every KV format; their LDS ring of 2 x waves slices must fit the CU.
 // The column blocks divide the waves evenly: 8 waves give four full blocks
@@ -698,12 +814,24 @@ constexpr int kStagedWaves33To48 = 6;
 template <class Kv, int kStagedW>
 using StagedOf = Staged<Kv, Kv::kWidenK && kStagedW == kStagedWaves33To48>;
 
-// kStagedW: 0 for the decode and causal instances (the format's own wave
-// count), else the staged instance's wave count.
-template <class Kv, int kStagedW>
+// kStagedW: 0 for the decode and causal instances, else the staged
+// instance's wave count; kTileW: the wave count of a causal instance with
+// several column tiles, 0 for the format's own.
+template <class Kv, int kStagedW, int kTileW = 0>
 constexpr int waves_of() {
-  return kStagedW > 0 ? kStagedW : Kv::kWaves;
+  return kStagedW > 0 ? kStagedW : kTileW > 0 ? kTileW : Kv::kWaves;
 }
+constexpr int kTile2Waves = LBP_TILE2_WAVES;
+
+// The loads of one wave step: one 16-token slice, or kSub consecutive ones
+// (the tile forms' 32-token spans).
+template <class Kv, int kSub>
+struct SpanOf {
+  typename Kv::Buf s[kSub];
+};
+template <class Kv, int kSub>
+using SpanBuf = std::conditional_t<kSub == 1, typename Kv::Buf, SpanOf<Kv, kSub>>;
+constexpr int kTile3Waves = LBP_TILE3_WAVES;
 
 // A slice's register image in LDS (Kv: a slice format with member type
 // Buf): vector v of lane l at [v][l], so each 16-byte write or read of a
@@ -752,7 +880,7 @@ struct BufImage {
 // round's slices from LDS.  Every KV byte is then fetched once per
 // workgroup with the full set of loads in flight, while each wave keeps the
 // register state of a single 16-column tile.
-template <class Kv, bool kCausal, int kStagedW, int kNB>
+template <class Kv, bool kCausal, int kStagedW, int kNB, int kTileW>
 __device__ inline void attend_bin(const AttendArgs& a, const int32_t* __restrict__ pt,
                                   const int4* __restrict__ descs,
                                   const int32_t* __restrict__ pair_count,
@@ -760,11 +888,12 @@ __device__ inline void attend_bin(const AttendArgs& a, const int32_t* __restrict
                                   const int4* __restrict__ bin_first,
                                   const int32_t* __restrict__ pair_first, float* smem, int bin) {
   constexpr bool kStaged = kStagedW > 0;
-  constexpr int kWaves = waves_of<Kv, kStagedW>();
+  constexpr int kWaves = waves_of<Kv, kStagedW, kTileW>();
   constexpr int kThreads = kWaves * 64;
   static_assert(kCausal || !kStaged, "the staged form serves verification only");
-  static_assert(kNB == 1 || (kNB == 2 && kCausal && !kStaged),
-                "two column tiles per wave: causal form only");
+  static_assert(kNB == 1 || (kNB <= 3 && kCausal && !kStaged),
+                "several column tiles per wave: causal form only");
+  static_assert(kTileW == 0 || kNB > 1, "a wave count of its own: tile forms only");
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15;         // MFMA column of this lane within its block
@@ -781,7 +910,14 @@ __device__ inline void attend_bin(const AttendArgs& a, const int32_t* __restrict
   const int cpb = kStaged ? a.block_cols : C;          // columns per block, <= 16 staged
   const int col0 = blk * cpb;
   const int nvalid = kStaged ? min(cpb, C - col0) : C; // this block's columns
-  constexpr int step = kWaves * kSlice;                // tokens per round / per wave stride
+  // the tile forms with one wave per SIMD (512 registers) step by spans of
+  // kSub 16-token sub-slices; at two waves per SIMD the second sub-slice's
+  // registers do not fit
+  constexpr int kSub = kNB > 1 && kWaves <= 4 ? LBP_TILE_SUB : 1;
+  static_assert(kSub == 1 || !kStaged, "spans: tile forms only");
+  constexpr int kSpan = kSlice * kSub;
+  constexpr int step = kWaves * kSpan;                 // tokens per round / per wave stride
+  using SBuf = SpanBuf<Kv, kSub>;
   // per wave in LDS for the merge: m and l of 16 kNB columns, then the rows
   constexpr int kRedHead = 32 * kNB;
   const int red_stride = kRedHead + cpb * kRedRow;
@@ -797,7 +933,18 @@ __device__ inline void attend_bin(const AttendArgs& a, const int32_t* __restrict
 
   QLane ql[kNB];
   typename Kv::Q qb[kNB];
-  typename Kv::Buf buf[2];
+  SBuf buf[2];
+  // the span at token t of KV head gq, whose page (tokens t and t + 16 share
+  // it: spans start at multiples of 32) is `page`
+  auto issue_span = [&](SBuf& b, int gq, int t, int e, int page) {
+    if constexpr (kSub == 1) {
+      Kv::template issue<kStaged>(b, slice_rsrc_at<Kv>(a, gq, t, e, page), lane);
+    } else {
+#pragma unroll
+      for (int u = 0; u < kSub; ++u)
+        Kv::issue(b.s[u], slice_rsrc_at<Kv>(a, gq, t + kSlice * u, e, page), lane);
+    }
+  };
   if constexpr (kNB == 1) {
     // (spelled out: the loop form below, though equivalent, made the
     // compiler schedule the decode instance differently, and slower)
@@ -810,8 +957,10 @@ __device__ inline void attend_bin(const AttendArgs& a, const int32_t* __restrict
       Kv::load_q(qb[t], a, ql[t], ds.x, ds.y, grp);
     }
   }
-  Kv::template issue<kStaged>(buf[0], slice_rsrc<Kv>(a, pt, ds.x, ds.y, ds.z + wave * kSlice, ds.w),
-                              lane);
+  {
+    const int t0 = ds.z + wave * kSpan;
+    issue_span(buf[0], ds.x, t0, ds.w, page_of(a, pt, ds.y, t0, ds.w));
+  }
 
   for (int d = d_begin; d < d_end; ++d) {
     const int g = ds.x, r = ds.y, t_begin = ds.z, t_end = ds.w;
@@ -822,7 +971,7 @@ __device__ inline void attend_bin(const AttendArgs& a, const int32_t* __restrict
     // the next descriptor's first slice of this wave and its page, looked up
     // now so that the lookup completes during this descriptor's loop instead
     // of delaying the prefetch after it
-    const int next_tok = (has_next ? dn.z : dn.w) + wave * kSlice;
+    const int next_tok = (has_next ? dn.z : dn.w) + wave * kSpan;
     const int next_page = page_of(a, pt, dn.y, next_tok, dn.w);
     // causal limit of this lane's column in multi-token verification: query
     // token j of the request sits at position L - q_len + j, L being the
@@ -890,20 +1039,29 @@ __device__ inline void attend_bin(const AttendArgs& a, const int32_t* __restrict
       // parity the compiler kept two copies of the wave state.  The loop has
       // one exit and every path to a step has the same loads outstanding, so
       // the compiler's wait counts stay exact.
-      int tok = t_begin + wave * kSlice;
+      int tok = t_begin + wave * kSpan;
       const int ns = wave_slices(tok, t_end, step);
       // (one tile spelled out, as in the query setup above)
       const float sc0 = Kv::score_scale(qb[0], a.scale_log2);
-      const float sc1 = kNB > 1 ? Kv::score_scale(qb[kNB - 1], a.scale_log2) : sc0;
-      auto compute = [&](const typename Kv::Buf& cur) {
-        consume<Kv, kCausal, false, (kNB > 1)>(st[0], cur, qb[0], tok, t_end, sc0, grp, lim[0]);
-        if constexpr (kNB > 1)
-          consume<Kv, kCausal, false, true>(st[1], cur, qb[1], tok, t_end, sc1, grp, lim[1]);
+      auto compute = [&](const SBuf& cur) {
+        if constexpr (kNB == 1) {
+          consume<Kv, kCausal>(st[0], cur, qb[0], tok, t_end, sc0, grp, lim[0]);
+        } else {
+          float sct[kNB];
+#pragma unroll
+          for (int t = 0; t < kNB; ++t) sct[t] = Kv::score_scale(qb[t], a.scale_log2);
+          if constexpr (kSub == 1) {
+            const typename Kv::Buf one[1] = {cur};
+            consume_tiles<Kv, kCausal, kNB, 1>(st, one, qb, tok, t_end, sct, grp, lim);
+          } else {
+            consume_tiles<Kv, kCausal, kNB, kSub>(st, cur.s, qb, tok, t_end, sct, grp, lim);
+          }
+        }
       };
-      auto step_on = [&](const typename Kv::Buf& cur, typename Kv::Buf& nxt) {
-        Kv::issue(nxt, slice_rsrc<Kv>(a, pt, g, r, tok + step, t_end), lane);
-        Kv::after_loads(qb[0]);
-        if constexpr (kNB > 1) Kv::after_loads(qb[1]);
+      auto step_on = [&](const SBuf& cur, SBuf& nxt) {
+        issue_span(nxt, g, tok + step, t_end, page_of(a, pt, r, tok + step, t_end));
+#pragma unroll
+        for (int t = 0; t < kNB; ++t) Kv::after_loads(qb[t]);
         compute(cur);
         tok += step;
       };
@@ -929,8 +1087,7 @@ __device__ inline void attend_bin(const AttendArgs& a, const int32_t* __restrict
     auto prefetch_next = [&]() {
 #pragma unroll
       for (int t = 0; t < kNB; ++t) Kv::load_q(qb[t], a, ql[t], dn.x, dn.y, grp);
-      Kv::template issue<kStaged>(buf[0], slice_rsrc_at<Kv>(a, dn.x, next_tok, dn.w, next_page),
-                                  lane);
+      issue_span(buf[0], dn.x, next_tok, dn.w, next_page);
     };
     if (!kStaged && has_next) prefetch_next();
 
@@ -1220,14 +1377,14 @@ __device__ void finish_split_pairs(const AttendArgs& a, const int4* __restrict__
 // loop's registers toward occupancies that never occur, and whenever that
 // loop is the kernel's register peak it stops issuing the next slice ahead
 // of the current slice's math.
-template <class Kv, bool kCausal, int kStagedW, int kNB>
-__global__ __launch_bounds__((waves_of<Kv, kStagedW>() * 64))
-__attribute__((amdgpu_waves_per_eu((waves_of<Kv, kStagedW>() + 3) / 4,
-                                   (waves_of<Kv, kStagedW>() + 3) / 4))) void attend_kernel(
+template <class Kv, bool kCausal, int kStagedW, int kNB, int kTileW>
+__global__ __launch_bounds__((waves_of<Kv, kStagedW, kTileW>() * 64))
+__attribute__((amdgpu_waves_per_eu((waves_of<Kv, kStagedW, kTileW>() + 3) / 4,
+                                   (waves_of<Kv, kStagedW, kTileW>() + 3) / 4))) void attend_kernel(
     AttendArgs a, const int32_t* __restrict__ page_table, const int4* __restrict__ descs,
     const int32_t* __restrict__ pair_count, const int32_t* __restrict__ bin_offset,
     const int32_t* __restrict__ pair_first, const int4* __restrict__ bin_first) {
-  constexpr int kThreads = waves_of<Kv, kStagedW>() * 64;
+  constexpr int kThreads = waves_of<Kv, kStagedW, kTileW>() * 64;
   extern __shared__ __attribute__((aligned(16))) float smem[];   // f32x4 rows are stored in it
   __shared__ int ticket_lds;
   __shared__ int arrive_lds[3];   // the merge's arrival flags
@@ -1246,7 +1403,7 @@ __attribute__((amdgpu_waves_per_eu((waves_of<Kv, kStagedW>() + 3) / 4,
   };
   int bin = a.grab_counter ? next_bin() : int(blockIdx.x);
   while (bin < a.num_bins) {
-    attend_bin<Kv, kCausal, kStagedW, kNB>(a, page_table, descs, pair_count, bin_offset,
+    attend_bin<Kv, kCausal, kStagedW, kNB, kTileW>(a, page_table, descs, pair_count, bin_offset,
                                            bin_first, pair_first, smem, bin);
     const int d_begin = bin_offset[bin], d_end = bin_offset[bin + 1];
     if (a.fuse)
@@ -1286,25 +1443,30 @@ __attribute__((amdgpu_waves_per_eu((waves_of<Kv, kStagedW>() + 3) / 4,
 
 }  // namespace
 
-// The instance for a KV format: decode, causal with one or two MFMA column
-// tiles per wave (q_len > 1, at most 16 or 32 columns) or staged with
-// staged_w waves; its wave count and, when staged, the bytes of its LDS
+// The instance for a KV format: decode, causal with one, two or three MFMA
+// column tiles per wave (q_len > 1, at most 16, 32 or 48 columns) or staged
+// with staged_w waves; its wave count and, when staged, the bytes of its LDS
 // ring.
 template <class Kv>
 void pick_instance(bool causal, int tiles, int staged_w, const void** fn, int* waves,
                    size_t* ring) {
   *ring = 0;
+  *waves = Kv::kWaves;
   if (staged_w == kStagedWaves) {
-    *fn = reinterpret_cast<const void*>(&attend_kernel<Kv, true, kStagedWaves, 1>);
+    *fn = reinterpret_cast<const void*>(&attend_kernel<Kv, true, kStagedWaves, 1, 0>);
   } else if (staged_w == kStagedWaves33To48) {
-    *fn = reinterpret_cast<const void*>(&attend_kernel<Kv, true, kStagedWaves33To48, 1>);
+    *fn = reinterpret_cast<const void*>(&attend_kernel<Kv, true, kStagedWaves33To48, 1, 0>);
+  } else if (tiles == 3) {
+    *fn = reinterpret_cast<const void*>(&attend_kernel<Kv, true, 0, 3, kTile3Waves>);
+    *waves = waves_of<Kv, 0, kTile3Waves>();
   } else if (tiles == 2) {
-    *fn = reinterpret_cast<const void*>(&attend_kernel<Kv, true, 0, 2>);
+    *fn = reinterpret_cast<const void*>(&attend_kernel<Kv, true, 0, 2, kTile2Waves>);
+    *waves = waves_of<Kv, 0, kTile2Waves>();
   } else {
-    *fn = causal ? reinterpret_cast<const void*>(&attend_kernel<Kv, true, 0, 1>)
-                 : reinterpret_cast<const void*>(&attend_kernel<Kv, false, 0, 1>);
+    *fn = causal ? reinterpret_cast<const void*>(&attend_kernel<Kv, true, 0, 1, 0>)
+                 : reinterpret_cast<const void*>(&attend_kernel<Kv, false, 0, 1, 0>);
   }
-  *waves = staged_w > 0 ? staged_w : Kv::kWaves;
+  if (staged_w > 0) *waves = staged_w;
   if (staged_w == kStagedWaves)
     *ring = 2 * size_t(staged_w) * BufImage<StagedOf<Kv, kStagedWaves>>::kBytes;
   else if (staged_w == kStagedWaves33To48)
@@ -1322,11 +1484,12 @@ hipError_t launch_attend(const AttendArgs& a, AttendKind kind, int grid, hipStre
   void* args[] = {&copy, &pt, &descs, &pc, &bo, &pf, &bf};
   // multi-token verification (q_len > 1) runs the instances with the causal
   // limit: one MFMA column tile per wave up to 16 query columns, two up to
-  // 32, and the staged instance past that; plain decode keeps the loop
-  // without either
+  // 32, three up to 48, and the staged instance past that; plain decode
+  // keeps the loop without either
   const bool causal = a.q_len > 1;
-  const int tiles = causal && a.ncols > 16 && a.ncols <= 32 ? 2 : 1;
-  const bool staged = causal && a.ncols > 32;
+  const int max_tiles = LBP_TILE3 ? 3 : 2;
+  const int tiles = !causal || a.ncols > 16 * max_tiles ? 1 : (a.ncols + 15) / 16;
+  const bool staged = causal && a.ncols > 16 * max_tiles;
   if (!causal && a.ncols > 16) return hipErrorInvalidValue;
   const int staged_w = !staged ? 0 : a.ncols <= 48 ? kStagedWaves33To48 : kStagedWaves;
   int waves;

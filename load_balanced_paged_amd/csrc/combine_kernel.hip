@@ -26,9 +26,11 @@
 // (bitwise deterministic).  Workgroups have 256 threads (128 rows per round
 // trip); a grid of at most one workgroup per CU, which few split pairs with
 // many partials each give, uses 512 (256 rows): the wider workgroups cost
-// dispatch time only when there are many of them.  A larger grid with at
-// most 8 columns (decode at G <= 8: many split pairs of few partials) runs
-// combine_pairs_kernel instead, one workgroup per pair.
+// dispatch time only when there are many of them.  When the list can hold
+// more than 32 pairs of at least 8 columns, or more than 256 / C pairs of
+// fewer (decode at G <= 8, or verification: many split pairs of few
+// partials), combine_pairs_kernel runs instead, one workgroup per pair and
+// chunk of 8 columns.
 #include "lse_merge.h"
 
 namespace lbp {
@@ -105,13 +107,14 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
   store_bf16x4(a.out, row, c4, L > 0.f ? tot / L : f32x4_t{0.f, 0.f, 0.f, 0.f});
 }
 
-// One workgroup per split pair, for many pairs of few partials each: 32
-// threads per query column (one float4 of the row each), each merging its
-// column's partials in order, kPairUnroll in flight.  One workgroup instead
-// of one per column makes the grid 8 times smaller at G = 8.
+// One workgroup per split pair and chunk of 8 query columns, for many pairs
+// of few partials each: 32 threads per column (one float4 of the row each),
+// each merging its column's partials in order, kPairUnroll in flight.  One
+// workgroup per 8 columns instead of one per column makes the grid 8 times
+// smaller.
 constexpr int kPairThreads = 256;
 constexpr int kPairUnroll = 8;
-constexpr int kPairMaxCols = kPairThreads / kLanesPerRow;   // 8
+constexpr int kPairCols = kPairThreads / kLanesPerRow;   // 8
 
 __global__ __launch_bounds__(kPairThreads) void combine_pairs_kernel(CombineArgs a) {
   const int nsplit = a.header[kHdrSplits];
@@ -120,7 +123,7 @@ __global__ __launch_bounds__(kPairThreads) void combine_pairs_kernel(CombineArgs
   if (int(blockIdx.x) >= nsplit) return;
   const int p = e.x, first = e.y, cnt = e.z;
   const int C = a.ncols;
-  const int q = threadIdx.x / kLanesPerRow;
+  const int q = int(blockIdx.y) * kPairCols + int(threadIdx.x) / kLanesPerRow;
   const int c4 = threadIdx.x % kLanesPerRow;
   if (q >= C) return;
   const int g = p / a.batch, r = p % a.batch;
@@ -153,8 +156,11 @@ hipError_t launch_combine(const CombineArgs& a, int max_split, hipStream_t s) {
   if (max_split <= 0) return hipSuccess;
   CombineArgs copy = a;
   void* args[] = {&copy};
-  if (int64_t(max_split) * a.ncols > kWideGrid && a.ncols <= kPairMaxCols)
-    return hipLaunchKernel(reinterpret_cast<const void*>(&combine_pairs_kernel), dim3(max_split),
+  // many possible split pairs: few partials each (the plan splits at most
+  // W - 1 times in all), so one workgroup per pair and 8 columns
+  if (int64_t(max_split) * (a.ncols < kPairCols ? a.ncols : kPairCols) > kWideGrid)
+    return hipLaunchKernel(reinterpret_cast<const void*>(&combine_pairs_kernel),
+                           dim3(max_split, (a.ncols + kPairCols - 1) / kPairCols),
                            dim3(kPairThreads), args, 0, s);
   const bool wide = int64_t(max_split) * a.ncols <= kWideGrid;
   const void* fn = wide ? reinterpret_cast<const void*>(&combine_kernel<512>)

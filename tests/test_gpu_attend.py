@@ -137,14 +137,16 @@ def test_attend_bin_shapes(gpu_lib, W, F):
 
 
 @pytest.mark.parametrize("form,batch,W,group", [("wide", 1, 600, 8), ("pairs", 40, 400, 8),
-                                                ("columns", 40, 400, 16)])
+                                                ("pairs", 40, 400, 16), ("columns", 20, 400, 16)])
 def test_combine_rounds_every_form(gpu_lib, form, batch, W, group):
     """A pair split into more partials than one round of the combine's loads
-    takes, through each combine form: 512 threads per column when the
+    takes, through each combine form.  With a split-list capacity of cap
+    entries: one workgroup per pair and chunk of 8 columns when
+    cap x min(columns, 8) > 256 (300 partials, 8 per round per thread; one
+    and two column chunks); else 512 threads per column when the
     (entries x columns) grid has at most 256 workgroups (600 partials, 256
-    rows per round); otherwise one workgroup per pair when there are at most
-    8 columns (300 partials, 8 per round per thread); else 256 threads per
-    column (300 partials, 128 rows per round)."""
+    rows per round); else 256 threads per column (300 partials, 128 rows per
+    round)."""
     n_long = 600 if batch == 1 else 300
     wcfg = dataclasses.replace(CONFIGS["skewed"], name=f"rounds-{form}", batch=batch,
                                num_q_heads=group)
@@ -153,8 +155,9 @@ def test_combine_rounds_every_form(gpu_lib, form, batch, W, group):
     assert_taskmap_matches(case)
     tm = lbp.read_taskmap(case.plan_ws, case.info)
     assert int(tm["pair_count"].max()) == n_long
-    grid = min(batch, W - 1) * group
-    expected = "wide" if grid <= 256 else "pairs" if group <= 8 else "columns"
+    cap = min(batch, W - 1)
+    expected = ("pairs" if cap * min(group, 8) > 256 else
+                "wide" if cap * group <= 256 else "columns")
     assert expected == form
     out = run_attend(case)
     compare(case, out, oracle_pairs(case, 0, all_pairs(case)), f"combine {form}")
