@@ -105,6 +105,13 @@ namespace {
 #ifndef LBP_TILE_SUB
 #define LBP_TILE_SUB 2
 #endif
+// Tile forms: the K scale times the softmax scale once per token (1).
+#ifndef LBP_TILE_UNMASKED_LOOP
+#define LBP_TILE_UNMASKED_LOOP 1
+#endif
+#ifndef LBP_TILE_KSFOLD
+#define LBP_TILE_KSFOLD 1
+#endif
 #ifndef LBP_KV_LOAD_AUX
 #define LBP_KV_LOAD_AUX 2
 #endif
@@ -711,7 +718,7 @@ __device__ inline void consume(WaveState& st, const typename Kv::Buf& b, const t
 // latencies.  P enters the P.V product as one BF16 value (kOneP in consume).
 // kSub = 2: the slice is 32 tokens, two 16-token sub-slices b[0] and b[1],
 // whose P.V is a single MFMA with K = 32 per output block.
-template <class Kv, bool kCausal, int kNB, int kSub>
+template <class Kv, bool kCausal, int kNB, int kSub, bool kMask = true>
 __device__ inline void consume_tiles(WaveState (&st)[kNB], const typename Kv::Buf (&b)[kSub],
                                      const typename Kv::Q (&q)[kNB], int tok, int e,
                                      const float (&scale_log2)[kNB], int grp,
@@ -733,10 +740,13 @@ __device__ inline void consume_tiles(WaveState (&st)[kNB], const typename Kv::Bu
     for (int u = 0; u < kSub; ++u) {
       const f32x4_t sc = Kv::scores(b[u], q[t]);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        x[t][u][j] = (tok + kSlice * u + 4 * grp + j < (kCausal ? min(e, lim[t]) : e))
-                         ? sc[j] * ks[u][j] * scale_log2[t]
+      for (int j = 0; j < 4; ++j) {
+        const float v = LBP_TILE_KSFOLD ? sc[j] * (ks[u][j] * scale_log2[t])
+                                        : sc[j] * ks[u][j] * scale_log2[t];
+        x[t][u][j] = !kMask || tok + kSlice * u + 4 * grp + j < (kCausal ? min(e, lim[t]) : e)
+                         ? v
                          : -INFINITY;
+      }
       mx = fmaxf(mx, fmaxf(fmaxf(x[t][u][0], x[t][u][1]), fmaxf(x[t][u][2], x[t][u][3])));
     }
     mx = wave_max_across_groups(mx);
@@ -1043,18 +1053,26 @@ __device__ inline void attend_bin(const AttendArgs& a, const int32_t* __restrict
       const int ns = wave_slices(tok, t_end, step);
       // (one tile spelled out, as in the query setup above)
       const float sc0 = Kv::score_scale(qb[0], a.scale_log2);
-      auto compute = [&](const SBuf& cur) {
+      // kMask: the per-token mask of the descriptor's end and the causal
+      // limits.  In the tile forms only a wave's last span can need it: the
+      // spans before it end at least step - kSpan tokens before the
+      // descriptor's end, and no query token's limit lies more than
+      // q_len - 1 <= C - 1 tokens before the pair's end.
+      static_assert(kNB == 1 || step - kSpan + 2 > 16 * kNB, "unmasked spans must be whole");
+      auto compute = [&](const SBuf& cur, auto mask) {
         if constexpr (kNB == 1) {
           consume<Kv, kCausal>(st[0], cur, qb[0], tok, t_end, sc0, grp, lim[0]);
         } else {
+          constexpr bool kMask = decltype(mask)::value || !LBP_TILE_UNMASKED_LOOP;
           float sct[kNB];
 #pragma unroll
           for (int t = 0; t < kNB; ++t) sct[t] = Kv::score_scale(qb[t], a.scale_log2);
           if constexpr (kSub == 1) {
             const typename Kv::Buf one[1] = {cur};
-            consume_tiles<Kv, kCausal, kNB, 1>(st, one, qb, tok, t_end, sct, grp, lim);
+            consume_tiles<Kv, kCausal, kNB, 1, kMask>(st, one, qb, tok, t_end, sct, grp, lim);
           } else {
-            consume_tiles<Kv, kCausal, kNB, kSub>(st, cur.s, qb, tok, t_end, sct, grp, lim);
+            consume_tiles<Kv, kCausal, kNB, kSub, kMask>(st, cur.s, qb, tok, t_end, sct, grp,
+                                                         lim);
           }
         }
       };
@@ -1062,7 +1080,7 @@ __device__ inline void attend_bin(const AttendArgs& a, const int32_t* __restrict
         issue_span(nxt, g, tok + step, t_end, page_of(a, pt, r, tok + step, t_end));
 #pragma unroll
         for (int t = 0; t < kNB; ++t) Kv::after_loads(qb[t]);
-        compute(cur);
+        compute(cur, std::false_type{});
         tok += step;
       };
       if (ns > 0) {
@@ -1074,7 +1092,7 @@ __device__ inline void attend_bin(const AttendArgs& a, const int32_t* __restrict
           step_on(buf[0], buf[1]);
           buf[0] = buf[1];
         }
-        compute(buf[0]);
+        compute(buf[0], std::true_type{});
       }
     }
     // the next descriptor's query and first slice, the query first: as the
