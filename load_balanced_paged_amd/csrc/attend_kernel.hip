@@ -65,11 +65,10 @@
 //  * Multi-token verification (q_len > 1 query tokens per request, each
 //    attending causally up to its own position): the G * q_len query rows of
 //    a KV head are the MFMA columns.  Up to 16 columns run the loop above
-//    with a per-column causal limit, up to 32 the same loop with two
-//    16-column tiles per wave (each slice's K and V serve both); past 32, a
-//    staged instance splits the columns into blocks over groups of waves and
-//    shares each KV slice through an LDS ring, so that every KV byte is
-//    still fetched once per workgroup (see attend_bin).
+//    with a per-column causal limit; past 16, every wave keeps one wave
+//    state per 16-column tile (up to four) and computes all of them from
+//    each slice it loads, so each KV byte is still fetched once per
+//    workgroup (see attend_bin).
 #include "lse_merge.h"
 
 namespace lbp {
@@ -88,17 +87,17 @@ namespace {
 #ifndef LBP_FP8Q_WAVES
 #define LBP_FP8Q_WAVES 8
 #endif
-// Multi-token verification: 33-48 query columns as three 16-column tiles per
-// wave (1) or through the staged instance (0), and the wave counts of the
-// two- and three-tile instances (0: the format's own).
-#ifndef LBP_TILE3
-#define LBP_TILE3 1
+// Multi-token verification: waves of the instances with three or four
+// column tiles, and of the two-tile instance per KV format (0: the format's
+// own wave count).
+#ifndef LBP_TILE_WAVES
+#define LBP_TILE_WAVES 4
 #endif
-#ifndef LBP_TILE3_WAVES
-#define LBP_TILE3_WAVES 4
+#ifndef LBP_BF16_TILE2_WAVES
+#define LBP_BF16_TILE2_WAVES 0
 #endif
-#ifndef LBP_TILE2_WAVES
-#define LBP_TILE2_WAVES 0
+#ifndef LBP_FP8_TILE2_WAVES
+#define LBP_FP8_TILE2_WAVES 4
 #endif
 // Tokens per step of a wave in the tile forms: 16 (1) or 32 (2, one K = 32
 // P.V product per pair of 16-token sub-slices).
@@ -172,15 +171,6 @@ __device__ inline float load_lse_coherent(const SplitRsrc& r, int64_t row) {
                             __builtin_amdgcn_raw_buffer_load_b32(r.lse, int(row * 4), 0, kCoherentAux));
 }
 
-// Keeps the memory operations on either side in program order (an empty
-// asm statement that clobbers memory): where one code path would otherwise
-// issue a slice's loads in another order than the loop that waits for them,
-// the wait counts at the join fall back to the most conservative.
-template <bool kOrdered>
-__device__ inline void keep_order() {
-  if constexpr (kOrdered) asm volatile("" ::: "memory");
-}
-
 // Ties a register block to the memory operations issued before it (an empty
 // asm statement that clobbers memory and claims to rewrite the block): math
 // that reads the block cannot be scheduled above those loads.  The decode
@@ -243,12 +233,12 @@ struct SliceRsrc {
 
 // Query rows of the query columns: column c is query token c / G, head c % G
 // of KV head g's group, at row (r * q_len + c / G) * Hq + g * G + c % G.
-// MFMA lane column n of a wave in column block b holds column
-// c = b * block_cols + n.  The lane's row relative to column 0's, and the
+// MFMA lane column n of a wave's tile t holds column c = 16 t + n (col0 =
+// 16 t below).  The lane's row relative to column 0's, and the
 // span of rows the buffer resource covers, depend only on the launch and the
 // wave, so they are computed once per kernel (the division stays out of the
 // descriptor loop, where it would delay the query loads behind the KV
-// loads).  Lanes past the block's columns get a row past the resource's end
+// loads).  Lanes past the tile's columns get a row past the resource's end
 // and read zeros.  With one query token (the non-causal instance, a single
 // block) the row is the column itself, which keeps the query offsets equal to
 // the K row offsets of the same lanes.
@@ -290,7 +280,8 @@ struct Bf16Kv {
   static constexpr int kRowBytes = kHeadDim * 2;
   static constexpr bool kScaled = false;
   static constexpr bool kSplitP = LBP_BF16_SPLIT_P;   // P.V with P as BF16 hi + lo
-  static constexpr bool kWidenK = false;              // K is BF16 already
+  // two-tile verification instance: its wave count (0: kWaves)
+  static constexpr int kTile2Waves = LBP_BF16_TILE2_WAVES;
   static constexpr int kWaves = LBP_BF16_WAVES;    // waves per workgroup
   struct Buf {
     i32x4_t k[4];   // K A-operand, one per 32-dim k-step
@@ -311,19 +302,14 @@ struct Bf16Kv {
     for (int k = 0; k < 4; ++k) lbp::after_loads(q.v[k]);
   }
 
-  template <bool kOrdered = false>
   __device__ static void issue(Buf& b, const SliceRsrc& rs, int lane) {
     const int m = lane & 15, grp = lane >> 4;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+    for (int s = 0; s < 4; ++s)
       b.k[s] = __builtin_amdgcn_raw_buffer_load_b128(rs.k, m * kRowBytes + 64 * s + 16 * grp, 0, kLoadAux);
-      keep_order<kOrdered>();
-    }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 4; ++i)
       b.v[i] = __builtin_amdgcn_raw_buffer_load_b128(rs.v, (4 * grp + i) * kRowBytes + 16 * m, 0, kLoadAux);
-      keep_order<kOrdered>();
-    }
   }
 
   // (B: any slice type holding the K operand as member k)
@@ -366,6 +352,9 @@ struct Fp8Kv {
   // two slices each keep enough loads in flight, and fewer waves make each
   // descriptor's merge cheaper
   static constexpr int kWaves = LBP_FP8_WAVES;
+  // two-tile verification instance: one wave per SIMD, 32-token spans (the
+  // widening leaves a two-wave instance short of registers for both tiles)
+  static constexpr int kTile2Waves = LBP_FP8_TILE2_WAVES;
   struct Buf {
     i32x4_t k[2];   // 32 codes: dims [32grp, 32grp + 32) of token m
     i32x2_t v[4];   // 8 codes: dims [8c, 8c+8) of token 4grp+i
@@ -387,21 +376,15 @@ struct Fp8Kv {
     for (int k = 0; k < 4; ++k) lbp::after_loads(q.v[k]);
   }
 
-  template <bool kOrdered = false>
   __device__ static void issue(Buf& b, const SliceRsrc& rs, int lane) {
     const int m = lane & 15, grp = lane >> 4;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < 2; ++h)
       b.k[h] = __builtin_amdgcn_raw_buffer_load_b128(rs.k, m * kRowBytes + 32 * grp + 16 * h, 0, kLoadAux);
-      keep_order<kOrdered>();
-    }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 4; ++i)
       b.v[i] = __builtin_amdgcn_raw_buffer_load_b64(rs.v, (4 * grp + i) * kRowBytes + 8 * m, 0, kLoadAux);
-      keep_order<kOrdered>();
-    }
     b.ks = __builtin_amdgcn_raw_buffer_load_b128(rs.ks, 16 * grp, 0, kLoadAux);
-    keep_order<kOrdered>();
     b.vs = __builtin_amdgcn_raw_buffer_load_b128(rs.vs, 16 * grp, 0, kLoadAux);
   }
 
@@ -419,8 +402,6 @@ struct Fp8Kv {
     return i32x4_t{int(widen2<false>(c0)), int(widen2<true>(c0)), int(widen2<false>(c1)),
                    int(widen2<true>(c1))};
   }
-  // the staged image may hold K already widened (Fp8KvQ8 scores on the codes)
-  static constexpr bool kWidenK = true;
 
   template <class B>
   __device__ static f32x4_t scores(const B& b, const Q& q) {
@@ -458,7 +439,6 @@ struct Fp8Kv {
 // probabilities take the FP8 KV path above.
 struct Fp8KvQ8 : Fp8Kv {
   static constexpr int kWaves = LBP_FP8Q_WAVES;
-  static constexpr bool kWidenK = false;
   struct Q {
     i32x4_t c[2];   // codes of dims [32grp, 32grp + 32) of head n
     float scale;    // the head's Q scale (0 for columns past the group)
@@ -495,79 +475,6 @@ struct Fp8KvQ8 : Fp8Kv {
       s = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(codes8(b.k, k), codes8(q.c, k), s, 0, 0, 0);
     return s;
   }
-};
-
-// A slice as the staged instance keeps it in LDS: the K operand as loaded,
-// the eight P.V A operands already built (for FP8: already widened), and the
-// FP8 scales.  The wave that loads a slice builds this once; every column
-// block then reads it ready for the MFMAs.  128 bytes per lane in every
-// format (160 in the widened-K form below).
-template <class Kv, bool kScaled = Kv::kScaled>
-struct StagedSlice {
-  decltype(Kv::Buf::k) k;
-  i16x4_t v[8];
-};
-template <class Kv>
-struct StagedSlice<Kv, true> {
-  decltype(Kv::Buf::k) k;
-  i16x4_t v[8];
-  i32x4_t ks, vs;
-};
-
-// FP8 KV with a BF16 query, K widened to BF16 once by the loading wave
-// instead of once per column block: 160 bytes per lane.
-struct StagedSliceWideK {
-  i32x4_t k[4];   // K operand per 32-dim k-step, as BF16
-  i16x4_t v[8];
-  i32x4_t ks, vs;
-};
-
-// kWide: the image holds K widened (StagedSliceWideK); only where the ring
-// of 2 x waves images still fits the CU's LDS.
-template <class Kv, bool kWide = false>
-struct Staged {
-  using Buf = std::conditional_t<kWide, StagedSliceWideK, StagedSlice<Kv>>;
-  using Q = typename Kv::Q;
-  static constexpr bool kSplitP = Kv::kSplitP;
-  static constexpr bool kScaled = Kv::kScaled;
-  __device__ static Buf build(const typename Kv::Buf& b) {
-    Buf t;
-    if constexpr (kWide) {
-#pragma unroll
-      for (int k = 0; k < 4; ++k) t.k[k] = Kv::k_bf16(b, k);
-    } else {
-#pragma unroll
-      for (int i = 0; i < int(sizeof(t.k) / sizeof(t.k[0])); ++i) t.k[i] = b.k[i];
-    }
-#pragma unroll
-    for (int mb = 0; mb < 8; ++mb) t.v[mb] = Kv::v_operand(b, mb);
-    if constexpr (kScaled) {
-      t.ks = b.ks;
-      t.vs = b.vs;
-    }
-    return t;
-  }
-  __device__ static f32x4_t scores(const Buf& b, const Q& q) {
-    if constexpr (kWide) {
-      f32x4_t s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, b.k[k]), q.v[k],
-                                                    s, 0, 0, 0);
-      return s;
-    } else {
-      return Kv::scores(b, q);
-    }
-  }
-  __device__ static f32x4_t k_scales(const Buf& b) {
-    if constexpr (kScaled) return __builtin_bit_cast(f32x4_t, b.ks);
-    else return f32x4_t{1.f, 1.f, 1.f, 1.f};
-  }
-  __device__ static f32x4_t v_scales(const Buf& b) {
-    if constexpr (kScaled) return __builtin_bit_cast(f32x4_t, b.vs);
-    else return f32x4_t{1.f, 1.f, 1.f, 1.f};
-  }
-  __device__ static i16x4_t v_operand(const Buf& b, int mb) { return b.v[mb]; }
 };
 
 // ---------------------------------------------------------------------------
@@ -622,14 +529,11 @@ struct WaveState {
   f32x4_t acc[8];   // O^T blocks: lane (grp, n) holds dims 32grp + 8j + mb
 };
 
-// lim: this lane's column sees tokens < lim (its causal limit in
+// One slice into one wave state (decode, and verification up to 16
+// columns).  lim: this lane's column sees tokens < lim (its causal limit in
 // multi-token verification, kCausal only).  A column with no visible token
-// so far keeps an empty state (m = -inf, l = 0, acc = 0).  Kv: the slice
-// format (a KV format, or its staged form).  kLazy: skip the rescale of the
-// running state when no lane's maximum grew; its factor would be exactly 1,
-// so the result is the same bit for bit.  kOneP: P as one BF16 value even
-// where the format asks for the pair (see below).
-template <class Kv, bool kCausal, bool kLazy = false, bool kOneP = false>
+// so far keeps an empty state (m = -inf, l = 0, acc = 0).
+template <class Kv, bool kCausal>
 __device__ inline void consume(WaveState& st, const typename Kv::Buf& b, const typename Kv::Q& q,
                                int tok, int e, float scale_log2, int grp, int lim) {
   f32x4_t s = Kv::scores(b, q);
@@ -646,10 +550,7 @@ __device__ inline void consume(WaveState& st, const typename Kv::Buf& b, const t
   // without a causal limit every slice has a visible token in every column,
   // so the running max is finite after the first one
   const float ref = kCausal ? finite_or_zero(m_new) : m_new;
-  if (!kLazy || __ballot(m_new > st.m) != 0) {
-    // (an opaque statement keeps the skip a branch instead of a select
-    // folded into the multiplies, which would do the work anyway)
-    if constexpr (kLazy) asm volatile("");
+  {
     const float alpha = __builtin_amdgcn_exp2f(st.m - ref);
     st.l *= alpha;
 #pragma unroll
@@ -657,20 +558,13 @@ __device__ inline void consume(WaveState& st, const typename Kv::Buf& b, const t
   }
   st.m = m_new;
   // BF16 KV: P enters the P.V product as a BF16 pair (below), which the
-  // HBM-bound decode loop pays nothing for.  The verification instances past
-  // 16 columns, bound by their math, take one BF16 P instead (kOneP) and sum
-  // the same rounded values into l: the output is then an exact convex
-  // combination of the V rows under the rounded weights, whose error scales
-  // with |v - o| rather than |v| (a row with one dominant token stays
-  // exact).  The FP8 formats fold the V scale into P and keep one BF16 P with
-  // l from the unrounded values.
-  constexpr bool kSplit = Kv::kSplitP && !kOneP;
-  constexpr bool kRoundedSum = Kv::kSplitP && kOneP;
+  // HBM-bound decode loop pays nothing for.  The FP8 formats fold the V
+  // scale into P and keep one BF16 P with l from the unrounded values.
   float p[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) p[j] = __builtin_amdgcn_exp2f(x[j] - ref);
-  if constexpr (!kRoundedSum) st.l += (p[0] + p[1]) + (p[2] + p[3]);
-  if constexpr (kSplit) {
+  st.l += (p[0] + p[1]) + (p[2] + p[3]);
+  if constexpr (Kv::kSplitP) {
     const float pv[4] = {p[0] * vs[0], p[1] * vs[1], p[2] * vs[2], p[3] * vs[3]};
     i32x2_t pb2 = {int(pack_bf16(pv[0], pv[1])), int(pack_bf16(pv[2], pv[3]))};
     const i16x4_t pb = __builtin_bit_cast(i16x4_t, pb2);
@@ -694,11 +588,6 @@ __device__ inline void consume(WaveState& st, const typename Kv::Buf& b, const t
   } else {
     i32x2_t pb2 = {int(pack_bf16(p[0] * vs[0], p[1] * vs[1])),
                    int(pack_bf16(p[2] * vs[2], p[3] * vs[3]))};
-    if constexpr (kRoundedSum) {
-      const uint32_t h01 = uint32_t(pb2[0]), h23 = uint32_t(pb2[1]);
-      st.l += (__builtin_bit_cast(float, h01 << 16) + __builtin_bit_cast(float, h01 & 0xFFFF0000u)) +
-              (__builtin_bit_cast(float, h23 << 16) + __builtin_bit_cast(float, h23 & 0xFFFF0000u));
-    }
     const i16x4_t pb = __builtin_bit_cast(i16x4_t, pb2);
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb)
@@ -715,7 +604,12 @@ __device__ inline void consume(WaveState& st, const typename Kv::Buf& b, const t
 // and P.V products.  The tiles' chains are independent, and with one branch
 // per slice instead of one per tile the scheduler can interleave them, which
 // a wave alone on its SIMD needs to hide the MFMA and transcendental
-// latencies.  P enters the P.V product as one BF16 value (kOneP in consume).
+// latencies.  Bound by their math rather than by HBM, these forms take P as
+// one BF16 value instead of consume's BF16 pair; for BF16 KV they sum the same
+// rounded values into l, so the output is an exact convex combination of the
+// V rows under the rounded weights, whose error scales with |v - o| rather
+// than |v| (a row with one dominant token stays exact).  The FP8 formats
+// keep l from the unrounded values, as in consume.
 // kSub = 2: the slice is 32 tokens, two 16-token sub-slices b[0] and b[1],
 // whose P.V is a single MFMA with K = 32 per output block.
 template <class Kv, bool kCausal, int kNB, int kSub, bool kMask = true>
@@ -809,29 +703,13 @@ __device__ inline void consume_tiles(WaveState (&st)[kNB], const typename Kv::Bu
   }
 }
 
-// Waves of the staged instances (column blocks, more than 32 query columns),
-// for every KV format; their LDS ring of 2 x waves slices must fit the CU.
-// The column blocks divide the waves evenly: 8 waves give four full blocks
-// for 49-64 columns; 33-48 columns over 8 waves would be four blocks of at
-// most 12, leaving a quarter of every MFMA tile idle, so those run 6 waves
-// (three blocks of at most 16).
-constexpr int kStagedWaves = 8;
-constexpr int kStagedWaves33To48 = 6;
-
-// The staged form of format Kv at kStagedW waves: K widened in the image
-// where the format allows it and the ring of 2 x 6 images (120 KB) fits;
-// at 8 waves it would need the CU's whole 160 KB.
-template <class Kv, int kStagedW>
-using StagedOf = Staged<Kv, Kv::kWidenK && kStagedW == kStagedWaves33To48>;
-
-// kStagedW: 0 for the decode and causal instances, else the staged
-// instance's wave count; kTileW: the wave count of a causal instance with
-// several column tiles, 0 for the format's own.
-template <class Kv, int kStagedW, int kTileW = 0>
+// The wave count of an instance: the format's own, or kTileW for a causal
+// instance with several column tiles.
+template <class Kv, int kTileW = 0>
 constexpr int waves_of() {
-  return kStagedW > 0 ? kStagedW : kTileW > 0 ? kTileW : Kv::kWaves;
+  return kTileW > 0 ? kTileW : Kv::kWaves;
 }
-constexpr int kTile2Waves = LBP_TILE2_WAVES;
+constexpr int kTileWaves = LBP_TILE_WAVES;   // instances with three or four tiles
 
 // The loads of one wave step: one 16-token slice, or kSub consecutive ones
 // (the tile forms' 32-token spans).
@@ -841,31 +719,6 @@ struct SpanOf {
 };
 template <class Kv, int kSub>
 using SpanBuf = std::conditional_t<kSub == 1, typename Kv::Buf, SpanOf<Kv, kSub>>;
-constexpr int kTile3Waves = LBP_TILE3_WAVES;
-
-// A slice's register image in LDS (Kv: a slice format with member type
-// Buf): vector v of lane l at [v][l], so each 16-byte write or read of a
-// wave covers 1 KB of consecutive LDS.
-template <class Kv>
-struct BufImage {
-  static constexpr int kVecs = sizeof(typename Kv::Buf) / 16;
-  static_assert(kVecs * 16 == sizeof(typename Kv::Buf), "Buf must be whole 16-byte vectors");
-  static constexpr int kBytes = kVecs * 64 * 16;   // one slice, one wave
-  struct Raw {
-    i32x4_t v[kVecs];
-  };
-  __device__ static void store(i32x4_t* dst, const typename Kv::Buf& b, int lane) {
-    const Raw r = __builtin_bit_cast(Raw, b);
-#pragma unroll
-    for (int v = 0; v < kVecs; ++v) dst[v * 64 + lane] = r.v[v];
-  }
-  __device__ static typename Kv::Buf load(const i32x4_t* src, int lane) {
-    Raw r;
-#pragma unroll
-    for (int v = 0; v < kVecs; ++v) r.v[v] = src[v * 64 + lane];
-    return __builtin_bit_cast(typename Kv::Buf, r);
-  }
-};
 
 // Drains one bin: every descriptor in it, in order.
 //
@@ -876,32 +729,22 @@ struct BufImage {
 // latency overlaps the merge and the wait for the slowest wave instead of
 // following them.
 //
-// kNB: 16-column MFMA tiles per wave in the decode/causal form (1, or 2 for
-// 17-32 query columns: every wave keeps a wave state per tile and computes
-// both from each slice it loads, which at up to 32 columns stays cheaper
-// than staging slices through LDS).
-//
-// Staged form (kStaged: multi-token verification with more than 32 query
-// columns): the columns split into nblk blocks of at most 16, one per group
-// of waves.  The descriptor is walked in rounds of one slice per wave:
-// every wave loads a different slice (two rounds in flight, as above),
-// copies it into a two-stage LDS ring once it has arrived, and after one
-// barrier per round computes, for its block's columns, its share of the
-// round's slices from LDS.  Every KV byte is then fetched once per
-// workgroup with the full set of loads in flight, while each wave keeps the
-// register state of a single 16-column tile.
-template <class Kv, bool kCausal, int kStagedW, int kNB, int kTileW>
+// kNB: 16-column MFMA tiles per wave (1 for decode and up to 16 query
+// columns; 2, 3 or 4 for 17-64 columns in multi-token verification: every
+// wave keeps a wave state per tile and computes all of them from each slice
+// it loads, so every KV byte is still fetched once per workgroup).  kTileW:
+// the tile form's wave count (0: the format's own).  With one wave per SIMD
+// the register file has room for 32-token spans (two slices per step).
+template <class Kv, bool kCausal, int kNB, int kTileW>
 __device__ inline void attend_bin(const AttendArgs& a, const int32_t* __restrict__ pt,
                                   const int4* __restrict__ descs,
                                   const int32_t* __restrict__ pair_count,
                                   const int32_t* __restrict__ bin_offset,
                                   const int4* __restrict__ bin_first,
                                   const int32_t* __restrict__ pair_first, float* smem, int bin) {
-  constexpr bool kStaged = kStagedW > 0;
-  constexpr int kWaves = waves_of<Kv, kStagedW, kTileW>();
+  constexpr int kWaves = waves_of<Kv, kTileW>();
   constexpr int kThreads = kWaves * 64;
-  static_assert(kCausal || !kStaged, "the staged form serves verification only");
-  static_assert(kNB == 1 || (kNB <= 3 && kCausal && !kStaged),
+  static_assert(kNB == 1 || (kNB <= 4 && kCausal),
                 "several column tiles per wave: causal form only");
   static_assert(kTileW == 0 || kNB > 1, "a wave count of its own: tile forms only");
   const int lane = threadIdx.x & 63;
@@ -909,30 +752,19 @@ __device__ inline void attend_bin(const AttendArgs& a, const int32_t* __restrict
   const int n = lane & 15;         // MFMA column of this lane within its block
   const int grp = lane >> 4;
   const int G = a.group;
-  const int C = a.ncols;           // G * q_len
-  // column blocks, staged form: the waves split into nblk equal groups,
-  // group b computes columns [b * cpb, b * cpb + cpb); otherwise every wave
-  // computes all C <= 16 kNB columns, as kNB 16-column MFMA tiles
-  const int nblk = kStaged ? a.col_blocks : 1;
-  const int wpb = kStaged ? kWaves / nblk : kWaves;    // waves per block
-  const int blk = kStaged ? wave / wpb : 0;
-  const int wslot = kStaged ? wave - blk * wpb : wave;  // the wave's place in its block
-  const int cpb = kStaged ? a.block_cols : C;          // columns per block, <= 16 staged
-  const int col0 = blk * cpb;
-  const int nvalid = kStaged ? min(cpb, C - col0) : C; // this block's columns
+  const int C = a.ncols;           // G * q_len: every wave computes all C <= 16 kNB
   // the tile forms with one wave per SIMD (512 registers) step by spans of
   // kSub 16-token sub-slices; at two waves per SIMD the second sub-slice's
   // registers do not fit
   constexpr int kSub = kNB > 1 && kWaves <= 4 ? LBP_TILE_SUB : 1;
-  static_assert(kSub == 1 || !kStaged, "spans: tile forms only");
   constexpr int kSpan = kSlice * kSub;
-  constexpr int step = kWaves * kSpan;                 // tokens per round / per wave stride
+  constexpr int step = kWaves * kSpan;                 // a wave's stride in tokens
   using SBuf = SpanBuf<Kv, kSub>;
   // per wave in LDS for the merge: m and l of 16 kNB columns, then the rows
   constexpr int kRedHead = 32 * kNB;
-  const int red_stride = kRedHead + cpb * kRedRow;
-  // tile t's columns: [col0 + 16 t, + tile_cols(t))
-  auto tile_cols = [&](int t) { return kNB == 1 ? nvalid : min(16, C - 16 * t); };
+  const int red_stride = kRedHead + C * kRedRow;
+  // tile t's columns: [16 t, + tile_cols(t))
+  auto tile_cols = [&](int t) { return kNB == 1 ? C : min(16, C - 16 * t); };
   float* red = smem + wave * red_stride;
   // range and first descriptor are independent loads: one round trip
   const int d_begin = bin_offset[bin];
@@ -948,7 +780,7 @@ __device__ inline void attend_bin(const AttendArgs& a, const int32_t* __restrict
   // it: spans start at multiples of 32) is `page`
   auto issue_span = [&](SBuf& b, int gq, int t, int e, int page) {
     if constexpr (kSub == 1) {
-      Kv::template issue<kStaged>(b, slice_rsrc_at<Kv>(a, gq, t, e, page), lane);
+      Kv::issue(b, slice_rsrc_at<Kv>(a, gq, t, e, page), lane);
     } else {
 #pragma unroll
       for (int u = 0; u < kSub; ++u)
@@ -958,12 +790,12 @@ __device__ inline void attend_bin(const AttendArgs& a, const int32_t* __restrict
   if constexpr (kNB == 1) {
     // (spelled out: the loop form below, though equivalent, made the
     // compiler schedule the decode instance differently, and slower)
-    ql[0] = q_lane<kCausal>(a, n, col0, nvalid);
+    ql[0] = q_lane<kCausal>(a, n, 0, C);
     Kv::load_q(qb[0], a, ql[0], ds.x, ds.y, grp);
   } else {
 #pragma unroll
     for (int t = 0; t < kNB; ++t) {
-      ql[t] = q_lane<kCausal>(a, n, col0 + 16 * t, tile_cols(t));
+      ql[t] = q_lane<kCausal>(a, n, 16 * t, tile_cols(t));
       Kv::load_q(qb[t], a, ql[t], ds.x, ds.y, grp);
     }
   }
@@ -993,7 +825,7 @@ __device__ inline void attend_bin(const AttendArgs& a, const int32_t* __restrict
       lim[t] = INT_MAX;
       if constexpr (kCausal) {
         const int L = descs[pair_first[p] + pair_count[p] - 1].w;
-        lim[t] = L - a.q_len + 1 + (col0 + 16 * t + n) / G;
+        lim[t] = L - a.q_len + 1 + (16 * t + n) / G;
       }
       st[t].m = -INFINITY;
       st[t].l = 0.f;
@@ -1001,113 +833,71 @@ __device__ inline void attend_bin(const AttendArgs& a, const int32_t* __restrict
       for (int mb = 0; mb < 8; ++mb) st[t].acc[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
 
-    // buf[0] already holds (or is loading) this wave's first slice of d; a
-    // slice past t_end loads nothing
-    if constexpr (kStaged) {
-      using S = StagedOf<Kv, kStagedW>;
-      constexpr int kImg = BufImage<S>::kBytes;
-      i32x4_t* ring = reinterpret_cast<i32x4_t*>(smem);   // [2 stages][kWaves slices][image]
-      int base = t_begin;          // round: tokens [base, base + step), slice w at base + 16 w
-      Kv::template issue<true>(buf[1], slice_rsrc<Kv>(a, pt, g, r, base + step + wave * kSlice, t_end),
-                               lane);
-      // one round from ring stage u (buf[u] holds this wave's slice of it)
-      auto round = [&](const int u) {
-        i32x4_t* stage = ring + u * (kWaves * kImg / 16);
-        BufImage<S>::store(stage + wave * (kImg / 16), S::build(buf[u]), lane);
-        Kv::template issue<true>(
-            buf[u], slice_rsrc<Kv>(a, pt, g, r, base + 2 * step + wave * kSlice, t_end), lane);
-        // the round's slices are in LDS; every wave is past the round that
-        // last used this stage
-        __syncthreads();
-        for (int j = wslot; j < kWaves; j += wpb) {
-          const int tok = base + j * kSlice;
-          if (tok >= t_end) break;
-          const typename S::Buf b = BufImage<S>::load(stage + j * (kImg / 16), lane);
-          consume<S, kCausal, true, true>(st[0], b, qb[0], tok, t_end,
-                                    Kv::score_scale(qb[0], a.scale_log2), grp, lim[0]);
-        }
-        base += step;
-      };
-      // rounds go in pairs (a second round past t_end loads and computes
-      // nothing): with a single exit, every path to the loop top has buf[0]
-      // as the older of the two loads in flight, so the waits stay exact
-      do {
-        round(0);
-        round(1);
-      } while (base < t_end);
-      // the merge below reuses the ring's LDS
-      __syncthreads();
-    } else {
-      // The wave's n slices of the descriptor, the first in buf[0]: each one
-      // that has a successor issues the successor's loads and then
-      // computes, with both in flight; the last one issues nothing (the next
-      // descriptor's loads follow the loop; a load past the end, though it
-      // moves no data, costs as much issue and queue time as a real one).
-      // Whole trips of two steps, then for even n one more step and a copy
-      // of the last slice from buf[1] to buf[0] (which waits for it), so a
-      // single code path computes every last slice: with one such path per
-      // parity the compiler kept two copies of the wave state.  The loop has
-      // one exit and every path to a step has the same loads outstanding, so
-      // the compiler's wait counts stay exact.
-      int tok = t_begin + wave * kSpan;
-      const int ns = wave_slices(tok, t_end, step);
-      // (one tile spelled out, as in the query setup above)
-      const float sc0 = Kv::score_scale(qb[0], a.scale_log2);
-      // kMask: the per-token mask of the descriptor's end and the causal
-      // limits.  In the tile forms only a wave's last span can need it: the
-      // spans before it end at least step - kSpan tokens before the
-      // descriptor's end, and no query token's limit lies more than
-      // q_len - 1 <= C - 1 tokens before the pair's end.
-      static_assert(kNB == 1 || step - kSpan + 2 > 16 * kNB, "unmasked spans must be whole");
-      auto compute = [&](const SBuf& cur, auto mask) {
-        if constexpr (kNB == 1) {
-          consume<Kv, kCausal>(st[0], cur, qb[0], tok, t_end, sc0, grp, lim[0]);
+    // The wave's n slices (spans) of the descriptor, the first already in
+    // (or loading into) buf[0]; a slice past t_end loads nothing.  Each one
+    // that has a successor issues the successor's loads and then computes,
+    // with both in flight; the last one issues nothing (the next
+    // descriptor's loads follow the loop; a load past the end, though it
+    // moves no data, costs as much issue and queue time as a real one).
+    // Whole trips of two steps, then for even n one more step and a copy of
+    // the last slice from buf[1] to buf[0] (which waits for it), so a single
+    // code path computes every last slice: with one such path per parity the
+    // compiler kept two copies of the wave state.  The loop has one exit and
+    // every path to a step has the same loads outstanding, so the compiler's
+    // wait counts stay exact.
+    int tok = t_begin + wave * kSpan;
+    const int ns = wave_slices(tok, t_end, step);
+    // (one tile spelled out, as in the query setup above)
+    const float sc0 = Kv::score_scale(qb[0], a.scale_log2);
+    // kMask: the per-token mask of the descriptor's end and the causal
+    // limits.  In the tile forms only a wave's last span can need it: the
+    // spans before it end at least step - kSpan tokens before the
+    // descriptor's end, and no query token's limit lies more than
+    // q_len - 1 <= C - 1 tokens before the pair's end.
+    static_assert(kNB == 1 || step - kSpan + 2 > 16 * kNB, "unmasked spans must be whole");
+    auto compute = [&](const SBuf& cur, auto mask) {
+      if constexpr (kNB == 1) {
+        consume<Kv, kCausal>(st[0], cur, qb[0], tok, t_end, sc0, grp, lim[0]);
+      } else {
+        constexpr bool kMask = decltype(mask)::value || !LBP_TILE_UNMASKED_LOOP;
+        float sct[kNB];
+#pragma unroll
+        for (int t = 0; t < kNB; ++t) sct[t] = Kv::score_scale(qb[t], a.scale_log2);
+        if constexpr (kSub == 1) {
+          const typename Kv::Buf one[1] = {cur};
+          consume_tiles<Kv, kCausal, kNB, 1, kMask>(st, one, qb, tok, t_end, sct, grp, lim);
         } else {
-          constexpr bool kMask = decltype(mask)::value || !LBP_TILE_UNMASKED_LOOP;
-          float sct[kNB];
-#pragma unroll
-          for (int t = 0; t < kNB; ++t) sct[t] = Kv::score_scale(qb[t], a.scale_log2);
-          if constexpr (kSub == 1) {
-            const typename Kv::Buf one[1] = {cur};
-            consume_tiles<Kv, kCausal, kNB, 1, kMask>(st, one, qb, tok, t_end, sct, grp, lim);
-          } else {
-            consume_tiles<Kv, kCausal, kNB, kSub, kMask>(st, cur.s, qb, tok, t_end, sct, grp,
-                                                         lim);
-          }
+          consume_tiles<Kv, kCausal, kNB, kSub, kMask>(st, cur.s, qb, tok, t_end, sct, grp,
+                                                       lim);
         }
-      };
-      auto step_on = [&](const SBuf& cur, SBuf& nxt) {
-        issue_span(nxt, g, tok + step, t_end, page_of(a, pt, r, tok + step, t_end));
-#pragma unroll
-        for (int t = 0; t < kNB; ++t) Kv::after_loads(qb[t]);
-        compute(cur, std::false_type{});
-        tok += step;
-      };
-      if (ns > 0) {
-        for (int i = (ns - 1) >> 1; i > 0; --i) {
-          step_on(buf[0], buf[1]);
-          step_on(buf[1], buf[0]);
-        }
-        if ((ns & 1) == 0) {
-          step_on(buf[0], buf[1]);
-          buf[0] = buf[1];
-        }
-        compute(buf[0], std::true_type{});
       }
+    };
+    auto step_on = [&](const SBuf& cur, SBuf& nxt) {
+      issue_span(nxt, g, tok + step, t_end, page_of(a, pt, r, tok + step, t_end));
+#pragma unroll
+      for (int t = 0; t < kNB; ++t) Kv::after_loads(qb[t]);
+      compute(cur, std::false_type{});
+      tok += step;
+    };
+    if (ns > 0) {
+      for (int i = (ns - 1) >> 1; i > 0; --i) {
+        step_on(buf[0], buf[1]);
+        step_on(buf[1], buf[0]);
+      }
+      if ((ns & 1) == 0) {
+        step_on(buf[0], buf[1]);
+        buf[0] = buf[1];
+      }
+      compute(buf[0], std::true_type{});
     }
     // the next descriptor's query and first slice, the query first: as the
     // older load it is complete whenever the slice's first K row is, so the
-    // next descriptor's loop can wait for its loads one by one.  The staged
-    // form issues them after the merge's stores instead, and always (past
-    // the bin's last descriptor, an empty token range that moves no data),
-    // so that its round loop is entered with exactly the loads outstanding
-    // that it loops with and the compiler's wait counts stay exact.
-    auto prefetch_next = [&]() {
+    // next descriptor's loop can wait for its loads one by one
+    if (has_next) {
 #pragma unroll
       for (int t = 0; t < kNB; ++t) Kv::load_q(qb[t], a, ql[t], dn.x, dn.y, grp);
       issue_span(buf[0], dn.x, next_tok, dn.w, next_page);
-    };
-    if (!kStaged && has_next) prefetch_next();
+    }
 
     // merge the wave states of this descriptor
 #pragma unroll
@@ -1137,24 +927,21 @@ __device__ inline void attend_bin(const AttendArgs& a, const int32_t* __restrict
     constexpr int kD4 = kHeadDim / 4;
     for (int idx = threadIdx.x; idx < C * kD4; idx += kThreads) {
       const int q = idx / kD4, d4 = idx % kD4;
-      // the waves of q's column block hold it, as their column qc
-      const int qblk = kStaged ? q / cpb : 0;
-      const int qc = q - qblk * cpb;
-      const float* rb = smem + qblk * wpb * red_stride;
+      const float* rb = smem;   // every wave's state of column q
       float M = -INFINITY;
 #pragma unroll
-      for (int w = 0; w < wpb; ++w) M = fmaxf(M, rb[w * red_stride + qc]);
+      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, rb[w * red_stride + q]);
       // a column with no visible token in this descriptor (possible only
       // under a causal limit) gives an empty partial: o = 0, lse = -inf
       const float Mu = kCausal ? finite_or_zero(M) : M;
       float L = 0.f;
       f32x4_t o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int w = 0; w < wpb; ++w) {
+      for (int w = 0; w < kWaves; ++w) {
         const float* rw = rb + w * red_stride;
-        const float c = __builtin_amdgcn_exp2f(rw[qc] - Mu);
-        L += rw[16 * kNB + qc] * c;
-        o += *reinterpret_cast<const f32x4_t*>(rw + kRedHead + qc * kRedRow + 4 * d4) * c;
+        const float c = __builtin_amdgcn_exp2f(rw[q] - Mu);
+        L += rw[16 * kNB + q] * c;
+        o += *reinterpret_cast<const f32x4_t*>(rw + kRedHead + q * kRedRow + 4 * d4) * c;
       }
       const bool empty = kCausal && !(L > 0.f);
       const f32x4_t on = empty ? f32x4_t{0.f, 0.f, 0.f, 0.f} : o / L;
@@ -1179,7 +966,6 @@ __device__ inline void attend_bin(const AttendArgs& a, const int32_t* __restrict
       }
     }
     __syncthreads();
-    if (kStaged) prefetch_next();
     ds = dn;
   }
 }
@@ -1395,14 +1181,14 @@ __device__ void finish_split_pairs(const AttendArgs& a, const int4* __restrict__
 // loop's registers toward occupancies that never occur, and whenever that
 // loop is the kernel's register peak it stops issuing the next slice ahead
 // of the current slice's math.
-template <class Kv, bool kCausal, int kStagedW, int kNB, int kTileW>
-__global__ __launch_bounds__((waves_of<Kv, kStagedW, kTileW>() * 64))
-__attribute__((amdgpu_waves_per_eu((waves_of<Kv, kStagedW, kTileW>() + 3) / 4,
-                                   (waves_of<Kv, kStagedW, kTileW>() + 3) / 4))) void attend_kernel(
+template <class Kv, bool kCausal, int kNB, int kTileW>
+__global__ __launch_bounds__((waves_of<Kv, kTileW>() * 64))
+__attribute__((amdgpu_waves_per_eu((waves_of<Kv, kTileW>() + 3) / 4,
+                                   (waves_of<Kv, kTileW>() + 3) / 4))) void attend_kernel(
     AttendArgs a, const int32_t* __restrict__ page_table, const int4* __restrict__ descs,
     const int32_t* __restrict__ pair_count, const int32_t* __restrict__ bin_offset,
     const int32_t* __restrict__ pair_first, const int4* __restrict__ bin_first) {
-  constexpr int kThreads = waves_of<Kv, kStagedW, kTileW>() * 64;
+  constexpr int kThreads = waves_of<Kv, kTileW>() * 64;
   extern __shared__ __attribute__((aligned(16))) float smem[];   // f32x4 rows are stored in it
   __shared__ int ticket_lds;
   __shared__ int arrive_lds[3];   // the merge's arrival flags
@@ -1421,7 +1207,7 @@ __attribute__((amdgpu_waves_per_eu((waves_of<Kv, kStagedW, kTileW>() + 3) / 4,
   };
   int bin = a.grab_counter ? next_bin() : int(blockIdx.x);
   while (bin < a.num_bins) {
-    attend_bin<Kv, kCausal, kStagedW, kNB, kTileW>(a, page_table, descs, pair_count, bin_offset,
+    attend_bin<Kv, kCausal, kNB, kTileW>(a, page_table, descs, pair_count, bin_offset,
                                            bin_first, pair_first, smem, bin);
     const int d_begin = bin_offset[bin], d_end = bin_offset[bin + 1];
     if (a.fuse)
@@ -1461,34 +1247,25 @@ __attribute__((amdgpu_waves_per_eu((waves_of<Kv, kStagedW, kTileW>() + 3) / 4,
 
 }  // namespace
 
-// The instance for a KV format: decode, causal with one, two or three MFMA
-// column tiles per wave (q_len > 1, at most 16, 32 or 48 columns) or staged
-// with staged_w waves; its wave count and, when staged, the bytes of its LDS
-// ring.
+// The instance for a KV format: decode, or causal with 1-4 MFMA column
+// tiles per wave (q_len > 1: at most 16, 32, 48 or 64 columns); its wave
+// count.
 template <class Kv>
-void pick_instance(bool causal, int tiles, int staged_w, const void** fn, int* waves,
-                   size_t* ring) {
-  *ring = 0;
+void pick_instance(bool causal, int tiles, const void** fn, int* waves) {
   *waves = Kv::kWaves;
-  if (staged_w == kStagedWaves) {
-    *fn = reinterpret_cast<const void*>(&attend_kernel<Kv, true, kStagedWaves, 1, 0>);
-  } else if (staged_w == kStagedWaves33To48) {
-    *fn = reinterpret_cast<const void*>(&attend_kernel<Kv, true, kStagedWaves33To48, 1, 0>);
+  if (tiles == 4) {
+    *fn = reinterpret_cast<const void*>(&attend_kernel<Kv, true, 4, kTileWaves>);
+    *waves = waves_of<Kv, kTileWaves>();
   } else if (tiles == 3) {
-    *fn = reinterpret_cast<const void*>(&attend_kernel<Kv, true, 0, 3, kTile3Waves>);
-    *waves = waves_of<Kv, 0, kTile3Waves>();
+    *fn = reinterpret_cast<const void*>(&attend_kernel<Kv, true, 3, kTileWaves>);
+    *waves = waves_of<Kv, kTileWaves>();
   } else if (tiles == 2) {
-    *fn = reinterpret_cast<const void*>(&attend_kernel<Kv, true, 0, 2, kTile2Waves>);
-    *waves = waves_of<Kv, 0, kTile2Waves>();
+    *fn = reinterpret_cast<const void*>(&attend_kernel<Kv, true, 2, Kv::kTile2Waves>);
+    *waves = waves_of<Kv, Kv::kTile2Waves>();
   } else {
-    *fn = causal ? reinterpret_cast<const void*>(&attend_kernel<Kv, true, 0, 1, 0>)
-                 : reinterpret_cast<const void*>(&attend_kernel<Kv, false, 0, 1, 0>);
+    *fn = causal ? reinterpret_cast<const void*>(&attend_kernel<Kv, true, 1, 0>)
+                 : reinterpret_cast<const void*>(&attend_kernel<Kv, false, 1, 0>);
   }
-  if (staged_w > 0) *waves = staged_w;
-  if (staged_w == kStagedWaves)
-    *ring = 2 * size_t(staged_w) * BufImage<StagedOf<Kv, kStagedWaves>>::kBytes;
-  else if (staged_w == kStagedWaves33To48)
-    *ring = 2 * size_t(staged_w) * BufImage<StagedOf<Kv, kStagedWaves33To48>>::kBytes;
 }
 
 hipError_t launch_attend(const AttendArgs& a, AttendKind kind, int grid, hipStream_t s) {
@@ -1501,39 +1278,25 @@ hipError_t launch_attend(const AttendArgs& a, AttendKind kind, int grid, hipStre
   const int4* bf = reinterpret_cast<const int4*>(a.bin_first);
   void* args[] = {&copy, &pt, &descs, &pc, &bo, &pf, &bf};
   // multi-token verification (q_len > 1) runs the instances with the causal
-  // limit: one MFMA column tile per wave up to 16 query columns, two up to
-  // 32, three up to 48, and the staged instance past that; plain decode
-  // keeps the loop without either
+  // limit, one MFMA column tile per wave per 16 query columns; plain decode
+  // keeps the loop without it
   const bool causal = a.q_len > 1;
-  const int max_tiles = LBP_TILE3 ? 3 : 2;
-  const int tiles = !causal || a.ncols > 16 * max_tiles ? 1 : (a.ncols + 15) / 16;
-  const bool staged = causal && a.ncols > 16 * max_tiles;
-  if (!causal && a.ncols > 16) return hipErrorInvalidValue;
-  const int staged_w = !staged ? 0 : a.ncols <= 48 ? kStagedWaves33To48 : kStagedWaves;
+  if (a.ncols < 1 || a.ncols > 64 || (!causal && a.ncols > 16)) return hipErrorInvalidValue;
+  const int tiles = causal ? (a.ncols + 15) / 16 : 1;
   int waves;
   const void* fn;
-  size_t ring;   // the staged instance's LDS ring
   switch (kind) {
     case kAttendFp8:
-      pick_instance<Fp8Kv>(causal, tiles, staged_w, &fn, &waves, &ring);
+      pick_instance<Fp8Kv>(causal, tiles, &fn, &waves);
       break;
     case kAttendFp8Q8:
-      pick_instance<Fp8KvQ8>(causal, tiles, staged_w, &fn, &waves, &ring);
+      pick_instance<Fp8KvQ8>(causal, tiles, &fn, &waves);
       break;
     default:
-      pick_instance<Bf16Kv>(causal, tiles, staged_w, &fn, &waves, &ring);
+      pick_instance<Bf16Kv>(causal, tiles, &fn, &waves);
   }
-  // staged: columns in blocks of at most 16 over an equal share of the
-  // waves each, the fewest blocks that divide the waves
-  int blocks = 1;
-  if (staged) {
-    blocks = (a.ncols + 15) / 16;
-    while (waves % blocks != 0) ++blocks;
-  }
-  copy.col_blocks = blocks;
-  copy.block_cols = (a.ncols + blocks - 1) / blocks;
-  size_t lds = size_t(waves) * (32 * tiles + copy.block_cols * kRedRow) * sizeof(float);
-  if (staged && ring > lds) lds = ring;
+  // per wave for the merge: m and l of 16 tiles columns, then the C rows
+  size_t lds = size_t(waves) * (32 * tiles + size_t(a.ncols) * kRedRow) * sizeof(float);
   const size_t merge_lds = size_t(merge_lds_floats(waves * 64)) * sizeof(float);
   if (a.fuse && merge_lds > lds) lds = merge_lds;
   if (grid <= 0) return hipSuccess;

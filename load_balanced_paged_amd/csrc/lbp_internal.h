@@ -115,8 +115,6 @@ struct AttendArgs {
   int32_t num_bins;
   int32_t batch, num_q_heads, num_kv_heads, group;
   int32_t q_len, ncols;      // query tokens per request; columns = group * q_len
-  int32_t col_blocks;        // column blocks (set by launch_attend); waves split over them
-  int32_t block_cols;        // columns per block, <= 16
   float scale_log2;          // sm_scale * log2(e)
 };
 

@@ -2,8 +2,8 @@
 
 Token j of request r sits at position L_r - q_len + j and attends causally to
 the KV positions up to its own; the MFMA columns hold (token, head) pairs of
-the KV head's group, G * q_len <= 64, in column blocks of at most 16 once
-there are more than 16.  Every case is compared with the fp64
+the KV head's group, G * q_len <= 64, as up to four 16-column MFMA tiles per
+wave.  Every case is compared with the fp64
 oracle (oracle.attention.paged_verify_attention) at the path's tolerance,
 through lbp_attend, lbp_attend_fused and (FP8) lbp_attend_fp8q, including
 tokens with no visible position (zeros) and descriptors in which a column
@@ -82,9 +82,9 @@ def test_verify_shapes_short_requests(gpu_lib, group, hkv, T):
                                          (1, 1, 32), (1, 2, 40), (2, 1, 30), (1, 1, 64)])
 def test_verify_column_blocks(gpu_lib, group, hkv, T):
     """More than 16 query columns (up to 64): two 16-column tiles per wave up
-    to 32, staged column blocks past that (6 waves up to 48, 8 beyond); with
-    one or two heads per group, nearly every column has its own causal
-    limit."""
+    to 32, three up to 48 and four up to 64 (one wave per SIMD, 32-token
+    spans); with one or two heads per group, nearly every column has its own
+    causal limit, and q_len up to 64 puts limits deep into the last spans."""
     wcfg = dataclasses.replace(CONFIGS["tiny"], name=f"vb{group}x{T}", batch=6,
                                num_q_heads=group * hkv, num_kv_heads=hkv)
     case = build_case(wcfg, lengths=[1, 5, 64, 200, 777, 2100], num_workgroups=9, min_tiles=1,
@@ -148,8 +148,8 @@ def test_verify_fp8_kv_and_query(gpu_lib, T):
 
 
 def test_verify_fp8_column_blocks(gpu_lib):
-    """FP8 KV and FP8 query with 48 columns (the staged instance: three
-    blocks of 16 columns over 6 waves)."""
+    """FP8 KV and FP8 query with 48 columns (three column tiles per wave at
+    one wave per SIMD)."""
     wcfg = dataclasses.replace(CONFIGS["fp8"], name="vb-fp8", batch=4)
     case = build_case(wcfg, lengths=[3, 300, 4000, 9000], num_workgroups=20, q_len=6)
     q = make_q(case, 6, seed=8)
@@ -171,7 +171,7 @@ def test_verify_fp8_column_blocks(gpu_lib):
 @pytest.mark.parametrize("T", [2, 6])
 def test_verify_ticket_mode(gpu_lib, T):
     """More bins than CUs: workgroups take bins from the ticket counter, in
-    the causal (T = 2) and staged (T = 6) instances, both merge forms."""
+    the causal (T = 2) and three-tile (T = 6) instances, both merge forms."""
     wcfg = dataclasses.replace(CONFIGS["tiny"], name=f"v-ticket{T}", batch=4)
     case = build_case(wcfg, lengths=[3000, 50, 700, 9000], num_workgroups=1024, min_tiles=1,
                       q_len=T)
@@ -206,7 +206,7 @@ def test_verify_fused_two_levels_blocks(gpu_lib):
 
 
 def test_verify_graph_replay_matches_eager(gpu_lib):
-    """Plan and staged fused verification captured in a HIP graph: every
+    """Plan and three-tile fused verification captured in a HIP graph: every
     replay equals eager, bit for bit."""
     T = 6
     wcfg = dataclasses.replace(CONFIGS["tiny"], name="v-graph", batch=4)
