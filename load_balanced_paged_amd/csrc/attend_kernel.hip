@@ -322,6 +322,11 @@ struct Bf16Kv {
                                                   0, 0, 0);
     return s;
   }
+  // k-step k of the score product (K operand of the step, the query's)
+  __device__ static bf16x8_t k_step(const Buf& b, int k) { return __builtin_bit_cast(bf16x8_t, b.k[k]); }
+  __device__ static f32x4_t score_step(bf16x8_t kop, const Q& q, int k, f32x4_t s) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, q.v[k], s, 0, 0, 0);
+  }
   __device__ static f32x4_t k_scales(const Buf&) { return f32x4_t{1.f, 1.f, 1.f, 1.f}; }
   __device__ static f32x4_t v_scales(const Buf&) { return f32x4_t{1.f, 1.f, 1.f, 1.f}; }
 
@@ -412,6 +417,12 @@ struct Fp8Kv {
                                                   q.v[k], s, 0, 0, 0);
     return s;
   }
+  __device__ static bf16x8_t k_step(const Buf& b, int k) {
+    return __builtin_bit_cast(bf16x8_t, k_bf16(b, k));
+  }
+  __device__ static f32x4_t score_step(bf16x8_t kop, const Q& q, int k, f32x4_t s) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, q.v[k], s, 0, 0, 0);
+  }
   __device__ static f32x4_t k_scales(const Buf& b) { return __builtin_bit_cast(f32x4_t, b.ks); }
   __device__ static f32x4_t v_scales(const Buf& b) { return __builtin_bit_cast(f32x4_t, b.vs); }
 
@@ -474,6 +485,10 @@ struct Fp8KvQ8 : Fp8Kv {
     for (int k = 0; k < 4; ++k)
       s = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(codes8(b.k, k), codes8(q.c, k), s, 0, 0, 0);
     return s;
+  }
+  __device__ static long k_step(const Buf& b, int k) { return codes8(b.k, k); }
+  __device__ static f32x4_t score_step(long kop, const Q& q, int k, f32x4_t s) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(kop, codes8(q.c, k), s, 0, 0, 0);
   }
 };
 
@@ -624,6 +639,21 @@ __device__ inline void consume_tiles(WaveState (&st)[kNB], const typename Kv::Bu
     ks[u] = Kv::k_scales(b[u]);
     vs[u] = Kv::v_scales(b[u]);
   }
+  // the score products with the k-step outermost: each K operand (for FP8
+  // the widened codes) serves the kNB tiles' independent MFMAs at once and
+  // is dead after them
+  f32x4_t scs[kNB][kSub];
+#pragma unroll
+  for (int u = 0; u < kSub; ++u) {
+#pragma unroll
+    for (int t = 0; t < kNB; ++t) scs[t][u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const auto kop = Kv::k_step(b[u], k);
+#pragma unroll
+      for (int t = 0; t < kNB; ++t) scs[t][u] = Kv::score_step(kop, q[t], k, scs[t][u]);
+    }
+  }
   float x[kNB][kSub][4];
   float m_new[kNB];
   bool grew = false;
@@ -632,7 +662,7 @@ __device__ inline void consume_tiles(WaveState (&st)[kNB], const typename Kv::Bu
     float mx = -INFINITY;
 #pragma unroll
     for (int u = 0; u < kSub; ++u) {
-      const f32x4_t sc = Kv::scores(b[u], q[t]);
+      const f32x4_t sc = scs[t][u];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const float v = LBP_TILE_KSFOLD ? sc[j] * (ks[u][j] * scale_log2[t])
@@ -659,11 +689,15 @@ __device__ inline void consume_tiles(WaveState (&st)[kNB], const typename Kv::Bu
     }
   }
   constexpr bool kRoundedSum = Kv::kSplitP;
+  // every tile's P first, then the P.V products with the output block
+  // outermost: each V operand (for FP8 the widened codes) serves the kNB
+  // tiles' independent MFMAs at once and is dead after them
+  i32x2_t pbs[kNB][kSub];
 #pragma unroll
   for (int t = 0; t < kNB; ++t) {
     st[t].m = m_new[t];
     const float ref = kCausal ? finite_or_zero(m_new[t]) : m_new[t];
-    i32x2_t pb2[kSub];
+    i32x2_t (&pb2)[kSub] = pbs[t];
 #pragma unroll
     for (int u = 0; u < kSub; ++u) {
       float p[4];
@@ -680,24 +714,27 @@ __device__ inline void consume_tiles(WaveState (&st)[kNB], const typename Kv::Bu
                     __builtin_bit_cast(float, h23 & 0xFFFF0000u));
       }
     }
-    if constexpr (kSub == 1) {
-      const i16x4_t pb = __builtin_bit_cast(i16x4_t, pb2[0]);
+  }
 #pragma unroll
-      for (int mb = 0; mb < 8; ++mb)
-        st[t].acc[mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(Kv::v_operand(b[0], mb), pb,
-                                                                   st[t].acc[mb], 0, 0, 0);
+  for (int mb = 0; mb < 8; ++mb) {
+    if constexpr (kSub == 1) {
+      const i16x4_t vop = Kv::v_operand(b[0], mb);
+#pragma unroll
+      for (int t = 0; t < kNB; ++t)
+        st[t].acc[mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+            vop, __builtin_bit_cast(i16x4_t, pbs[t][0]), st[t].acc[mb], 0, 0, 0);
     } else {
       // one K = 32 product over both sub-slices: contraction index 8 grp + i
       // is token 4 grp + (i mod 4) of sub-slice i / 4, in P and in V alike
-      const i32x4_t pw = {pb2[0][0], pb2[0][1], pb2[1][0], pb2[1][1]};
-      const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pw);
+      const i32x2_t v0 = __builtin_bit_cast(i32x2_t, Kv::v_operand(b[0], mb));
+      const i32x2_t v1 = __builtin_bit_cast(i32x2_t, Kv::v_operand(b[1], mb));
+      const i32x4_t vw = {v0[0], v0[1], v1[0], v1[1]};
+      const bf16x8_t vop = __builtin_bit_cast(bf16x8_t, vw);
 #pragma unroll
-      for (int mb = 0; mb < 8; ++mb) {
-        const i32x2_t v0 = __builtin_bit_cast(i32x2_t, Kv::v_operand(b[0], mb));
-        const i32x2_t v1 = __builtin_bit_cast(i32x2_t, Kv::v_operand(b[1], mb));
-        const i32x4_t vw = {v0[0], v0[1], v1[0], v1[1]};
-        st[t].acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, vw),
-                                                                pb, st[t].acc[mb], 0, 0, 0);
+      for (int t = 0; t < kNB; ++t) {
+        const i32x4_t pw = {pbs[t][0][0], pbs[t][0][1], pbs[t][1][0], pbs[t][1][1]};
+        st[t].acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, __builtin_bit_cast(bf16x8_t, pw),
+                                                                st[t].acc[mb], 0, 0, 0);
       }
     }
   }
