@@ -79,12 +79,14 @@ def test_verify_shapes_short_requests(gpu_lib, group, hkv, T):
 
 
 @pytest.mark.parametrize("group,hkv,T", [(8, 2, 6), (8, 1, 8), (4, 2, 5), (16, 1, 4), (3, 3, 7),
-                                         (1, 1, 32), (1, 2, 40), (2, 1, 30), (1, 1, 64)])
+                                         (1, 1, 32), (1, 2, 40), (2, 1, 30), (1, 1, 64),
+                                         (1, 1, 17), (11, 1, 3), (7, 2, 7)])
 def test_verify_column_blocks(gpu_lib, group, hkv, T):
     """More than 16 query columns (up to 64): two 16-column tiles per wave up
     to 32, three up to 48 and four up to 64 (one wave per SIMD, 32-token
-    spans); with one or two heads per group, nearly every column has its own
-    causal limit, and q_len up to 64 puts limits deep into the last spans."""
+    spans), each at its lowest column count too (17, 33, 49); with one or two
+    heads per group, nearly every column has its own causal limit, and q_len
+    up to 64 puts limits deep into the last spans."""
     wcfg = dataclasses.replace(CONFIGS["tiny"], name=f"vb{group}x{T}", batch=6,
                                num_q_heads=group * hkv, num_kv_heads=hkv)
     case = build_case(wcfg, lengths=[1, 5, 64, 200, 777, 2100], num_workgroups=9, min_tiles=1,
