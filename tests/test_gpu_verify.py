@@ -149,17 +149,19 @@ def test_verify_fp8_kv_and_query(gpu_lib, T):
     compare_verify(case, out, oracle_verify_pairs(case, 0, pairs, q8), "verify fp8 q")
 
 
-def test_verify_fp8_column_blocks(gpu_lib):
-    """FP8 KV and FP8 query with 48 columns (three column tiles per wave at
-    one wave per SIMD)."""
-    wcfg = dataclasses.replace(CONFIGS["fp8"], name="vb-fp8", batch=4)
-    case = build_case(wcfg, lengths=[3, 300, 4000, 9000], num_workgroups=20, q_len=6)
-    q = make_q(case, 6, seed=8)
+@pytest.mark.parametrize("T", [6, 8])
+def test_verify_fp8_column_blocks(gpu_lib, T):
+    """FP8 KV and FP8 query with 48 and 64 columns (three and four column
+    tiles per wave at one wave per SIMD)."""
+    wcfg = dataclasses.replace(CONFIGS["fp8"], name=f"vb-fp8-{T}", batch=4)
+    case = build_case(wcfg, lengths=[3, 300, 4000, 9000], num_workgroups=20, q_len=T)
+    q = make_q(case, T, seed=8)
     pairs = all_pairs(case)
     compare_verify(case, run(case, q), oracle_verify_pairs(case, 0, pairs, q64_of(q)),
-                   "verify blocks fp8 kv")
+                   f"verify blocks fp8 kv T={T}")
     compare_verify(case, run(case, q, lbp.lbp_attend_fused),
-                   oracle_verify_pairs(case, 0, pairs, q64_of(q)), "verify blocks fp8 kv fused")
+                   oracle_verify_pairs(case, 0, pairs, q64_of(q)),
+                   f"verify blocks fp8 kv fused T={T}")
     codes, scale = quantize_query_e4m3(q)
     lay = case.wl.layers[0]
     out = torch.full_like(q, float("nan"))
@@ -167,7 +169,7 @@ def test_verify_fp8_column_blocks(gpu_lib):
                         lay.v_cache, lay.k_scale, lay.v_scale, case.split_ws, out)
     torch.cuda.synchronize()
     q8 = oracle.e4m3.dequantize(codes.cpu().numpy(), scale.cpu().numpy())
-    compare_verify(case, out, oracle_verify_pairs(case, 0, pairs, q8), "verify blocks fp8 q")
+    compare_verify(case, out, oracle_verify_pairs(case, 0, pairs, q8), f"verify blocks fp8 q T={T}")
 
 
 @pytest.mark.parametrize("T", [2, 6])
