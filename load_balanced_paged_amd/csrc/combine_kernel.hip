@@ -13,10 +13,10 @@
 // with one descriptor is finished in place by the attention kernel, a pair
 // with none is zero-filled there too), and the plan lists them compactly:
 // (pair, first descriptor, count).  A dynamic plan splits at most W - 1 pairs
-// (one per internal bin boundary), so the grid is (min(pairs, W - 1), G)
-// regardless of batch size; workgroup (i, q) merges column q (query token
-// q / G, head q % G) of list entry i, or exits if the plan has fewer
-// entries.  Thread t owns dims
+// (one per internal bin boundary), so the grid is (min(pairs, W - 1), C)
+// regardless of batch size, C = G * q_len query columns; workgroup (i, q)
+// merges column q (query token q / G, head q % G) of list entry i, or exits
+// if the plan has fewer entries.  Thread t owns dims
 // [4(t%32), +4) of partials k = t/32 (mod R), R = threads / 32, and loads
 // each partial's log-sum-exp together with its row, merging online (running
 // max, sum and rescaled accumulator), sixteen partials per thread in flight:
