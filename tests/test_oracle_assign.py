@@ -41,3 +41,20 @@ def test_rejects_bad_arguments():
         oracle.assign.assign_dynamic([-1], 1, 4, 4)
     with pytest.raises(ValueError):
         oracle.assign.assign_static_chunk([1000], 1, 2, 3)
+
+
+def test_descriptors_start_on_page_boundaries():
+    """Every descriptor of every policy begins on a 64-token page boundary.
+    The attention kernel relies on it: its spans of two 16-token slices start
+    at multiples of 32 tokens inside a descriptor, so both slices of a span
+    lie in one page.  (The GPU plans equal these maps bit for bit.)"""
+    rng = np.random.default_rng(5)
+    L = rng.integers(0, 5000, size=40)
+    L[:3] = [0, 1, 64]
+    maps = [oracle.assign.assign_dynamic(L, 3, 37, 1), oracle.assign.assign_dynamic(L, 3, 256, 4),
+            oracle.assign.assign_static_splits(L, 3, 7),
+            oracle.assign.assign_static_chunk(L, 3, 5, int(np.ceil(L.max() / 64)))]
+    for tm in maps:
+        assert tm.D > 0
+        assert np.all(tm.desc[:tm.D, 2] % 64 == 0)
+        assert np.all(tm.desc[:tm.D, 3] > tm.desc[:tm.D, 2])
