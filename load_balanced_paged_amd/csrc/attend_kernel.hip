@@ -964,10 +964,20 @@ __device__ inline void attend_bin(const AttendArgs& a, const int32_t* __restrict
     constexpr int kD4 = kHeadDim / 4;
     for (int idx = threadIdx.x; idx < C * kD4; idx += kThreads) {
       const int q = idx / kD4, d4 = idx % kD4;
-      const float* rb = smem;   // every wave's state of column q
+      // every wave's state of column q, all loads issued before the first
+      // use (one LDS round trip instead of one per wave)
+      float mw[kWaves], lw[kWaves];
+      f32x4_t ow[kWaves];
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float* rw = smem + w * red_stride;
+        mw[w] = rw[q];
+        lw[w] = rw[16 * kNB + q];
+        ow[w] = *reinterpret_cast<const f32x4_t*>(rw + kRedHead + q * kRedRow + 4 * d4);
+      }
       float M = -INFINITY;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, rb[w * red_stride + q]);
+      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, mw[w]);
       // a column with no visible token in this descriptor (possible only
       // under a causal limit) gives an empty partial: o = 0, lse = -inf
       const float Mu = kCausal ? finite_or_zero(M) : M;
@@ -975,13 +985,14 @@ __device__ inline void attend_bin(const AttendArgs& a, const int32_t* __restrict
       f32x4_t o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) {
-        const float* rw = rb + w * red_stride;
-        const float c = __builtin_amdgcn_exp2f(rw[q] - Mu);
-        L += rw[16 * kNB + q] * c;
-        o += *reinterpret_cast<const f32x4_t*>(rw + kRedHead + q * kRedRow + 4 * d4) * c;
+        const float c = __builtin_amdgcn_exp2f(mw[w] - Mu);
+        L += lw[w] * c;
+        o += ow[w] * c;
       }
       const bool empty = kCausal && !(L > 0.f);
-      const f32x4_t on = empty ? f32x4_t{0.f, 0.f, 0.f, 0.f} : o / L;
+      // one division for the four dims (each then one rounding more than a
+      // division per dim: far inside the partials' float tolerance)
+      const f32x4_t on = empty ? f32x4_t{0.f, 0.f, 0.f, 0.f} : o * (1.f / L);
       if (single) {
         // the pair's only descriptor: this is already the final output
         const int64_t row = kCausal ? query_row(r, g, q, a.q_len, G, a.num_q_heads)
