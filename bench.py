@@ -94,7 +94,7 @@ class Bench:
             f"{self.wl.kv_bytes / 1e9:.3f} GB KV/layer in {time.time() - t0:.1f}s")
         self.cfg = lbp.make_config(self.wcfg.num_q_heads, self.wcfg.num_kv_heads, self.wcfg.batch,
                                    self.wl.page_table.shape[1], kv_dtype=self.wcfg.kv_dtype,
-                                   num_workgroups=0, min_tiles_per_bin=4,
+                                   num_workgroups=0, min_tiles_per_bin=0,
                                    sm_scale=self.wcfg.sm_scale)
         self.seq = torch.from_numpy(np.asarray(self.wl.lengths, dtype=np.int32)).cuda()
         self.table = torch.from_numpy(self.wl.page_table).cuda()
@@ -135,7 +135,7 @@ class Bench:
             lbp, w = self.lbp, self.wcfg
             cfg = lbp.make_config(w.num_q_heads, w.num_kv_heads, w.batch,
                                   self.wl.page_table.shape[1], kv_dtype=w.kv_dtype,
-                                  num_workgroups=0, min_tiles_per_bin=4, sm_scale=w.sm_scale,
+                                  num_workgroups=0, min_tiles_per_bin=0, sm_scale=w.sm_scale,
                                   q_len=q_len)
             pb, sb = lbp.lbp_query_workspace(cfg)
             plan_ws = torch.empty(pb, dtype=torch.uint8, device="cuda")
@@ -620,7 +620,10 @@ def bench_table3(lbp, args):
             static[S] = sms * 1e3
         best = min(static, key=static.get)
         # the minimum-work floor F (tiles per bin) of the dynamic plan; the
-        # default is 4, which binds only while T <= 3 W
+        # library's default is 1 (no floor), and F binds only while
+        # T <= (F - 1) W.  The default plan runs again first, so that no F is
+        # timed straight after the static sweep's slowest plans.
+        b.warm(0.05)
         by_f = {}
         for F in (1, 2, 4):
             fms_f, _ = b.time_steps(min(args.steps, 50), 2, lbp.LBP_POLICY_DYNAMIC, F,
@@ -706,7 +709,7 @@ def main():
             "num_kv_heads": wcfg.num_kv_heads, "head_dim": 128, "page_size": 64,
             "layers": head["layers"], "total_tokens": head["total_tokens"],
             "kv_bytes_per_layer": head["kv_bytes_per_layer"], "workgroups": head["workgroups"],
-            "min_tiles_per_bin": 4, "timing": head["timing"],
+            "min_tiles_per_bin": 1, "timing": head["timing"],
         },
         "roofline": head["roofline"],
         "plan_us": head["plan_us"],

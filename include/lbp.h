@@ -100,7 +100,9 @@ typedef struct lbp_config {
   int32_t max_pages_per_seq; /* page-table row capacity; lengths above
                                 64 * max_pages_per_seq are clamped and flagged */
   int32_t num_workgroups;    /* W, persistent workgroups (bins); 0 = one per CU */
-  int32_t min_tiles_per_bin; /* F, the minimum-work floor in tiles; 0 = 4 */
+  int32_t min_tiles_per_bin; /* F, the minimum-work floor in tiles; 0 = 1,
+                                i.e. no floor (measured fastest on small
+                                batches, where a floor cuts parallelism) */
   int32_t kv_dtype;          /* lbp_kv_dtype */
   float sm_scale;            /* softmax scale, > 0 (1/sqrt(128) typically) */
   int32_t q_len;             /* query tokens per request per step (0 = 1): > 1 for

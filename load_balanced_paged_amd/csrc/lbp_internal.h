@@ -11,7 +11,11 @@ namespace lbp {
 constexpr int kHeadDim = LBP_HEAD_DIM;   // 128
 constexpr int kPageTokens = LBP_PAGE_SIZE;  // 64: one page is one scheduling tile
 constexpr int kMaxGroup = LBP_MAX_GROUP;    // query heads per KV head, padded to 16 MFMA rows
-constexpr int kDefaultMinTiles = 4;         // F, the minimum-work floor (tiles per bin)
+// F, the minimum-work floor (tiles per bin) when the config leaves it 0: 1,
+// no floor.  A small batch's attention is latency-bound here and the combine
+// is one launch of at most W - 1 pairs whatever the split count, so fewer,
+// larger bins measured slower (up to 1.5 us on a one-request batch).
+constexpr int kDefaultMinTiles = 1;
 
 // header word indices inside the plan workspace
 enum HeaderWord {

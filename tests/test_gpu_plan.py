@@ -47,16 +47,19 @@ def check(got, ref):
         assert np.array_equal(got["bin_first"][b], want), b
 
 
+@pytest.mark.parametrize("F", [0, 4])
 @pytest.mark.parametrize("name", list(CONFIGS))
-def test_workload_taskmap_bitexact(gpu_lib, name):
-    """The five workloads' maps, at the benchmark's launch shape (one bin per CU, F = 4)."""
+def test_workload_taskmap_bitexact(gpu_lib, name, F):
+    """The five workloads' maps at the benchmark's launch shape (one bin per
+    CU): with the library's default floor (F = 0 in the config, which means
+    F = 1, no floor) and with F = 4."""
     import oracle
     wcfg = CONFIGS[name]
     from workloads import draw_lengths
     L = draw_lengths(wcfg, np.random.default_rng(wcfg.seed))
-    say(f"[plan] {name}")
-    got, info, _ = plan_only(wcfg, L, wcfg.num_kv_heads, 0, 4)
-    ref = oracle.assign.assign_dynamic(L, wcfg.num_kv_heads, info.num_bins, 4)
+    say(f"[plan] {name} F={F}")
+    got, info, _ = plan_only(wcfg, L, wcfg.num_kv_heads, 0, F)
+    ref = oracle.assign.assign_dynamic(L, wcfg.num_kv_heads, info.num_bins, F if F > 0 else 1)
     check(got, ref)
     say(f"[plan] {name}: W={info.num_bins} T={ref.T} budget={ref.budget} D={ref.D} U={ref.U}")
 
