@@ -772,7 +772,7 @@ using SpanBuf = std::conditional_t<kSub == 1, typename Kv::Buf, SpanOf<Kv, kSub>
 // it loads, so every KV byte is still fetched once per workgroup).  kTileW:
 // the tile form's wave count (0: the format's own).  With one wave per SIMD
 // the register file has room for 32-token spans (two slices per step).
-template <class Kv, bool kCausal, int kNB, int kTileW>
+template <class Kv, bool kCausal, int kNB, int kTileW, bool kFuse>
 __device__ inline void attend_bin(const AttendArgs& a, const int32_t* __restrict__ pt,
                                   const int4* __restrict__ descs,
                                   const int32_t* __restrict__ pair_count,
@@ -1002,7 +1002,7 @@ __device__ inline void attend_bin(const AttendArgs& a, const int32_t* __restrict
         float* po = a.o_part + (int64_t(d) * C + q) * kHeadDim + 4 * d4;
         float* pl = a.lse_part + int64_t(d) * C + q;
         const float lse = empty ? -INFINITY : M + __builtin_amdgcn_logf(L);
-        if (a.fuse) {
+        if constexpr (kFuse) {
           // merged inside this launch, possibly by a workgroup on another XCD
           const SplitRsrc sr = split_rsrc(a);
           store_row_coherent(sr, int64_t(d) * C + q, d4, on);
@@ -1223,13 +1223,18 @@ __device__ void finish_split_pairs(const AttendArgs& a, const int4* __restrict__
 // on a faster CU simply drains more bins; every workgroup draws exactly one
 // ticket past the last bin, and the one holding the final ticket returns the
 // counter to zero for the next launch.
+// kFuse: the instance of the single-launch form, which merges split pairs
+// itself (finish_split_pairs); the other instances leave the merge to the
+// combine kernel and carry none of its code (about 2400 of the decode
+// kernel's 4100 instructions, which measurably lengthen every launch
+// although they never run there).
 // One workgroup runs per CU (persistent bins), so more waves per SIMD than
 // its own (waves / 4, rounded up) can never be resident.  Saying so pins the
 // compiler's occupancy target: otherwise its scheduler squeezes the slice
 // loop's registers toward occupancies that never occur, and whenever that
 // loop is the kernel's register peak it stops issuing the next slice ahead
 // of the current slice's math.
-template <class Kv, bool kCausal, int kNB, int kTileW>
+template <class Kv, bool kCausal, int kNB, int kTileW, bool kFuse>
 __global__ __launch_bounds__((waves_of<Kv, kTileW>() * 64))
 __attribute__((amdgpu_waves_per_eu((waves_of<Kv, kTileW>() + 3) / 4,
                                    (waves_of<Kv, kTileW>() + 3) / 4))) void attend_kernel(
@@ -1255,10 +1260,10 @@ __attribute__((amdgpu_waves_per_eu((waves_of<Kv, kTileW>() + 3) / 4,
   };
   int bin = a.grab_counter ? next_bin() : int(blockIdx.x);
   while (bin < a.num_bins) {
-    attend_bin<Kv, kCausal, kNB, kTileW>(a, page_table, descs, pair_count, bin_offset,
+    attend_bin<Kv, kCausal, kNB, kTileW, kFuse>(a, page_table, descs, pair_count, bin_offset,
                                            bin_first, pair_first, smem, bin);
     const int d_begin = bin_offset[bin], d_end = bin_offset[bin + 1];
-    if (a.fuse)
+    if constexpr (kFuse)
       finish_split_pairs<kThreads>(a, descs, pair_count, pair_first, smem, arrive_lds, d_begin,
                                    d_end);
     drained += d_end - d_begin;
@@ -1296,24 +1301,31 @@ __attribute__((amdgpu_waves_per_eu((waves_of<Kv, kTileW>() + 3) / 4,
 }  // namespace
 
 // The instance for a KV format: decode, or causal with 1-4 MFMA column
-// tiles per wave (q_len > 1: at most 16, 32, 48 or 64 columns); its wave
-// count.
-template <class Kv>
+// tiles per wave (q_len > 1: at most 16, 32, 48 or 64 columns), with or
+// without the in-kernel merge; its wave count.
+template <class Kv, bool kFuse>
 void pick_instance(bool causal, int tiles, const void** fn, int* waves) {
   *waves = Kv::kWaves;
   if (tiles == 4) {
-    *fn = reinterpret_cast<const void*>(&attend_kernel<Kv, true, 4, kTileWaves>);
+    *fn = reinterpret_cast<const void*>(&attend_kernel<Kv, true, 4, kTileWaves, kFuse>);
     *waves = waves_of<Kv, kTileWaves>();
   } else if (tiles == 3) {
-    *fn = reinterpret_cast<const void*>(&attend_kernel<Kv, true, 3, kTileWaves>);
+    *fn = reinterpret_cast<const void*>(&attend_kernel<Kv, true, 3, kTileWaves, kFuse>);
     *waves = waves_of<Kv, kTileWaves>();
   } else if (tiles == 2) {
-    *fn = reinterpret_cast<const void*>(&attend_kernel<Kv, true, 2, Kv::kTile2Waves>);
+    *fn = reinterpret_cast<const void*>(&attend_kernel<Kv, true, 2, Kv::kTile2Waves, kFuse>);
     *waves = waves_of<Kv, Kv::kTile2Waves>();
   } else {
-    *fn = causal ? reinterpret_cast<const void*>(&attend_kernel<Kv, true, 1, 0>)
-                 : reinterpret_cast<const void*>(&attend_kernel<Kv, false, 1, 0>);
+    *fn = causal ? reinterpret_cast<const void*>(&attend_kernel<Kv, true, 1, 0, kFuse>)
+                 : reinterpret_cast<const void*>(&attend_kernel<Kv, false, 1, 0, kFuse>);
   }
+}
+template <class Kv>
+void pick_instance(bool causal, int tiles, bool fuse, const void** fn, int* waves) {
+  if (fuse)
+    pick_instance<Kv, true>(causal, tiles, fn, waves);
+  else
+    pick_instance<Kv, false>(causal, tiles, fn, waves);
 }
 
 hipError_t launch_attend(const AttendArgs& a, AttendKind kind, int grid, hipStream_t s) {
@@ -1335,13 +1347,13 @@ hipError_t launch_attend(const AttendArgs& a, AttendKind kind, int grid, hipStre
   const void* fn;
   switch (kind) {
     case kAttendFp8:
-      pick_instance<Fp8Kv>(causal, tiles, &fn, &waves);
+      pick_instance<Fp8Kv>(causal, tiles, a.fuse != 0, &fn, &waves);
       break;
     case kAttendFp8Q8:
-      pick_instance<Fp8KvQ8>(causal, tiles, &fn, &waves);
+      pick_instance<Fp8KvQ8>(causal, tiles, a.fuse != 0, &fn, &waves);
       break;
     default:
-      pick_instance<Bf16Kv>(causal, tiles, &fn, &waves);
+      pick_instance<Bf16Kv>(causal, tiles, a.fuse != 0, &fn, &waves);
   }
   // per wave for the merge: m and l of 16 tiles columns, then the C rows
   size_t lds = size_t(waves) * (32 * tiles + size_t(a.ncols) * kRedRow) * sizeof(float);
