@@ -53,7 +53,7 @@ class Case:
 
 
 def build_case(wcfg: WorkloadConfig, layers: int = 1, lengths: Optional[Sequence[int]] = None,
-               num_workgroups: int = 0, min_tiles: int = 4, poison: bool = True,
+               num_workgroups: int = 0, min_tiles: int = 0, poison: bool = True,
                policy: int = lbp.LBP_POLICY_DYNAMIC, param: int = 0,
                max_pages_per_seq: Optional[int] = None, q_len: int = 1) -> Case:
     say(f"[case] {wcfg.name} B={wcfg.batch if lengths is None else len(lengths)} "

@@ -20,11 +20,14 @@ from workloads import TABLE3
 pytestmark = pytest.mark.gpu
 
 
+@pytest.mark.parametrize("F", [0, 4])
 @pytest.mark.parametrize("mix", list(TABLE3))
-def test_table3_mix_dynamic(gpu_lib, mix):
-    case = build_case(TABLE3[mix])
+def test_table3_mix_dynamic(gpu_lib, mix, F):
+    """The benchmark's plan (the library's default floor, F = 0 in the
+    config: no floor) and the plan with F = 4, which binds on 64x0.5K."""
+    case = build_case(TABLE3[mix], min_tiles=F)
     got, ref = assert_taskmap_matches(case)
-    say(f"[table3] {mix}: T={ref.T} budget={ref.budget} D={ref.D} U={ref.U} "
+    say(f"[table3] {mix} F={F}: T={ref.T} budget={ref.budget} D={ref.D} U={ref.U} "
         f"max splits={int(ref.pair_count.max())}")
     ref_rows = oracle_pairs(case, 0, all_pairs(case))
     lay = case.wl.layers[0]
