@@ -757,6 +757,102 @@ struct SpanOf {
 template <class Kv, int kSub>
 using SpanBuf = std::conditional_t<kSub == 1, typename Kv::Buf, SpanOf<Kv, kSub>>;
 
+// Drains a bin of many short descriptors, one descriptor per wave.
+//
+// attend_bin ends every descriptor with a merge of all waves' states through
+// LDS between two workgroup barriers, and the next descriptor's first loads
+// wait for this one's last: about 1.1 us per boundary, more than a 64-token
+// tile of streaming.  Where short requests pile up (the plan fills bins in
+// request order, so a bin can hold many pairs of one or two tiles) the
+// boundaries dominate.  Here wave w instead takes the bin's descriptors
+// w, w + W, ... and drains each one alone, its 16-token slices in order
+// with two in flight, then writes its result straight from its registers:
+// the normalised row of a pair with one descriptor, else the partial row and
+// its log-sum-exp for the combine kernel.  No LDS, no barrier, and the waves'
+// descriptor chains overlap.  Decode only (one column tile, no causal
+// limit, no in-kernel merge).
+template <class Kv>
+__device__ inline void drain_waves(const AttendArgs& a, const int32_t* __restrict__ pt,
+                                   const int4* __restrict__ descs,
+                                   const int32_t* __restrict__ pair_count, int d_begin, int d_end,
+                                   int wave, int lane) {
+  constexpr int kWaves = Kv::kWaves;
+  int d = d_begin + wave;
+  if (d >= d_end) return;
+  const int n = lane & 15, grp = lane >> 4;
+  const int C = a.ncols;   // = G: one query token
+  const QLane ql = q_lane<false>(a, n, 0, C);
+  int4 ds = descs[d];
+  typename Kv::Q qb;
+  typename Kv::Buf buf[2];
+  Kv::load_q(qb, a, ql, ds.x, ds.y, grp);
+  Kv::issue(buf[0], slice_rsrc<Kv>(a, pt, ds.x, ds.y, ds.z, ds.w), lane);
+  for (; d < d_end; d += kWaves) {
+    const int g = ds.x, r = ds.y, t_end = ds.w;
+    const bool single = pair_count[g * a.batch + r] == 1;
+    const bool has_next = d + kWaves < d_end;
+    const int4 dn = descs[has_next ? d + kWaves : d];
+    const int next_page = page_of(a, pt, dn.y, dn.z, dn.w);
+    WaveState st;
+    st.m = -INFINITY;
+    st.l = 0.f;
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) st.acc[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    // the descriptor's ns >= 1 slices, the first in (or loading into)
+    // buf[0]; as in attend_bin, a slice with a successor issues it before
+    // its own math, and one code path computes every last slice
+    int tok = ds.z;
+    const int ns = wave_slices(tok, t_end, kSlice);
+    const float sc = Kv::score_scale(qb, a.scale_log2);
+    auto step_on = [&](const typename Kv::Buf& cur, typename Kv::Buf& nxt) {
+      Kv::issue(nxt, slice_rsrc<Kv>(a, pt, g, r, tok + kSlice, t_end), lane);
+      Kv::after_loads(qb);
+      consume<Kv, false>(st, cur, qb, tok, t_end, sc, grp, INT_MAX);
+      tok += kSlice;
+    };
+    for (int i = (ns - 1) >> 1; i > 0; --i) {
+      step_on(buf[0], buf[1]);
+      step_on(buf[1], buf[0]);
+    }
+    if ((ns & 1) == 0) {
+      step_on(buf[0], buf[1]);
+      buf[0] = buf[1];
+    }
+    consume<Kv, false>(st, buf[0], qb, tok, t_end, sc, grp, INT_MAX);
+    // this wave's next descriptor: query and first slice, before the stores
+    if (has_next) {
+      Kv::load_q(qb, a, ql, dn.x, dn.y, grp);
+      Kv::issue(buf[0], slice_rsrc_at<Kv>(a, dn.x, dn.z, dn.w, next_page), lane);
+    }
+    // lane (grp, n) holds dims 32 grp + 8 j + mb of column n: per j, the
+    // float4s 8 grp + 2 j (mb 0-3) and 8 grp + 2 j + 1 (mb 4-7)
+    const float L = wave_sum_across_groups(st.l);
+    const float inv = 1.f / L;
+    if (n < C) {
+      auto half = [&](int j, int h) {
+        return f32x4_t{st.acc[4 * h][j], st.acc[4 * h + 1][j], st.acc[4 * h + 2][j],
+                       st.acc[4 * h + 3][j]} * inv;
+      };
+      if (single) {
+        const int64_t row = int64_t(r) * a.num_q_heads + int64_t(g) * C + n;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) store_bf16x4(a.out, row, 8 * grp + 2 * j + h, half(j, h));
+      } else {
+        const int64_t e = int64_t(d) * C + n;
+        f32x4_t* po = reinterpret_cast<f32x4_t*>(a.o_part + e * kHeadDim) + 8 * grp;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) po[2 * j + h] = half(j, h);
+        if (grp == 0) a.lse_part[e] = st.m + __builtin_amdgcn_logf(L);
+      }
+    }
+    ds = dn;
+  }
+}
+
 // Drains one bin: every descriptor in it, in order.
 //
 // Slice i of a descriptor goes to wave i % kWaves; each wave keeps two
@@ -772,7 +868,7 @@ using SpanBuf = std::conditional_t<kSub == 1, typename Kv::Buf, SpanOf<Kv, kSub>
 // it loads, so every KV byte is still fetched once per workgroup).  kTileW:
 // the tile form's wave count (0: the format's own).  With one wave per SIMD
 // the register file has room for 32-token spans (two slices per step).
-template <class Kv, bool kCausal, int kNB, int kTileW, bool kFuse>
+template <class Kv, bool kCausal, int kNB, int kTileW, bool kFuse, bool kWave>
 __device__ inline void attend_bin(const AttendArgs& a, const int32_t* __restrict__ pt,
                                   const int4* __restrict__ descs,
                                   const int32_t* __restrict__ pair_count,
@@ -809,6 +905,16 @@ __device__ inline void attend_bin(const AttendArgs& a, const int32_t* __restrict
   int4 ds = bin_first[bin];
   asm volatile("" ::"s"(ds.x), "s"(ds.y), "s"(ds.z), "s"(ds.w));   // keep the load above the exit
   if (d_begin >= d_end) return;
+  if constexpr (kWave) {
+    // at least three descriptors of at most two tiles on average (every
+    // bin but the last holds exactly `budget` tiles, the last fewer): one
+    // descriptor per wave
+    const int budget = bin_offset[kHdrBudget - kHdrWords];
+    if (d_end - d_begin >= 3 && budget <= 2 * (d_end - d_begin)) {
+      drain_waves<Kv>(a, pt, descs, pair_count, d_begin, d_end, wave, lane);
+      return;
+    }
+  }
 
   QLane ql[kNB];
   typename Kv::Q qb[kNB];
@@ -1223,6 +1329,10 @@ __device__ void finish_split_pairs(const AttendArgs& a, const int4* __restrict__
 // on a faster CU simply drains more bins; every workgroup draws exactly one
 // ticket past the last bin, and the one holding the final ticket returns the
 // counter to zero for the next launch.
+// kWave: the decode instance that drains bins of many short descriptors one
+// descriptor per wave (drain_waves); the host launches it only for batches
+// of at least two (KV head, request) pairs per bin, since its code costs
+// every other short launch about 0.4 us although it never runs there.
 // kFuse: the instance of the single-launch form, which merges split pairs
 // itself (finish_split_pairs); the other instances leave the merge to the
 // combine kernel and carry none of its code (about 2400 of the decode
@@ -1234,7 +1344,7 @@ __device__ void finish_split_pairs(const AttendArgs& a, const int4* __restrict__
 // loop's registers toward occupancies that never occur, and whenever that
 // loop is the kernel's register peak it stops issuing the next slice ahead
 // of the current slice's math.
-template <class Kv, bool kCausal, int kNB, int kTileW, bool kFuse>
+template <class Kv, bool kCausal, int kNB, int kTileW, bool kFuse, bool kWave = false>
 __global__ __launch_bounds__((waves_of<Kv, kTileW>() * 64))
 __attribute__((amdgpu_waves_per_eu((waves_of<Kv, kTileW>() + 3) / 4,
                                    (waves_of<Kv, kTileW>() + 3) / 4))) void attend_kernel(
@@ -1260,7 +1370,7 @@ __attribute__((amdgpu_waves_per_eu((waves_of<Kv, kTileW>() + 3) / 4,
   };
   int bin = a.grab_counter ? next_bin() : int(blockIdx.x);
   while (bin < a.num_bins) {
-    attend_bin<Kv, kCausal, kNB, kTileW, kFuse>(a, page_table, descs, pair_count, bin_offset,
+    attend_bin<Kv, kCausal, kNB, kTileW, kFuse, kWave>(a, page_table, descs, pair_count, bin_offset,
                                            bin_first, pair_first, smem, bin);
     const int d_begin = bin_offset[bin], d_end = bin_offset[bin + 1];
     if constexpr (kFuse)
@@ -1303,7 +1413,7 @@ __attribute__((amdgpu_waves_per_eu((waves_of<Kv, kTileW>() + 3) / 4,
 // The instance for a KV format: decode, or causal with 1-4 MFMA column
 // tiles per wave (q_len > 1: at most 16, 32, 48 or 64 columns), with or
 // without the in-kernel merge; its wave count.
-template <class Kv, bool kFuse>
+template <class Kv, bool kFuse, bool kWave>
 void pick_instance(bool causal, int tiles, const void** fn, int* waves) {
   *waves = Kv::kWaves;
   if (tiles == 4) {
@@ -1317,15 +1427,17 @@ void pick_instance(bool causal, int tiles, const void** fn, int* waves) {
     *waves = waves_of<Kv, Kv::kTile2Waves>();
   } else {
     *fn = causal ? reinterpret_cast<const void*>(&attend_kernel<Kv, true, 1, 0, kFuse>)
-                 : reinterpret_cast<const void*>(&attend_kernel<Kv, false, 1, 0, kFuse>);
+                 : reinterpret_cast<const void*>(&attend_kernel<Kv, false, 1, 0, kFuse, kWave>);
   }
 }
 template <class Kv>
-void pick_instance(bool causal, int tiles, bool fuse, const void** fn, int* waves) {
+void pick_instance(bool causal, int tiles, bool fuse, bool wave, const void** fn, int* waves) {
   if (fuse)
-    pick_instance<Kv, true>(causal, tiles, fn, waves);
+    pick_instance<Kv, true, false>(causal, tiles, fn, waves);
+  else if (wave)
+    pick_instance<Kv, false, true>(causal, tiles, fn, waves);
   else
-    pick_instance<Kv, false>(causal, tiles, fn, waves);
+    pick_instance<Kv, false, false>(causal, tiles, fn, waves);
 }
 
 hipError_t launch_attend(const AttendArgs& a, AttendKind kind, int grid, hipStream_t s) {
@@ -1343,17 +1455,20 @@ hipError_t launch_attend(const AttendArgs& a, AttendKind kind, int grid, hipStre
   const bool causal = a.q_len > 1;
   if (a.ncols < 1 || a.ncols > 64 || (!causal && a.ncols > 16)) return hipErrorInvalidValue;
   const int tiles = causal ? (a.ncols + 15) / 16 : 1;
+  // decode bins can fill with short descriptors only where there are
+  // several pairs per bin
+  const bool wave = !causal && int64_t(a.batch) * a.num_kv_heads >= 2 * int64_t(a.num_bins);
   int waves;
   const void* fn;
   switch (kind) {
     case kAttendFp8:
-      pick_instance<Fp8Kv>(causal, tiles, a.fuse != 0, &fn, &waves);
+      pick_instance<Fp8Kv>(causal, tiles, a.fuse != 0, wave, &fn, &waves);
       break;
     case kAttendFp8Q8:
-      pick_instance<Fp8KvQ8>(causal, tiles, a.fuse != 0, &fn, &waves);
+      pick_instance<Fp8KvQ8>(causal, tiles, a.fuse != 0, wave, &fn, &waves);
       break;
     default:
-      pick_instance<Bf16Kv>(causal, tiles, a.fuse != 0, &fn, &waves);
+      pick_instance<Bf16Kv>(causal, tiles, a.fuse != 0, wave, &fn, &waves);
   }
   // per wave for the merge: m and l of 16 tiles columns, then the C rows
   size_t lds = size_t(waves) * (32 * tiles + size_t(a.ncols) * kRedRow) * sizeof(float);

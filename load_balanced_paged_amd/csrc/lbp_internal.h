@@ -44,6 +44,10 @@ inline int arrive_words(int policy, int max_desc) {
 }
 
 // Byte layout of the task map for one plan.
+// The header words directly precede the bin offsets in every plan workspace
+// (below), so a kernel holding bin_offset reads header word i at
+// bin_offset[i - kHdrWords].
+static_assert(kHdrWords * 4 % 64 == 0, "the bin offsets follow the header directly");
 inline lbp_plan_offsets plan_layout(int policy, int num_bins, int max_desc, int npairs) {
   lbp_plan_offsets o;
   o.header = 0;

@@ -1,13 +1,15 @@
 """GPU parity of bins holding many short descriptors.
 
 Where short requests pile up, one bin holds many descriptors of one or two
-64-token tiles, so the attention kernel crosses a descriptor boundary (the
-merge of every wave's state, the next descriptor's first loads) every few
-slices, and most waves hold one slice or none of a descriptor.  These cases
-make bins of at least three descriptors averaging at most two tiles, up to
-about twenty per bin (more descriptors than waves), with pairs finished in
-place and pairs split across bins, in every KV format and entry point, and
-check every output row against the oracle.
+64-token tiles.  For decode batches of at least two (KV head, request)
+pairs per bin, lbp_attend and lbp_attend_fp8q launch the instance that
+drains such a bin (at least three descriptors averaging at most two tiles)
+one descriptor per wave and writes each result from the wave's registers;
+other bins of that launch, and every bin of the single-launch form, go
+through the per-descriptor loop with its merge across waves.  These cases
+make such bins, up to about twenty descriptors each (more than the waves),
+with pairs finished in place and pairs split across bins, in every KV
+format and entry point, and check every output row against the oracle.
 """
 
 import dataclasses
@@ -96,3 +98,20 @@ def test_short_descriptor_bins(gpu_lib, name, kv, entry, hq, hkv, batch, hi, W, 
     assert nbins >= 2 and nsplit >= 1
     out, q64 = run(case, entry)
     compare(case, out, oracle_pairs(case, 0, all_pairs(case), q64), f"short {name}")
+
+
+def test_short_and_long_bins_in_one_launch(gpu_lib):
+    """Forty short requests, then eight of 512 tokens: the same launch
+    drains the bins of the short ones one descriptor per wave and the bins
+    of the long ones descriptor by descriptor."""
+    lengths = short_lengths(40, 128, 3) + [512] * 8
+    wcfg = dataclasses.replace(CONFIGS["tiny"], name="short-long", batch=len(lengths),
+                               num_q_heads=16, num_kv_heads=2)
+    case = build_case(wcfg, lengths=lengths, num_workgroups=32, min_tiles=1)
+    assert wcfg.num_kv_heads * len(lengths) >= 2 * case.info.num_bins   # the per-wave instance
+    nbins, nsplit = short_bins(case)
+    used = int(lbp.read_taskmap(case.plan_ws, case.info)["header"][3])
+    say(f"[short] short and long: {nbins} of {used} bins of short descriptors, {nsplit} split")
+    assert 2 <= nbins <= used - 2 and nsplit >= 1
+    out, q64 = run(case, "attend")
+    compare(case, out, oracle_pairs(case, 0, all_pairs(case), q64), "short and long")
