@@ -78,6 +78,8 @@ CASES = [
     ("bf16 fused W=4", "bf16", "fused", 16, 2, 40, 96, 4, 7),
     ("bf16 group 3", "bf16", "attend", 9, 3, 30, 128, 16, 9),
     ("bf16 group 16", "bf16", "fused", 16, 1, 60, 128, 12, 4),
+    ("bf16 group 16 attend", "bf16", "attend", 16, 1, 60, 128, 12, 5),
+    ("bf16 group 1", "bf16", "attend", 4, 4, 24, 128, 16, 1),
     ("fp8 attend", "fp8_e4m3", "attend", 16, 2, 48, 160, 24, 5),
     ("fp8 fused W=4", "fp8_e4m3", "fused", 16, 2, 40, 96, 4, 8),
     ("fp8 fp8q", "fp8_e4m3", "fp8q", 16, 2, 48, 160, 24, 6),
