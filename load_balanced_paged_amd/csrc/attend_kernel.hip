@@ -36,6 +36,9 @@
 //    slice of a descriptor issues nothing.  BF16 runs 8 waves per
 //    workgroup, FP8 6: with both slices really in flight, more FP8 waves
 //    only added merge work per descriptor and register pressure.
+//  * Batches of at least two (KV head, request) pairs per bin run an
+//    instance that drains a bin of many short descriptors one descriptor
+//    per wave, with no merge across waves (drain_waves).
 //  * A pair served by a single descriptor is finished in place: its
 //    normalised output goes straight to `out` in BF16, and a pair without
 //    tokens gets zero rows here too.  Only pairs split over several bins use
