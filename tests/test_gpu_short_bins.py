@@ -117,3 +117,22 @@ def test_short_and_long_bins_in_one_launch(gpu_lib):
     assert 2 <= nbins <= used - 2 and nsplit >= 1
     out, q64 = run(case, "attend")
     compare(case, out, oracle_pairs(case, 0, all_pairs(case), q64), "short and long")
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3"])
+def test_large_batch_of_short_requests(gpu_lib, kv):
+    """1024 requests of 1-128 tokens at 64 query / 8 KV heads (8192 pairs,
+    32 per bin at one bin per CU): the launch shape of the benchmark, every
+    row against the oracle."""
+    base = CONFIGS["uniform"] if kv == "bf16" else CONFIGS["fp8"]
+    rng = np.random.default_rng(31)
+    lengths = [int(x) for x in rng.integers(1, 129, size=1024)]
+    wcfg = dataclasses.replace(base, name=f"short-large-{kv}", batch=len(lengths))
+    case = build_case(wcfg, lengths=lengths)
+    assert wcfg.num_kv_heads * len(lengths) >= 2 * case.info.num_bins   # the per-wave instance
+    nbins, nsplit = short_bins(case)
+    used = int(lbp.read_taskmap(case.plan_ws, case.info)["header"][3])
+    say(f"[short] large {kv}: {nbins} of {used} bins of short descriptors, {nsplit} split")
+    assert nbins >= used // 2 and nsplit >= 1
+    out, q64 = run(case, "attend")
+    compare(case, out, oracle_pairs(case, 0, all_pairs(case), q64), f"short large {kv}")
