@@ -106,12 +106,13 @@ def test_large_pair_count_bitexact(gpu_lib):
 
 
 def test_pair_count_past_lds_bitexact(gpu_lib):
-    """More than 8192 pairs: the assign kernel keeps its per-pair arrays in
-    the plan workspace instead of LDS (dynamic and static plans)."""
+    """More than 12288 pairs: the assign kernel keeps its flat starts and
+    first slots in the plan workspace instead of LDS (dynamic and static
+    plans)."""
     import oracle
     rng = np.random.default_rng(6)
-    L = rng.integers(0, 3000, size=1100).astype(np.int32)
-    assert 8 * len(L) > 8192
+    L = rng.integers(0, 3000, size=1600).astype(np.int32)
+    assert 8 * len(L) > 12288
     got, info, _ = plan_only(None, L, 8, 512, 4)
     check(got, oracle.assign.assign_dynamic(L, 8, 512, 4))
     got, info, _ = plan_only(None, L, 8, 0, 4, lbp.LBP_POLICY_STATIC_SPLITS, 3)
@@ -156,4 +157,22 @@ def test_plan_matches_after_reuse_of_workspace(gpu_lib):
     info = lbp.lbp_plan(case.cfg, case.seq_lens, case.page_table, case.plan_ws)
     torch.cuda.synchronize()
     check(lbp.read_taskmap(case.plan_ws, info),
-          oracle.assign.assign_dynamic(L2, 1, info.num_bins, 4))
+          oracle.assign.assign_dynamic(L2, 1, info.num_bins, info.param))
+
+
+@pytest.mark.parametrize("B,H,W", [(1536, 8, 256), (4096, 8, 256), (12288, 1, 1024), (300, 64, 7),
+                                   (5000, 8, 256)])
+def test_large_batch_plans_bitexact(gpu_lib, B, H, W):
+    """Large batches, up to 40000 pairs: per-pair arrays in LDS (up to 12288
+    pairs), lengths only in LDS (up to 36864) and everything in the plan
+    workspace; short requests among long ones, so bins hold many
+    descriptors and a long pair spans many bins."""
+    import oracle
+    rng = np.random.default_rng(B + H)
+    L = np.where(rng.random(B) < 0.9, rng.integers(0, 200, size=B),
+                 rng.integers(1000, 100000, size=B)).astype(np.int32)
+    say(f"[plan] large B={B} H={H} W={W} pairs={B * H}")
+    got, info, _ = plan_only(None, L, H, W, 1)
+    check(got, oracle.assign.assign_dynamic(L, H, W, 1))
+    got, info, _ = plan_only(None, L, H, 0, 1, lbp.LBP_POLICY_STATIC_SPLITS, 2)
+    check(got, oracle.assign.assign_static_splits(L, H, 2))
