@@ -36,9 +36,8 @@
 //    slice of a descriptor issues nothing.  BF16 runs 8 waves per
 //    workgroup, FP8 6: with both slices really in flight, more FP8 waves
 //    only added merge work per descriptor and register pressure.
-//  * Batches of at least two (KV head, request) pairs per bin run an
-//    instance that drains a bin of many short descriptors one descriptor
-//    per wave, with no merge across waves (drain_waves).
+//  * The decode instance drains a bin of many short descriptors one
+//    descriptor per wave, with no merge across waves (drain_waves).
 //  * A pair served by a single descriptor is finished in place: its
 //    normalised output goes straight to `out` in BF16, and a pair without
 //    tokens gets zero rows here too.  Only pairs split over several bins use
@@ -871,7 +870,7 @@ __device__ inline void drain_waves(const AttendArgs& a, const int32_t* __restric
 // it loads, so every KV byte is still fetched once per workgroup).  kTileW:
 // the tile form's wave count (0: the format's own).  With one wave per SIMD
 // the register file has room for 32-token spans (two slices per step).
-template <class Kv, bool kCausal, int kNB, int kTileW, bool kFuse, bool kWave>
+template <class Kv, bool kCausal, int kNB, int kTileW, bool kFuse>
 __device__ inline void attend_bin(const AttendArgs& a, const int32_t* __restrict__ pt,
                                   const int4* __restrict__ descs,
                                   const int32_t* __restrict__ pair_count,
@@ -908,12 +907,14 @@ __device__ inline void attend_bin(const AttendArgs& a, const int32_t* __restrict
   int4 ds = bin_first[bin];
   asm volatile("" ::"s"(ds.x), "s"(ds.y), "s"(ds.z), "s"(ds.w));   // keep the load above the exit
   if (d_begin >= d_end) return;
-  if constexpr (kWave) {
+  if constexpr (!kCausal && kNB == 1 && !kFuse) {
     // at least three descriptors of at most two tiles on average (every
     // bin but the last holds exactly `budget` tiles, the last fewer): one
-    // descriptor per wave
+    // descriptor per wave.  Marked unlikely so that the compiler places
+    // drain_waves after the loop below instead of between this test and it,
+    // which costs short launches less
     const int budget = bin_offset[kHdrBudget - kHdrWords];
-    if (d_end - d_begin >= 3 && budget <= 2 * (d_end - d_begin)) {
+    if (__builtin_expect(d_end - d_begin >= 3 && budget <= 2 * (d_end - d_begin), 0)) {
       drain_waves<Kv>(a, pt, descs, pair_count, d_begin, d_end, wave, lane);
       return;
     }
@@ -1332,10 +1333,10 @@ __device__ void finish_split_pairs(const AttendArgs& a, const int4* __restrict__
 // on a faster CU simply drains more bins; every workgroup draws exactly one
 // ticket past the last bin, and the one holding the final ticket returns the
 // counter to zero for the next launch.
-// kWave: the decode instance that drains bins of many short descriptors one
-// descriptor per wave (drain_waves); the host launches it only for batches
-// of at least two (KV head, request) pairs per bin, since its code costs
-// every other short launch about 0.4 us although it never runs there.
+// The decode instance (no causal limit, one column tile, merge in a second
+// launch) carries drain_waves for bins of many short descriptors.  Its code
+// costs short launches that never use it 0.1-0.3 us; a bin that needs it
+// saves about a microsecond per descriptor past the first few.
 // kFuse: the instance of the single-launch form, which merges split pairs
 // itself (finish_split_pairs); the other instances leave the merge to the
 // combine kernel and carry none of its code (about 2400 of the decode
@@ -1347,7 +1348,7 @@ __device__ void finish_split_pairs(const AttendArgs& a, const int4* __restrict__
 // loop's registers toward occupancies that never occur, and whenever that
 // loop is the kernel's register peak it stops issuing the next slice ahead
 // of the current slice's math.
-template <class Kv, bool kCausal, int kNB, int kTileW, bool kFuse, bool kWave = false>
+template <class Kv, bool kCausal, int kNB, int kTileW, bool kFuse>
 __global__ __launch_bounds__((waves_of<Kv, kTileW>() * 64))
 __attribute__((amdgpu_waves_per_eu((waves_of<Kv, kTileW>() + 3) / 4,
                                    (waves_of<Kv, kTileW>() + 3) / 4))) void attend_kernel(
@@ -1373,8 +1374,8 @@ __attribute__((amdgpu_waves_per_eu((waves_of<Kv, kTileW>() + 3) / 4,
   };
   int bin = a.grab_counter ? next_bin() : int(blockIdx.x);
   while (bin < a.num_bins) {
-    attend_bin<Kv, kCausal, kNB, kTileW, kFuse, kWave>(a, page_table, descs, pair_count, bin_offset,
-                                           bin_first, pair_first, smem, bin);
+    attend_bin<Kv, kCausal, kNB, kTileW, kFuse>(a, page_table, descs, pair_count, bin_offset,
+                                                bin_first, pair_first, smem, bin);
     const int d_begin = bin_offset[bin], d_end = bin_offset[bin + 1];
     if constexpr (kFuse)
       finish_split_pairs<kThreads>(a, descs, pair_count, pair_first, smem, arrive_lds, d_begin,
@@ -1416,7 +1417,7 @@ __attribute__((amdgpu_waves_per_eu((waves_of<Kv, kTileW>() + 3) / 4,
 // The instance for a KV format: decode, or causal with 1-4 MFMA column
 // tiles per wave (q_len > 1: at most 16, 32, 48 or 64 columns), with or
 // without the in-kernel merge; its wave count.
-template <class Kv, bool kFuse, bool kWave>
+template <class Kv, bool kFuse>
 void pick_instance(bool causal, int tiles, const void** fn, int* waves) {
   *waves = Kv::kWaves;
   if (tiles == 4) {
@@ -1430,17 +1431,15 @@ void pick_instance(bool causal, int tiles, const void** fn, int* waves) {
     *waves = waves_of<Kv, Kv::kTile2Waves>();
   } else {
     *fn = causal ? reinterpret_cast<const void*>(&attend_kernel<Kv, true, 1, 0, kFuse>)
-                 : reinterpret_cast<const void*>(&attend_kernel<Kv, false, 1, 0, kFuse, kWave>);
+                 : reinterpret_cast<const void*>(&attend_kernel<Kv, false, 1, 0, kFuse>);
   }
 }
 template <class Kv>
-void pick_instance(bool causal, int tiles, bool fuse, bool wave, const void** fn, int* waves) {
+void pick_instance(bool causal, int tiles, bool fuse, const void** fn, int* waves) {
   if (fuse)
-    pick_instance<Kv, true, false>(causal, tiles, fn, waves);
-  else if (wave)
-    pick_instance<Kv, false, true>(causal, tiles, fn, waves);
+    pick_instance<Kv, true>(causal, tiles, fn, waves);
   else
-    pick_instance<Kv, false, false>(causal, tiles, fn, waves);
+    pick_instance<Kv, false>(causal, tiles, fn, waves);
 }
 
 hipError_t launch_attend(const AttendArgs& a, AttendKind kind, int grid, hipStream_t s) {
@@ -1458,20 +1457,17 @@ hipError_t launch_attend(const AttendArgs& a, AttendKind kind, int grid, hipStre
   const bool causal = a.q_len > 1;
   if (a.ncols < 1 || a.ncols > 64 || (!causal && a.ncols > 16)) return hipErrorInvalidValue;
   const int tiles = causal ? (a.ncols + 15) / 16 : 1;
-  // decode bins can fill with short descriptors only where there are
-  // several pairs per bin
-  const bool wave = !causal && int64_t(a.batch) * a.num_kv_heads >= 2 * int64_t(a.num_bins);
   int waves;
   const void* fn;
   switch (kind) {
     case kAttendFp8:
-      pick_instance<Fp8Kv>(causal, tiles, a.fuse != 0, wave, &fn, &waves);
+      pick_instance<Fp8Kv>(causal, tiles, a.fuse != 0, &fn, &waves);
       break;
     case kAttendFp8Q8:
-      pick_instance<Fp8KvQ8>(causal, tiles, a.fuse != 0, wave, &fn, &waves);
+      pick_instance<Fp8KvQ8>(causal, tiles, a.fuse != 0, &fn, &waves);
       break;
     default:
-      pick_instance<Bf16Kv>(causal, tiles, a.fuse != 0, wave, &fn, &waves);
+      pick_instance<Bf16Kv>(causal, tiles, a.fuse != 0, &fn, &waves);
   }
   // per wave for the merge: m and l of 16 tiles columns, then the C rows
   size_t lds = size_t(waves) * (32 * tiles + size_t(a.ncols) * kRedRow) * sizeof(float);

@@ -1,12 +1,11 @@
 """GPU parity of bins holding many short descriptors.
 
 Where short requests pile up, one bin holds many descriptors of one or two
-64-token tiles.  For decode batches of at least two (KV head, request)
-pairs per bin, lbp_attend and lbp_attend_fp8q launch the instance that
-drains such a bin (at least three descriptors averaging at most two tiles)
-one descriptor per wave and writes each result from the wave's registers;
-other bins of that launch, and every bin of the single-launch form, go
-through the per-descriptor loop with its merge across waves.  These cases
+64-token tiles.  In decode, lbp_attend and lbp_attend_fp8q drain such a bin
+(at least three descriptors averaging at most two tiles) one descriptor per
+wave and write each result from the wave's registers; other bins of the
+same launch, and every bin of the single-launch form, go through the
+per-descriptor loop with its merge across waves.  These cases
 make such bins, up to about twenty descriptors each (more than the waves),
 with pairs finished in place and pairs split across bins, in every KV
 format and entry point, and check every output row against the oracle.
@@ -110,13 +109,29 @@ def test_short_and_long_bins_in_one_launch(gpu_lib):
     wcfg = dataclasses.replace(CONFIGS["tiny"], name="short-long", batch=len(lengths),
                                num_q_heads=16, num_kv_heads=2)
     case = build_case(wcfg, lengths=lengths, num_workgroups=32, min_tiles=1)
-    assert wcfg.num_kv_heads * len(lengths) >= 2 * case.info.num_bins   # the per-wave instance
     nbins, nsplit = short_bins(case)
     used = int(lbp.read_taskmap(case.plan_ws, case.info)["header"][3])
     say(f"[short] short and long: {nbins} of {used} bins of short descriptors, {nsplit} split")
     assert 2 <= nbins <= used - 2 and nsplit >= 1
     out, q64 = run(case, "attend")
     compare(case, out, oracle_pairs(case, 0, all_pairs(case), q64), "short and long")
+
+
+@pytest.mark.parametrize("entry", ["attend", "fp8q"])
+def test_short_requests_after_a_long_one(gpu_lib, entry):
+    """One 8192-token request, then fifteen of 1-128 tokens, over 16 bins:
+    fewer pairs than bins, yet the short ones pack six to nine to a bin
+    behind the long one's last piece, one of them split across two such
+    bins."""
+    lengths = [8192] + short_lengths(15, 128, 9)
+    wcfg = dataclasses.replace(CONFIGS["fp8"], name=f"short-after-long-{entry}",
+                               batch=len(lengths), num_q_heads=8, num_kv_heads=1)
+    case = build_case(wcfg, lengths=lengths, num_workgroups=16, min_tiles=1)
+    nbins, nsplit = short_bins(case)
+    say(f"[short] after a long one ({entry}): {nbins} bins of short descriptors, {nsplit} split")
+    assert nbins >= 2 and nsplit >= 1
+    out, q64 = run(case, entry)
+    compare(case, out, oracle_pairs(case, 0, all_pairs(case), q64), f"short after long {entry}")
 
 
 @pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3"])
@@ -129,7 +144,6 @@ def test_large_batch_of_short_requests(gpu_lib, kv):
     lengths = [int(x) for x in rng.integers(1, 129, size=1024)]
     wcfg = dataclasses.replace(base, name=f"short-large-{kv}", batch=len(lengths))
     case = build_case(wcfg, lengths=lengths)
-    assert wcfg.num_kv_heads * len(lengths) >= 2 * case.info.num_bins   # the per-wave instance
     nbins, nsplit = short_bins(case)
     used = int(lbp.read_taskmap(case.plan_ws, case.info)["header"][3])
     say(f"[short] large {kv}: {nbins} of {used} bins of short descriptors, {nsplit} split")
