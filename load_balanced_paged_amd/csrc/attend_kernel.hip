@@ -1335,7 +1335,7 @@ __device__ void finish_split_pairs(const AttendArgs& a, const int4* __restrict__
 // counter to zero for the next launch.
 // The decode instance (no causal limit, one column tile, merge in a second
 // launch) carries drain_waves for bins of many short descriptors.  Its code
-// costs short launches that never use it 0.1-0.3 us; a bin that needs it
+// costs short launches that never use it 0.1-0.4 us; a bin that needs it
 // saves about a microsecond per descriptor past the first few.
 // kFuse: the instance of the single-launch form, which merges split pairs
 // itself (finish_split_pairs); the other instances leave the merge to the
