@@ -24,6 +24,7 @@ import hashlib
 import json
 import math
 import os
+import statistics
 import sys
 import time
 
@@ -40,6 +41,7 @@ LAYERS = {"mixed": 8, "uniform": 4, "skewed": 16, "fp8": 1, "tiny": 1}
 ATTEND_KERNEL = {"bf16": "attend_kernel<Bf16Kv>", "fp8_e4m3": "attend_kernel<Fp8Kv>"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attend_traffic.json")
 ATTEND_SRC = os.path.join(ROOT, "load_balanced_paged_amd", "csrc", "attend_kernel.hip")
+TIMED_REPLAYS = 3   # timed runs of K steps per configuration; the median is reported
 
 
 def log(msg):
@@ -51,9 +53,12 @@ def parse_args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--warmup-seconds", type=float, default=0.5,
-                    help="before the W warmup steps, run steps for this long (GPU clocks ramp "
-                         "up over the first tens of milliseconds of load)")
+    ap.add_argument("--warmup-seconds", type=float, default=1.0,
+                    help="before the W warmup steps, run steps for this long (the GPU's clocks "
+                         "need up to about a second of load to settle after an idle spell)")
+    ap.add_argument("--settle-seconds", type=float, default=0.25,
+                    help="steps run for this long before each later timing of a workload "
+                         "(fused, FP8 query, kernel, verification, static sweep)")
     ap.add_argument("--workloads", default="mixed,uniform,skewed,fp8",
                     help="comma list; the first is the headline (default mixed)")
     ap.add_argument("--no-static", action="store_true", help="skip the static split-KV comparison")
@@ -220,22 +225,26 @@ class Bench:
                 torch.cuda.current_stream().wait_stream(s)
                 graph.replay()                                # untimed warm replay
                 torch.cuda.synchronize()
-                mode = "hip_graph"
+                mode = f"hip_graph, median of {TIMED_REPLAYS} timed replays"
             except Exception as e:  # graph capture unavailable: time stream launches
                 log(f"graph capture failed ({e}); timing stream launches")
                 graph = None
-        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        start.record()
-        if graph is not None:
-            graph.replay()
-        else:
-            for i in range(steps):
-                run(i)
-        end.record()
-        torch.cuda.synchronize()
-        ms = start.elapsed_time(end) / steps
-        return ms, mode
+        # TIMED_REPLAYS timed runs of exactly `steps` steps, each bracketed by
+        # events and a synchronize; the median is reported
+        per_step = []
+        for _ in range(TIMED_REPLAYS):
+            start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            start.record()
+            if graph is not None:
+                graph.replay()
+            else:
+                for i in range(steps):
+                    run(i)
+            end.record()
+            torch.cuda.synchronize()
+            per_step.append(start.elapsed_time(end) / steps)
+        return statistics.median(per_step), mode
 
     def time_attend_kernel(self, steps):
         """Average duration of the persistent attention kernel alone:
@@ -521,11 +530,14 @@ def bench_one(name, lbp, args, headline, stream_gbs=None):
                kv_bytes_per_layer=b.wl.kv_bytes, total_tokens=b.wl.total_tokens,
                workgroups=info.num_bins, layers=b.layers)
     if not args.no_fused:
+        b.warm(args.settle_seconds)
         fms, _ = b.time_steps(args.steps, args.warmup, eager=args.eager, fused=True)
         res["fused_us_per_step"] = round(fms * 1e3, 2)      # lbp_attend_fused, one launch
     if b.wcfg.kv_dtype == "fp8_e4m3" and not args.no_fused:
+        b.warm(args.settle_seconds)
         qms, _ = b.time_steps(args.steps, args.warmup, eager=args.eager, fp8q=True)
         res["fp8q_us_per_step"] = round(qms * 1e3, 2)       # lbp_attend_fp8q: e4m3 query
+    b.warm(args.settle_seconds)
     k_mean, k_min, k_max = b.time_attend_kernel(max(20, min(args.steps, 100)))
     res["attend_kernel_us"] = {"mean": round(k_mean, 2), "min_of_replays": round(k_min, 2),
                                "max_of_replays": round(k_max, 2),
@@ -541,6 +553,7 @@ def bench_one(name, lbp, args, headline, stream_gbs=None):
                 continue
             if b.wcfg.num_q_heads // b.wcfg.num_kv_heads * T > 64:
                 continue
+            b.warm(args.settle_seconds)
             vms, _ = b.time_steps(args.steps, args.warmup, eager=args.eager, q_len=T)
             vgbs = b.wl.kv_bytes / (vms * 1e-3) / 1e9
             res["verify"][f"q_len={T}"] = {"us_per_step": round(vms * 1e3, 2),
@@ -551,6 +564,7 @@ def bench_one(name, lbp, args, headline, stream_gbs=None):
         s0 = max(1, math.ceil(W / (b.wcfg.num_kv_heads * b.wcfg.batch)))
         static = {}
         for S in sorted({s0, 1, 2, 4, 8, 16, 32, 64}):
+            b.warm(args.settle_seconds)
             sms, _ = b.time_steps(min(args.steps, 50), 2, lbp.LBP_POLICY_STATIC_SPLITS, S,
                                   eager=args.eager)
             static[S] = sms * 1e3
@@ -605,9 +619,11 @@ def bench_table3(lbp, args):
         layers = max(1, min(128, math.ceil(ROTATE_BYTES / kv)))
         b = Bench(wcfg.name, lbp, wcfg=wcfg, layers=layers)
         info, _, _ = b.plan()
-        b.warm(0.1)
+        b.warm(args.settle_seconds)
         ms, mode = b.time_steps(args.steps, args.warmup, eager=args.eager)
+        b.warm(args.settle_seconds)
         fms, _ = b.time_steps(args.steps, args.warmup, eager=args.eager, fused=True)
+        b.warm(args.settle_seconds)
         qms, _ = b.time_steps(args.steps, args.warmup, eager=args.eager, fp8q=True)
         b.check_finite()
         us = ms * 1e3
@@ -615,17 +631,18 @@ def bench_table3(lbp, args):
         s_grid = max(1, math.ceil(W / (wcfg.num_kv_heads * wcfg.batch)))
         static = {}
         for S in sorted({s_grid, 1, 2, 4, 8, 16, 32, 64}):
+            b.warm(args.settle_seconds)
             sms, _ = b.time_steps(min(args.steps, 50), 2, lbp.LBP_POLICY_STATIC_SPLITS, S,
                                   eager=args.eager)
             static[S] = sms * 1e3
         best = min(static, key=static.get)
         # the minimum-work floor F (tiles per bin) of the dynamic plan; the
         # library's default is 1 (no floor), and F binds only while
-        # T <= (F - 1) W.  The default plan runs again first, so that no F is
-        # timed straight after the static sweep's slowest plans.
-        b.warm(0.05)
+        # T <= (F - 1) W.  The default plan runs first before each F, so
+        # that no F is timed straight after another plan's timing.
         by_f = {}
         for F in (1, 2, 4):
+            b.warm(args.settle_seconds)
             fms_f, _ = b.time_steps(min(args.steps, 50), 2, lbp.LBP_POLICY_DYNAMIC, F,
                                     eager=args.eager)
             by_f[F] = {"us_per_step": round(fms_f * 1e3, 2), "bins_used": b.used_bins(F)}
