@@ -137,9 +137,12 @@ typedef struct lbp_plan_info {
  *               ticket counter of the attention kernel (0 between launches)
  *               [11] number of split_list entries
  *   bin_offset[num_bins + 1]  descriptors of bin b: [bin_offset[b], bin_offset[b+1])
- *   bin_first[num_bins][4]    copy of desc[bin_offset[b]] (zeros for an empty bin),
- *                             so a workgroup reads its bin's range and first
- *                             descriptor in one round trip
+ *   bin_first[num_bins][8]    copy of desc[bin_offset[b]], then the physical
+ *                             pages of that descriptor's first two tiles (the
+ *                             second is the first's when it has one tile), 0, 0
+ *                             (all zeros for an empty bin), so a workgroup
+ *                             reads its bin's range, first descriptor and
+ *                             first pages in one round trip
  *   desc[max_desc][4]         (kv_head, request, token_begin, token_end)
  *   pair_first[H_kv * batch], pair_count[H_kv * batch]; pair p = kv_head * batch + request
  *   scratch[H_kv * batch]     assign-kernel scratch

@@ -404,7 +404,8 @@ def read_taskmap(plan_ws, info: lbp_plan_info) -> dict:
         "batch": int(h[3]), "num_kv_heads": int(h[4]),
         "header": (int(h[5]), int(h[6]), int(h[7]), int(h[8])), "status": int(h[9]),
         "bin_offset": sl(off.bin_offset, info.num_bins + 1),
-        "bin_first": sl(off.bin_first, 4 * info.num_bins).reshape(-1, 4),
+        "bin_first": sl(off.bin_first, 8 * info.num_bins).reshape(-1, 8)[:, :4],
+        "bin_pages": sl(off.bin_first, 8 * info.num_bins).reshape(-1, 8)[:, 4:6],
         "desc": sl(off.desc, 4 * D).reshape(D, 4),
         "pair_first": sl(off.pair_first, npairs),
         "pair_count": sl(off.pair_count, npairs),

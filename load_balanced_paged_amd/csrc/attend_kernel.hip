@@ -901,11 +901,15 @@ __device__ inline void attend_bin(const AttendArgs& a, const int32_t* __restrict
   // tile t's columns: [16 t, + tile_cols(t))
   auto tile_cols = [&](int t) { return kNB == 1 ? C : min(16, C - 16 * t); };
   float* red = smem + wave * red_stride;
-  // range and first descriptor are independent loads: one round trip
+  // range, first descriptor and the pages of its first two tiles are
+  // independent loads: one round trip, after which the first KV loads can
+  // issue without a page-table lookup
   const int d_begin = bin_offset[bin];
   const int d_end = bin_offset[bin + 1];
-  int4 ds = bin_first[bin];
-  asm volatile("" ::"s"(ds.x), "s"(ds.y), "s"(ds.z), "s"(ds.w));   // keep the load above the exit
+  int4 ds = bin_first[2 * bin];
+  const int4 first_pages = bin_first[2 * bin + 1];
+  asm volatile("" ::"s"(ds.x), "s"(ds.y), "s"(ds.z), "s"(ds.w), "s"(first_pages.x),
+               "s"(first_pages.y));   // keep the loads above the exit
   if (d_begin >= d_end) return;
   if constexpr (!kCausal && kNB == 1 && !kFuse) {
     // at least three descriptors of at most two tiles on average (every
@@ -947,8 +951,12 @@ __device__ inline void attend_bin(const AttendArgs& a, const int32_t* __restrict
     }
   }
   {
+    // a wave's first span starts in the descriptor's first or second tile
+    // (or, past a short descriptor's end, loads nothing from its last one):
+    // the page page_of would look up
+    static_assert((kWaves - 1) * kSpan < 2 * kPageTokens, "first spans within two tiles");
     const int t0 = ds.z + wave * kSpan;
-    issue_span(buf[0], ds.x, t0, ds.w, page_of(a, pt, ds.y, t0, ds.w));
+    issue_span(buf[0], ds.x, t0, ds.w, wave * kSpan < kPageTokens ? first_pages.x : first_pages.y);
   }
 
   for (int d = d_begin; d < d_end; ++d) {

@@ -160,6 +160,8 @@ lbp_status build_plan(const lbp_config* cfg, int policy, int param, const int32_
   a.header = reinterpret_cast<int32_t*>(base + off.header);
   a.bin_offset = reinterpret_cast<int32_t*>(base + off.bin_offset);
   a.bin_first = reinterpret_cast<int32_t*>(base + off.bin_first);
+  a.page_table = page_table;
+  a.page_table_stride = stride;
   a.desc = reinterpret_cast<int32_t*>(base + off.desc);
   a.pair_first = reinterpret_cast<int32_t*>(base + off.pair_first);
   a.pair_count = reinterpret_cast<int32_t*>(base + off.pair_count);

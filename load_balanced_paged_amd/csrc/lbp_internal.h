@@ -53,7 +53,7 @@ inline lbp_plan_offsets plan_layout(int policy, int num_bins, int max_desc, int 
   o.header = 0;
   o.bin_offset = align_up(o.header + kHdrWords * 4, 64);
   o.bin_first = align_up(o.bin_offset + uint64_t(num_bins + 1) * 4, 64);
-  o.desc = align_up(o.bin_first + uint64_t(num_bins) * 16, 64);
+  o.desc = align_up(o.bin_first + uint64_t(num_bins) * 32, 64);
   o.pair_first = align_up(o.desc + uint64_t(max_desc) * 16, 64);
   o.pair_count = align_up(o.pair_first + uint64_t(npairs) * 4, 64);
   o.scratch = align_up(o.pair_count + uint64_t(npairs) * 4, 64);
@@ -85,7 +85,10 @@ struct PlanArgs {
   int32_t max_tokens;        // 64 * max_pages_per_seq
   int32_t* header;
   int32_t* bin_offset;
-  int32_t* bin_first;        // [num_bins][4]: copy of each bin's first descriptor
+  int32_t* bin_first;        // [num_bins][8]: each bin's first descriptor, then the pages
+                             // of its first two tiles (the second clamped to the last), 0, 0
+  const int32_t* page_table;
+  int64_t page_table_stride;
   int32_t* desc;             // [max_desc][4]
   int32_t* pair_first;
   int32_t* pair_count;

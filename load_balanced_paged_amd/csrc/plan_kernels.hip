@@ -259,18 +259,26 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   // arrival counters of the attention kernel's merge start at zero
   for (int i = tid; i < a.arrive_words; i += kPlanThreads) a.arrive[i] = 0;
 
-  // per bin: its descriptor offset and first descriptor (read by the
-  // attention kernel together with the range); in the dynamic plan also the
-  // descriptor itself where a bin boundary falls inside a pair, and in the
-  // static plans (one descriptor per bin) every descriptor
+  // per bin: its descriptor offset, first descriptor and that descriptor's
+  // first two pages (read by the attention kernel together with the range,
+  // so its first KV loads need no page-table round trip); in the dynamic
+  // plan also the descriptor itself where a bin boundary falls inside a
+  // pair, and in the static plans (one descriptor per bin) every descriptor
   int U;
-  int4* const bin_first = reinterpret_cast<int4*>(a.bin_first);
+  int4* const bin_first = reinterpret_cast<int4*>(a.bin_first);   // two int4 per bin
   int4* const desc = reinterpret_cast<int4*>(a.desc);
+  // pages of descriptor v's first tile and of the next one (its first again
+  // for a one-tile descriptor)
+  auto first_pages = [&](int r, int4 v) {
+    const int32_t* row = a.page_table + int64_t(r) * a.page_table_stride;
+    const int t0 = v.z / kPageTokens;
+    return make_int4(row[t0], row[min(t0 + 1, (v.w - 1) / kPageTokens)], 0, 0);
+  };
   if (dynamic) {
     U = T ? (T + budget - 1) / budget : 0;
     for (int b = tid; b <= a.num_bins; b += kPlanThreads) {
       int off = D;
-      int4 v = make_int4(0, 0, 0, 0);
+      int4 v = make_int4(0, 0, 0, 0), pg = v;
       if (b < U) {                   // a used bin holds at least one descriptor
         const int f = b * budget;    // < T, so fits in int
         const int p = last_le(start_of, npairs, f);
@@ -280,16 +288,20 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
         off = first_of[p] + j;
         v = desc_of(p / B, r, len_at(p, r), S, j);
         if (j > 0) desc[off] = v;
+        pg = first_pages(r, v);
       }
       a.bin_offset[b] = off;
-      if (b < a.num_bins) bin_first[b] = v;
+      if (b < a.num_bins) {
+        bin_first[2 * b] = v;
+        bin_first[2 * b + 1] = pg;
+      }
     }
   } else {
     U = D;
     const int Sp = a.splits_per_pair;
     for (int b = tid; b <= a.num_bins; b += kPlanThreads) {
       int off = D;
-      int4 v = make_int4(0, 0, 0, 0);
+      int4 v = make_int4(0, 0, 0, 0), pg = v;
       if (b < a.num_bins) {
         const int p = b / Sp, s = b % Sp;
         const int r = p % B;
@@ -299,8 +311,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
         if (s < cnt) {
           v = desc_of(p / B, r, L, 0, s);
           desc[off] = v;
+          pg = first_pages(r, v);
         }
-        bin_first[b] = v;
+        bin_first[2 * b] = v;
+        bin_first[2 * b + 1] = pg;
       }
       a.bin_offset[b] = off;
     }

@@ -128,7 +128,22 @@ def assert_taskmap_matches(case: Case):
         d0, d1 = ref.bin_offset[b], ref.bin_offset[b + 1]
         want = ref.desc[d0] if d1 > d0 else np.zeros(4, np.int32)
         assert np.array_equal(got["bin_first"][b], want), b
+    assert np.array_equal(got["bin_pages"], expected_bin_pages(ref, np.asarray(case.wl.page_table)))
     return got, ref
+
+
+def expected_bin_pages(ref, table):
+    """Per bin, the pages of its first descriptor's first tile and of the
+    next one (the first again for a one-tile descriptor); zeros for an empty
+    bin."""
+    out = np.zeros((ref.num_bins, 2), np.int32)
+    for b in range(ref.num_bins):
+        d0, d1 = ref.bin_offset[b], ref.bin_offset[b + 1]
+        if d1 > d0:
+            _, r, lo, hi = (int(x) for x in ref.desc[d0])
+            t0 = lo // 64
+            out[b] = (table[r, t0], table[r, min(t0 + 1, (hi - 1) // 64)])
+    return out
 
 
 def expected_split_list(ref):

@@ -265,7 +265,7 @@ def test_plan_layout(lib):
     off = lbp.lbp_plan_layout(info)
     assert off.header == 0
     assert off.bin_offset >= 64 and off.bin_first >= off.bin_offset + 4 * 257
-    assert off.bin_first % 16 == 0 and off.desc >= off.bin_first + 16 * 256
+    assert off.bin_first % 16 == 0 and off.desc >= off.bin_first + 32 * 256
     assert off.desc % 16 == 0
     assert off.pair_first >= off.desc + 16 * info.max_desc
     assert off.pair_count >= off.pair_first + 4 * 32

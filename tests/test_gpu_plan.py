@@ -7,7 +7,8 @@ import pytest
 import torch
 
 import load_balanced_paged_amd as lbp
-from gpu_support import assert_taskmap_matches, build_case, expected_split_list, say
+from gpu_support import (assert_taskmap_matches, build_case, expected_bin_pages,
+                         expected_split_list, say)
 from workloads import CONFIGS
 
 pytestmark = pytest.mark.gpu
@@ -22,13 +23,19 @@ def plan_only(wcfg, lengths, H, W, F, policy=lbp.LBP_POLICY_DYNAMIC, param=0, ma
     pb, _ = lbp.lbp_query_workspace(cfg, policy, param)
     ws = torch.full((pb,), 0xA5, dtype=torch.uint8, device="cuda")   # stale bytes must not leak
     seq = torch.from_numpy(lengths).cuda()
-    table = torch.zeros((len(lengths), mp), dtype=torch.int32, device="cuda")
+    # distinct page ids (a seeded permutation), so that the per-bin first
+    # pages the plan records are checkable
+    host_table = np.random.default_rng(len(lengths) * 7 + mp).permutation(
+        len(lengths) * mp).astype(np.int32).reshape(len(lengths), mp)
+    table = torch.from_numpy(host_table).cuda()
     if policy == lbp.LBP_POLICY_DYNAMIC:
         info = lbp.lbp_plan(cfg, seq, table, ws)
     else:
         info = lbp.lbp_plan_static(cfg, policy, param, seq, table, ws)
     torch.cuda.synchronize()
-    return lbp.read_taskmap(ws, info), info, cfg
+    got = lbp.read_taskmap(ws, info)
+    got["host_table"] = host_table
+    return got, info, cfg
 
 
 def check(got, ref):
@@ -45,6 +52,8 @@ def check(got, ref):
         d0, d1 = ref.bin_offset[b], ref.bin_offset[b + 1]
         want = ref.desc[d0] if d1 > d0 else np.zeros(4, np.int32)
         assert np.array_equal(got["bin_first"][b], want), b
+    if "host_table" in got:
+        assert np.array_equal(got["bin_pages"], expected_bin_pages(ref, got["host_table"]))
 
 
 @pytest.mark.parametrize("F", [0, 4])
