@@ -22,7 +22,10 @@
 // those are written bin by bin: bin b finds the pair holding its first tile
 // b*budget by binary search over the flat starts, and writes its offset,
 // its first descriptor and, when that is not the pair's first, the
-// descriptor itself.
+// descriptor itself.  Beside its first descriptor each bin also records the
+// physical pages of that descriptor's first two tiles, read from the page
+// table here, so that the attention kernel's first KV loads follow a single
+// round trip.
 #include "lbp_internal.h"
 
 namespace lbp {
