@@ -228,6 +228,18 @@ lbp_status lbp_plan_static(const lbp_config* cfg, int32_t policy, int32_t param,
 /* Offsets of the task-map sections for a filled plan info (host only). */
 lbp_status lbp_plan_layout(const lbp_plan_info* info, lbp_plan_offsets* offsets);
 
+/* Copies a plan's task map (the first lbp_plan_layout(info).total bytes of
+ * plan_ws_dev, laid out as lbp_plan_offsets describes) into host_buf, in
+ * order after the work already on `stream`, and waits for the copy: for
+ * tests and inspection of what the assign step built (SGLang x HPC-Ops
+ * page, "Scheduling around live KV work"), never for the decode path.  The
+ * only call in the library that synchronises.  host_buf (caller-owned, any
+ * host memory) must hold host_bytes >= that total, else
+ * LBP_ERR_WORKSPACE_TOO_SMALL; null pointers give LBP_ERR_INVALID_ARG, an
+ * unfilled info LBP_ERR_MISMATCH, a failed copy LBP_ERR_HIP. */
+lbp_status lbp_taskmap_to_host(const lbp_plan_info* info, const void* plan_ws_dev, void* host_buf,
+                               size_t host_bytes, void* stream);
+
 /* One decode-attention layer (SGLang x HPC-Ops page, "Scheduling around live
  * KV work", second paragraph; vLLM x HPC-Ops page, bullet "Compute and
  * combine"): the persistent attention kernel, then the combine kernel, both

@@ -41,7 +41,7 @@ EXPORTED_SYMBOLS = (
     "lbp_status_string", "lbp_version", "lbp_query_workspace", "lbp_plan", "lbp_plan_static",
     "lbp_plan_layout", "lbp_attend", "lbp_attend_fused", "lbp_attend_partials",
     "lbp_attend_traced", "lbp_attend_fp8q", "lbp_prologue",
-    "lbp_combine", "lbp_read_stream", "lbp_attend_noalloc",
+    "lbp_combine", "lbp_read_stream", "lbp_attend_noalloc", "lbp_taskmap_to_host",
 )
 
 
@@ -148,6 +148,7 @@ def load(path: str = LIB_PATH):
         "lbp_combine": (I32, [cfgp, infop, P, P, SZ, P, P]),
         "lbp_read_stream": (I32, [P, SZ, P, I32, P]),
         "lbp_attend_noalloc": (I32, [cfgp, infop, P, P, P, P, P, P, P, P]),
+        "lbp_taskmap_to_host": (I32, [infop, P, P, SZ, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -387,10 +388,22 @@ def lbp_read_stream(buf, sink, blocks, stream=None):
 # readers for host-side inspection (tests, benchmark)
 # ---------------------------------------------------------------------------
 
-def read_taskmap(plan_ws, info: lbp_plan_info) -> dict:
-    """Copy a plan workspace to the host and slice it by lbp_plan_layout."""
+def lbp_taskmap_to_host(plan_ws, info: lbp_plan_info, stream=None) -> np.ndarray:
+    """The plan's task map as host bytes (lbp_taskmap_to_host: ordered on
+    `stream`, waits for the copy)."""
     off = lbp_plan_layout(info)
-    raw = plan_ws.view(-1).view(dtype=__import__("torch").uint8)[:off.total].cpu().numpy()
+    raw = np.empty(off.total, dtype=np.uint8)
+    _check(load().lbp_taskmap_to_host(ctypes.byref(info), _ptr(plan_ws, "plan_ws"),
+                                      raw.ctypes.data_as(ctypes.c_void_p), raw.nbytes,
+                                      _stream(stream)), "lbp_taskmap_to_host")
+    return raw
+
+
+def read_taskmap(plan_ws, info: lbp_plan_info) -> dict:
+    """Copy a plan's task map to the host (lbp_taskmap_to_host) and slice it
+    by lbp_plan_layout."""
+    off = lbp_plan_layout(info)
+    raw = lbp_taskmap_to_host(plan_ws, info)
     words = raw.view(np.int32)
     h = words[off.header // 4: off.header // 4 + 16]
     D = int(h[7])

@@ -258,6 +258,19 @@ lbp_status lbp_plan_layout(const lbp_plan_info* info, lbp_plan_offsets* offsets)
   return LBP_OK;
 }
 
+lbp_status lbp_taskmap_to_host(const lbp_plan_info* info, const void* plan_ws_dev, void* host_buf,
+                               size_t host_bytes, void* stream) {
+  if (!info || !plan_ws_dev || !host_buf) return LBP_ERR_INVALID_ARG;
+  if (info->magic != LBP_PLAN_MAGIC) return LBP_ERR_MISMATCH;
+  const uint64_t total = offsets_of(info).total;
+  if (host_bytes < total) return LBP_ERR_WORKSPACE_TOO_SMALL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (hipMemcpyAsync(host_buf, plan_ws_dev, total, hipMemcpyDeviceToHost, s) != hipSuccess)
+    return LBP_ERR_HIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return LBP_ERR_HIP;
+  return LBP_OK;
+}
+
 // The attention kernel alone (fuse = false) or, for a dynamic plan with
 // fuse = true, the attention kernel that also merges the split pairs.
 static lbp_status attend_impl(const lbp_config* cfg, const lbp_plan_info* info,

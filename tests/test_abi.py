@@ -336,3 +336,19 @@ def test_read_stream_guards(lib):
     assert lib.lbp_read_stream(aligned, 1024, FAKE, 0, None) == lbp.LBP_ERR_INVALID_ARG
     assert lib.lbp_read_stream(aligned, 1000, FAKE, 8, None) == lbp.LBP_ERR_INVALID_ARG
     assert lib.lbp_read_stream(odd, 1024, FAKE, 8, None) == lbp.LBP_ERR_INVALID_ARG
+
+
+def test_taskmap_to_host_guards(lib):
+    """lbp_taskmap_to_host rejects bad arguments before any copy."""
+    c = cfg()
+    info = good_info(c)
+    total = lbp.lbp_plan_layout(info).total
+    buf = ctypes.create_string_buffer(int(total))
+    call = lib.lbp_taskmap_to_host
+    assert call(None, FAKE, buf, total, None) == lbp.LBP_ERR_INVALID_ARG
+    assert call(ctypes.byref(info), None, buf, total, None) == lbp.LBP_ERR_INVALID_ARG
+    assert call(ctypes.byref(info), FAKE, None, total, None) == lbp.LBP_ERR_INVALID_ARG
+    assert call(ctypes.byref(info), FAKE, buf, total - 1, None) == lbp.LBP_ERR_WORKSPACE_TOO_SMALL
+    bad = good_info(c)
+    bad.magic = 0
+    assert call(ctypes.byref(bad), FAKE, buf, total, None) == lbp.LBP_ERR_MISMATCH

@@ -185,3 +185,30 @@ def test_large_batch_plans_bitexact(gpu_lib, B, H, W):
     check(got, oracle.assign.assign_dynamic(L, H, W, 1))
     got, info, _ = plan_only(None, L, H, 0, 1, lbp.LBP_POLICY_STATIC_SPLITS, 2)
     check(got, oracle.assign.assign_static_splits(L, H, 2))
+
+
+def test_taskmap_to_host_on_a_side_stream(gpu_lib):
+    """lbp_taskmap_to_host, ordered on the stream that built the plan,
+    returns exactly the workspace's first lbp_plan_layout(info).total bytes
+    and agrees with the oracle's map."""
+    import oracle
+    rng = np.random.default_rng(77)
+    L = rng.integers(0, 3000, size=40).astype(np.int32)
+    H, W = 4, 64
+    mp = int((L.max() + 63) // 64)
+    cfg = lbp.make_config(8 * H, H, len(L), mp, num_workgroups=W, min_tiles_per_bin=1)
+    pb, _ = lbp.lbp_query_workspace(cfg)
+    ws = torch.full((pb,), 0x5A, dtype=torch.uint8, device="cuda")
+    seq = torch.from_numpy(L).cuda()
+    table = torch.arange(len(L) * mp, dtype=torch.int32, device="cuda").view(len(L), mp)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    info = lbp.lbp_plan(cfg, seq, table, ws, stream=s)
+    raw = lbp.lbp_taskmap_to_host(ws, info, stream=s)
+    torch.cuda.synchronize()
+    total = lbp.lbp_plan_layout(info).total
+    assert raw.nbytes == total
+    assert np.array_equal(raw, ws[:total].cpu().numpy())
+    got = lbp.read_taskmap(ws, info)
+    got["host_table"] = table.cpu().numpy()
+    check(got, oracle.assign.assign_dynamic(L, H, W, 1))
