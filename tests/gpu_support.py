@@ -221,6 +221,64 @@ def oracle_verify_pairs(case: Case, layer: int, pairs, q64: np.ndarray):
     return res
 
 
+def oracle_verify_layer(case: Case, layer: int, q64: np.ndarray, pairs=None,
+                        workers: Optional[int] = None):
+    """fp64 oracle rows [T, G, D] of multi-token verification for `pairs`
+    (default: every pair) of a layer, for whole-layer verification parity.
+
+    Like oracle_layer: the layer's caches are copied to the host once, and
+    the pairs run longest first on a thread pool (one BLAS thread per
+    worker), each through oracle.attention.paged_verify_attention over its
+    own pages."""
+    import concurrent.futures
+    import os
+    try:
+        from threadpoolctl import threadpool_limits
+    except Exception:  # pragma: no cover
+        threadpool_limits = None
+    Lyr = case.wl.layers[layer]
+    G = case.G
+    fp8 = case.wcfg.kv_dtype == "fp8_e4m3"
+    lengths = np.asarray(case.wl.lengths)
+    if pairs is None:
+        pairs = all_pairs(case)
+    if fp8:
+        kc, vc = Lyr.k_cache.cpu().numpy(), Lyr.v_cache.cpu().numpy()
+        ks, vs = Lyr.k_scale.cpu().numpy(), Lyr.v_scale.cpu().numpy()
+    else:
+        kc, vc, ks, vs = bits(Lyr.k_cache), bits(Lyr.v_cache), None, None
+    table = np.asarray(case.wl.page_table)
+
+    def one(pair):
+        g, r = pair
+        Lr = int(lengths[r])
+        n = max(1, (Lr + 63) // 64)
+        pages = table[r, :n].astype(np.int64)
+        sub = np.arange(n, dtype=np.int32)[None]
+        q = q64[r:r + 1, :, g * G:(g + 1) * G]
+        kw = {}
+        if fp8:
+            kw = dict(kv_dtype="fp8_e4m3", k_scale=ks[pages][:, g:g + 1],
+                      v_scale=vs[pages][:, g:g + 1])
+        o, _ = oracle.attention.paged_verify_attention(
+            q, kc[pages][:, g:g + 1], vc[pages][:, g:g + 1], sub, [Lr], 1,
+            case.wcfg.sm_scale, **kw)
+        return pair, o[0]
+
+    order = sorted(pairs, key=lambda p: -int(lengths[p[1]]))
+    n = workers or min(16, len(os.sched_getaffinity(0)))
+    ctx = threadpool_limits(limits=1) if threadpool_limits else None
+    if ctx:
+        ctx.__enter__()
+    try:
+        with concurrent.futures.ThreadPoolExecutor(n) as ex:
+            res = dict(ex.map(one, order))
+    finally:
+        if ctx:
+            ctx.__exit__(None, None, None)
+    return {p: res[p] for p in pairs}
+
+
 def parity_stats(got_rows, ref_rows, lengths=None):
     """Error statistics of stacked pair outputs ([n_pairs, ...] fp64 each).
 

@@ -11,15 +11,17 @@ sees no token at all.
 """
 
 import dataclasses
+import time
 
 import numpy as np
+
 import pytest
 import torch
 
 import load_balanced_paged_amd as lbp
 import oracle
 from gpu_support import (all_pairs, assert_taskmap_matches, bits, build_case, compare_verify,
-                         oracle_verify_pairs, sample_pairs, say)
+                         oracle_verify_layer, oracle_verify_pairs, say)
 from workloads import CONFIGS, quantize_query_e4m3
 
 pytestmark = pytest.mark.gpu
@@ -55,11 +57,15 @@ def test_verify_two_tokens_all_rows(gpu_lib, name):
     compare_verify(case, run(case, q, lbp.lbp_attend_fused), ref, f"verify {name} T=2 fused")
 
 
-def test_verify_mixed_sampled(gpu_lib):
+def test_verify_mixed_all_pairs(gpu_lib):
+    """Two verification rows per request: every pair of the mixed-length
+    workload against the oracle."""
     case = build_case(CONFIGS["mixed"], q_len=2)
     q = make_q(case, 2, seed=1)
-    compare_verify(case, run(case, q), oracle_verify_pairs(case, 0, sample_pairs(case, 10),
-                                                           q64_of(q)), "verify mixed T=2")
+    t0 = time.time()
+    ref = oracle_verify_layer(case, 0, q64_of(q))
+    say(f"[verify] mixed T=2 oracle over {len(ref)} pairs: {time.time() - t0:.1f} s")
+    compare_verify(case, run(case, q), ref, "verify mixed T=2 all pairs")
 
 
 @pytest.mark.parametrize("group,hkv,T", [(4, 2, 4), (1, 4, 16), (3, 3, 5), (16, 1, 1)])
@@ -100,13 +106,27 @@ def test_verify_column_blocks(gpu_lib, group, hkv, T):
     assert torch.all(out[0, :T - 1] == 0)
 
 
-def test_verify_six_rows_mixed_sampled(gpu_lib):
+def test_verify_six_rows_mixed_all_pairs(gpu_lib):
     """Six verification rows per request at the 8-query-head group (48
-    columns), on the mixed-length workload."""
+    columns): every pair of the mixed-length workload against the oracle."""
     case = build_case(CONFIGS["mixed"], q_len=6)
     q = make_q(case, 6, seed=7)
-    compare_verify(case, run(case, q), oracle_verify_pairs(case, 0, sample_pairs(case, 6),
-                                                           q64_of(q)), "verify mixed T=6")
+    t0 = time.time()
+    ref = oracle_verify_layer(case, 0, q64_of(q))
+    say(f"[verify] mixed T=6 oracle over {len(ref)} pairs: {time.time() - t0:.1f} s")
+    compare_verify(case, run(case, q), ref, "verify mixed T=6 all pairs")
+
+
+@pytest.mark.timeout(240)
+def test_verify_six_rows_fp8_all_pairs(gpu_lib):
+    """Six verification rows per request over the FP8-KV workload (128
+    requests of 1K-256K tokens, 48 columns): every pair against the oracle."""
+    case = build_case(CONFIGS["fp8"], q_len=6)
+    q = make_q(case, 6, seed=11)
+    t0 = time.time()
+    ref = oracle_verify_layer(case, 0, q64_of(q))
+    say(f"[verify] fp8 T=6 oracle over {len(ref)} pairs: {time.time() - t0:.1f} s")
+    compare_verify(case, run(case, q), ref, "verify fp8 T=6 all pairs")
 
 
 def test_verify_fully_masked_descriptor(gpu_lib):
