@@ -18,8 +18,9 @@
 // merges column q (query token q / G, head q % G) of list entry i, or exits
 // if the plan has fewer entries.  Thread t owns dims
 // [4(t%32), +4) of partials k = t/32 (mod R), R = threads / 32, and loads
-// each partial's log-sum-exp together with its row, merging online (running
-// max, sum and rescaled accumulator), sixteen partials per thread in flight:
+// each partial's log-sum-exp together with its row, sixteen partials per
+// thread in flight, and merges each round of loads at once (one rescale of
+// the running max, sum and accumulator per round, one exp2 per partial):
 // 16 R partial rows per round trip, so the critical path is the launch plus
 // two dependent memory round trips (the list entry, then the rows) for up to
 // 16 R splits.  The R per-thread states are merged in LDS in a fixed order
@@ -39,6 +40,33 @@ namespace {
 constexpr int kLanesPerRow = kHeadDim / 4;              // 32 float4 per 128-dim row
 constexpr int kUnroll = 16;
 constexpr int kWideGrid = 256;   // workgroups up to which the 512-thread form runs
+
+// Merges the first n of N loaded (lse, row) pairs into a running (max, sum,
+// acc) state at once: the state is rescaled once to the round's new maximum,
+// then every partial adds 2^(lse - max) times its row, one exp2 each instead
+// of the two and the rescale of an online merge per partial.  Empty partials
+// (lse = -inf) add nothing; an all-empty state stays (-inf, 0, 0).
+template <int N>
+__device__ inline void merge_round(float& m, float& l, f32x4_t& acc, const float (&ls)[N],
+                                   const f32x4_t (&v)[N], int n) {
+  float mr = m;
+#pragma unroll
+  for (int u = 0; u < N; ++u)
+    if (u < n) mr = fmaxf(mr, ls[u]);
+  const float ref = finite_or_zero(mr);
+  const float a = __builtin_amdgcn_exp2f(m - ref);   // 0 while the state is empty
+  acc = acc * a;
+  l = l * a;
+#pragma unroll
+  for (int u = 0; u < N; ++u) {
+    if (u < n) {
+      const float b = __builtin_amdgcn_exp2f(ls[u] - ref);
+      acc += v[u] * b;
+      l += b;
+    }
+  }
+  m = mr;
+}
 
 template <int kThreads>
 __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
@@ -80,9 +108,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
         v[u] = o[int64_t(k) * stride4 + c4];
       }
     }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u)
-      if (k0 + u * kRowGroups < cnt) merge_into(m, l, acc, ls[u], v[u]);
+    merge_round(m, l, acc, ls, v, (cnt - k0 + kRowGroups - 1) / kRowGroups);
   }
   if (c4 == 0) {
     red_m[kg] = m;
@@ -142,9 +168,7 @@ __global__ __launch_bounds__(kPairThreads) void combine_pairs_kernel(CombineArgs
         v[u] = o[int64_t(k0 + u) * stride4 + c4];
       }
     }
-#pragma unroll
-    for (int u = 0; u < kPairUnroll; ++u)
-      if (k0 + u < cnt) merge_into(m, l, acc, ls[u], v[u]);
+    merge_round(m, l, acc, ls, v, cnt - k0);
   }
   store_bf16x4(a.out, query_row(r, g, q, a.q_len, a.group, a.num_q_heads), c4,
                l > 0.f ? acc / l : f32x4_t{0.f, 0.f, 0.f, 0.f});
